@@ -1,0 +1,106 @@
+"""The oracle's pins must catch plausible mistakes (CPU only).
+
+Each case plants one wrong convention in the oracle module (monkeypatched for
+the duration of the case) and runs the pins that should notice it; the case
+passes only if at least one of them fails.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from oracle import moe_oracle as mo
+
+import test_oracle_decode as tdec
+import test_oracle_ffn as tffn
+import test_oracle_routing as trout
+
+
+def _unpack_high_first(q):
+    q = np.asarray(q, dtype=np.uint8)
+    out = np.empty(q.shape[:-1] + (q.shape[-1] * 2,), dtype=np.uint8)
+    out[..., 0::2] = q >> 4
+    out[..., 1::2] = q & 0xF
+    return out
+
+
+def _e8m0_bias_126(s):
+    s = np.asarray(s, dtype=np.int64)
+    return np.where(s == 255, np.nan, np.ldexp(1.0, s - 126))
+
+
+def _topk_ties_high(L, k):
+    E = L.shape[1]
+    order = np.argsort(-L[:, ::-1], axis=1, kind="stable")
+    return (E - 1 - order[:, :k]).astype(np.int32)
+
+
+def _softmax_all_experts(L, ids):
+    z = np.exp(L - L.max(axis=1, keepdims=True))
+    z = z / z.sum(axis=1, keepdims=True)
+    return np.take_along_axis(z, ids.astype(np.int64), axis=1)
+
+
+def _ffn(swap=False, transpose_down=False, no_silu=False):
+    def f(X, q13, s13, q2, s2):
+        W13 = mo.dequant_mxfp4(q13, s13)
+        I = W13.shape[0] // 2
+        gate, up = (W13[I:], W13[:I]) if swap else (W13[:I], W13[I:])
+        g, u = X @ gate.T, X @ up.T
+        h = g * u if no_silu else mo.silu(g) * u
+        W2 = mo.dequant_mxfp4(q2, s2)
+        return h @ (W2 if transpose_down else W2.T)
+    return f
+
+
+def _combine_unweighted(y, w):
+    T, k = w.shape
+    return y.reshape(T, k, -1).sum(axis=1)
+
+
+def _tiles_unstable(topk_ids, E, BM):
+    off, srt, tiles, nt = _orig_build_tiles(topk_ids, E, BM)
+    flat = np.asarray(topk_ids).ravel()
+    srt = np.argsort(flat, kind="quicksort")[::-1].copy()
+    srt = srt[np.argsort(flat[srt], kind="stable")].astype(np.int32)
+    return off, srt, tiles, nt
+
+
+_orig_build_tiles = mo.build_tiles
+
+PINS = [
+    tdec.test_nibble_order_low_first,
+    tdec.test_e8m0_matches_torch_exhaustive,
+    tdec.test_dequant_exhaustive_codes_times_scales,
+    trout.test_topk_tie_rule_and_order,
+    trout.test_softmax_equals_renormalised_full_softmax,
+    lambda: trout.test_tiles_against_python_sort_and_invariants(17, 3, 5, 4),
+    tffn.test_permutation_weights_closed_form,
+    tffn.test_single_expert_equals_textbook_swiglu_mlp,
+    lambda: tffn.test_routed_equals_dense_then_select(4, 64, 8, 2, 64, False),
+]
+
+MUTATIONS = {
+    "nibble_high_first": ("unpack_codes", _unpack_high_first),
+    "e8m0_bias_126": ("decode_e8m0", _e8m0_bias_126),
+    "ties_to_higher_index": ("top_k", _topk_ties_high),
+    "softmax_over_all_experts": ("softmax_selected", _softmax_all_experts),
+    "gate_up_swapped": ("expert_ffn", _ffn(swap=True)),
+    "down_transposed": ("expert_ffn", _ffn(transpose_down=True)),
+    "no_silu": ("expert_ffn", _ffn(no_silu=True)),
+    "combine_unweighted": ("combine", _combine_unweighted),
+    "unstable_scatter": ("build_tiles", _tiles_unstable),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutation_is_caught(name, monkeypatch):
+    attr, fn = MUTATIONS[name]
+    monkeypatch.setattr(mo, attr, fn)
+    monkeypatch.setattr(oracle, attr, fn)
+    caught = []
+    for pin in PINS:
+        try:
+            pin()
+        except (AssertionError, ValueError):
+            caught.append(getattr(pin, "__name__", "lambda"))
+    assert caught, f"mutation {name} passed every pin"
