@@ -1,0 +1,225 @@
+/*
+ * moe_mxfp4.h - C ABI of the MI355X (gfx950) MXFP4 grouped-expert MoE layer.
+ *
+ * The layer is the gpt-oss mixture-of-experts block that the SimpleLLM
+ * write-up ("A 297-line kernel file that decodes faster than vLLM") profiles
+ * as "Router + top-k", "MoE gate/up + SwiGLU" and "MoE down + combine"
+ * (section "Where the time went"), with the expert weights kept in MXFP4 and
+ * routed through a per-expert tile table (section "Optimizations": "MXFP4 MoE
+ * on tensor cores", "Per-expert routing tile table", "MoE token tile follows
+ * tokens per expert").  The triton-kernels README's fused MoE dispatch
+ * (section "Quick Start") names the same pipeline: router with softmax
+ * gating and top-k, permute, expert FFN, unpermute.
+ *
+ * One layer call is three entry points, all enqueued on one stream:
+ *   moe_route        router logits -> top-k -> softmax over the k selected
+ *   moe_build_tiles  per-expert counts, offsets, stable sort, tile table
+ *   moe_forward      grouped gate/up GEMM + SwiGLU, grouped down GEMM,
+ *                    weighted combine back to token order
+ *
+ * Conventions shared by every entry point:
+ *   - Every array argument is a DEVICE pointer on the current HIP device,
+ *     allocated and owned by the caller.  The library allocates nothing,
+ *     keeps no state across calls (beyond a per-device architecture check),
+ *     never synchronises the host, and enqueues all work on `stream`
+ *     (NULL = the default stream).
+ *   - Arguments are validated on the host before anything is enqueued; on a
+ *     non-OK return nothing was enqueued and nothing was written.  A launch
+ *     that fails returns MOE_ERR_HIP.
+ *   - T == 0 is a no-op that returns MOE_OK.
+ *   - Device pointers to arrays read with 128-bit loads (x, w_router, the
+ *     packed weights, workspaces) must be 16-byte aligned (MOE_ERR_ALIGN).
+ *   - Only gfx950 devices are accepted (MOE_ERR_DEVICE).
+ *   - Calls on one stream are ordered; calls that share output or workspace
+ *     buffers on different streams race.
+ *
+ * Data layouts (row-major, C order):
+ *   x             bf16 bits, uint16 [T][H]
+ *   w_router      fp32 [E][H];  bias fp32 [E] or NULL
+ *   w13_q         uint8 [E][2I][H/2]  MXFP4 e2m1 codes, two per byte, the
+ *                 even K element in the low nibble; rows [0, I) are the gate
+ *                 projection W1, rows [I, 2I) the up projection W3
+ *   w13_s         uint8 [E][2I][H/32] E8M0 scales, one per 32 consecutive K
+ *                 elements of a row: value 2^(s-127), s = 255 is NaN
+ *   w2_q, w2_s    uint8 [E][H][I/2], uint8 [E][H][I/32]  down projection
+ *   topk_ids      int32 [T][k];  topk_weights fp32 [T][k]
+ *   expert_offsets int32 [E+1];  sorted_ids int32 [T*k]
+ *   tiles         int32 [tiles_max][3] rows (expert, row_start, rows)
+ *   num_tiles     int32 [1]
+ *   out           bf16 bits, uint16 [T][H]
+ *
+ * Numerics: router logits are accumulated in fp64 (bf16 x fp32 products are
+ * exact in fp64), so the top-k choice matches an exact evaluation whenever
+ * logits differ by more than ~1e-13.  Expert weights are decoded exactly to
+ * bf16 (exact for scale bytes 2..252) and multiplied on bf16 MFMA with fp32
+ * accumulation; h = silu(g)*u is rounded to bf16, y kept in fp32, and the
+ * combine accumulates in fp32 in slot order and rounds once to bf16.
+ */
+#ifndef MOE_MXFP4_H
+#define MOE_MXFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+struct ihipStream_t; /* hipStream_t is `struct ihipStream_t*` */
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL = 1,      /* a required pointer is NULL */
+  MOE_ERR_SHAPE = 2,     /* a size is out of the supported range */
+  MOE_ERR_ALIGN = 3,     /* a pointer is not 16-byte aligned */
+  MOE_ERR_WORKSPACE = 4, /* workspace smaller than the *_workspace_bytes query */
+  MOE_ERR_DEVICE = 5,    /* current device is not gfx950 or cannot be queried */
+  MOE_ERR_HIP = 6        /* a kernel launch failed */
+} moe_status;
+
+/* Static description of a status code (host). */
+const char* moe_status_string(int status);
+
+/* Library version string, e.g. "0.1.0" (host). */
+const char* moe_version(void);
+
+/* ------------------------------------------------------------------ limits */
+#define MOE_MAX_EXPERTS 256
+#define MOE_MAX_TOPK 8
+#define MOE_MAX_DIM 65536 /* largest H or I */
+
+/* Token tile for the tile table (host, pure function).  The SimpleLLM
+ * write-up pins the decode tile rather than autotuning it ("Fixed decode
+ * tiles") and grows the token tile with tokens per expert ("MoE token tile
+ * follows tokens per expert": 16 for decode, 32 or 64 for prefill).  Rule:
+ * with m = T*k/E expected rows per expert, 16 if m <= 16, 32 if m <= 48,
+ * else 64.  Returns 16 for degenerate inputs. */
+int moe_pick_bm(int T, int k, int E);
+
+/* Upper bound on num_tiles for any routing (host, pure function):
+ * min(T*k, ceil(T*k/BM) + min(E, T*k)).  The tiles array passed to
+ * moe_build_tiles / moe_forward must hold this many rows of 3 int32. */
+int64_t moe_tiles_max(int T, int k, int E, int BM);
+
+/* Workspace bytes moe_route needs (host, pure function; 0 when T == 0). */
+size_t moe_route_workspace_bytes(int T, int H, int E);
+
+/* Workspace bytes moe_forward needs (host, pure function): h bf16 [T*k][I]
+ * and y fp32 [T*k][H], each rounded up to 256 bytes. */
+size_t moe_forward_workspace_bytes(int T, int H, int I, int k);
+
+/* ------------------------------------------------------------- moe_route
+ * Router logits L[t][e] = sum_h x[t][h]*w_router[e][h] (+ bias[e]) in fp64,
+ * then per token the k largest logits in descending order (exact ties go to
+ * the lower expert index) and the softmax over those k logits.
+ * ("Where the time went": "Router + top-k"; triton-kernels README "Project
+ * Structure": moe/router.py "Softmax/sigmoid gating + top-k".)
+ *
+ *   x           [T][H] bf16 bits, 16-byte aligned
+ *   w_router    [E][H] fp32, 16-byte aligned
+ *   bias        [E] fp32 or NULL; added before top-k and softmax
+ *   T >= 0, 0 < H <= 65536, H % 32 == 0, 1 <= E <= 256, 1 <= k <= min(E, 8),
+ *   T*E < 2^31
+ *   topk_ids    out [T][k] int32
+ *   topk_weights out [T][k] fp32 (each row sums to 1 within 1e-6)
+ *   logits      out [T][E] fp64, or NULL if not wanted
+ *   workspace   >= moe_route_workspace_bytes(T, H, E), 16-byte aligned
+ * NaN logits make the choice unspecified (but in range).
+ */
+moe_status moe_route(const uint16_t* x, const float* w_router, const float* bias,
+                     int T, int H, int E, int k,
+                     int32_t* topk_ids, float* topk_weights, double* logits,
+                     void* workspace, size_t workspace_bytes,
+                     struct ihipStream_t* stream);
+
+/* ------------------------------------------------------- moe_build_tiles
+ * Per-expert tile table ("Optimizations": "Per-expert routing tile table" -
+ * each expert writes its own tiles instead of the GEMM searching a
+ * tiles x experts grid; "MoE token tile follows tokens per expert").
+ * Bit-exact and deterministic:
+ *   counts c_e = #{p : topk_ids[p] == e}, p = t*k + j the flat slot id
+ *   expert_offsets[0] = 0, expert_offsets[e+1] = expert_offsets[e] + c_e
+ *   sorted_ids = the slot ids ordered by expert, ascending p within an
+ *                expert (a stable counting sort)
+ *   tiles: for e ascending, for i in 0..ceil(c_e/BM)-1:
+ *          (e, expert_offsets[e] + i*BM, min(BM, c_e - i*BM))
+ *   num_tiles[0] = sum_e ceil(c_e/BM)
+ *
+ *   topk_ids    [T][k] int32; ids outside [0, E) are dropped from counts and
+ *               tiles (they are placed after expert_offsets[E] in
+ *               sorted_ids so every slot id still appears exactly once)
+ *   T >= 0, 1 <= k <= 8, 1 <= E <= 256, T*k < 2^31, BM in {16,32,64,128}
+ *   expert_offsets out [E+1]; sorted_ids out [T*k];
+ *   tiles out [moe_tiles_max(T,k,E,BM)][3] (rows past num_tiles untouched);
+ *   num_tiles out [1]
+ */
+moe_status moe_build_tiles(const int32_t* topk_ids, int T, int k, int E, int BM,
+                           int32_t* expert_offsets, int32_t* sorted_ids,
+                           int32_t* tiles, int32_t* num_tiles,
+                           struct ihipStream_t* stream);
+
+/* ----------------------------------------------------------- moe_forward
+ * For every tile (e, row_start, rows) and each slot p = sorted_ids[r],
+ * r in [row_start, row_start+rows), token t = p / k:
+ *   g = x[t] W1_e^T, u = x[t] W3_e^T, h[r] = silu(g) * u       (gate/up)
+ *   y[p] = h[r] W2_e^T                                          (down)
+ * then out[t] = sum_{j<k} topk_weights[t][j] * y[t*k + j]       (combine)
+ * with MXFP4 weights W = e2m1(code) * 2^(s-127).  ("MXFP4 MoE on tensor
+ * cores", "MoE gate/up + SwiGLU", "MoE down + combine"; the README's fused
+ * SwiGLU is silu(gate) * up.)  The combine uses no atomics; results are
+ * bit-identical from run to run.
+ *
+ *   x             [T][H] bf16 bits, 16-byte aligned
+ *   w13_q, w13_s, w2_q, w2_s   MXFP4 weights (layouts above), 16-byte aligned
+ *   topk_weights  [T][k] fp32 (from moe_route)
+ *   sorted_ids, tiles, num_tiles  from moe_build_tiles with the same T, k,
+ *                 E and BM; every slot id must appear once in sorted_ids
+ *   T >= 0, 0 < H, I <= 65536, H % 32 == 0, I % 32 == 0, 1 <= E <= 256,
+ *   1 <= k <= min(E, 8), BM in {16,32,64,128}, T*k < 2^31, E*2I < 2^31
+ *   workspace     >= moe_forward_workspace_bytes(T, H, I, k), 16-byte aligned
+ *   out           out [T][H] bf16 bits
+ * If topk_ids held ids outside [0, E) the output is unspecified, but every
+ * memory access stays inside the buffers described here.
+ */
+moe_status moe_forward(const uint16_t* x,
+                       const uint8_t* w13_q, const uint8_t* w13_s,
+                       const uint8_t* w2_q, const uint8_t* w2_s,
+                       const float* topk_weights, const int32_t* sorted_ids,
+                       const int32_t* tiles, const int32_t* num_tiles,
+                       int T, int H, int I, int E, int k, int BM,
+                       void* workspace, size_t workspace_bytes,
+                       uint16_t* out, struct ihipStream_t* stream);
+
+/* --------------------------------------------- the three steps of moe_forward
+ * moe_forward is exactly these three calls in order; they are exported so a
+ * caller can time or overlap them separately.  Arguments and constraints are
+ * those of moe_forward; h and y are caller buffers (device):
+ *   h  bf16 bits [T*k][I], row r = position r in sorted_ids
+ *   y  fp32 [T*k][H], row p = flat slot id p = t*k + j
+ */
+
+/* Grouped gate/up GEMM with fused SwiGLU ("Where the time went": "MoE
+ * gate/up + SwiGLU"; triton-kernels README "Fused SwiGLU": silu(gate) * up):
+ * h[r] = bf16(silu(x[t] W1_e^T) * (x[t] W3_e^T)) for every tiled row r. */
+moe_status moe_gateup_swiglu(const uint16_t* x, const uint8_t* w13_q, const uint8_t* w13_s,
+                             const int32_t* sorted_ids, const int32_t* tiles,
+                             const int32_t* num_tiles, int T, int H, int I, int E, int k, int BM,
+                             uint16_t* h, struct ihipStream_t* stream);
+
+/* Grouped down GEMM ("MoE down + combine"): y[sorted_ids[r]] = h[r] W2_e^T. */
+moe_status moe_down(const uint16_t* h, const uint8_t* w2_q, const uint8_t* w2_s,
+                    const int32_t* sorted_ids, const int32_t* tiles, const int32_t* num_tiles,
+                    int T, int H, int I, int E, int k, int BM, float* y,
+                    struct ihipStream_t* stream);
+
+/* Weighted combine ("MoE down + combine"; the README's unpermute):
+ * out[t] = bf16(sum_{j<k} topk_weights[t][j] * y[t*k + j]), fp32 in
+ * ascending j.  y must be 16-byte aligned. */
+moe_status moe_combine(const float* y, const float* topk_weights, int T, int H, int k,
+                       uint16_t* out, struct ihipStream_t* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MXFP4_H */

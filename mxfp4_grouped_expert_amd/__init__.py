@@ -1,0 +1,15 @@
+"""MI355X (gfx950) MXFP4 grouped-expert MoE layer.
+
+The layer runs as three calls of the HIP library libmoe_mxfp4.so (see
+include/moe_mxfp4.h): moe_route, moe_build_tiles and moe_forward.  This
+package is the thin Python binding over them; torch provides device memory
+and streams only.
+"""
+from .binding import (MoeError, LIB_PATH, load, version, status_string, pick_bm, tiles_max,
+                      route_workspace_bytes, forward_workspace_bytes, moe_route,
+                      moe_build_tiles, moe_forward, moe_gateup_swiglu, moe_down, moe_combine)
+from .layer import MoeLayer
+
+__all__ = ["MoeError", "LIB_PATH", "load", "version", "status_string", "pick_bm", "tiles_max",
+           "route_workspace_bytes", "forward_workspace_bytes", "moe_route", "moe_build_tiles",
+           "moe_forward", "moe_gateup_swiglu", "moe_down", "moe_combine", "MoeLayer"]

@@ -1,0 +1,219 @@
+// C ABI of the MXFP4 grouped-expert MoE library (declared in moe_mxfp4.h).
+//
+// Every entry point validates its arguments on the host before anything is
+// enqueued, checks once per device that the device is gfx950, then enqueues
+// its kernels on the caller's stream and returns without synchronising.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstring>
+
+#include "../../include/moe_mxfp4.h"
+#include "moe_launch.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_device_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+moe_status check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return MOE_ERR_DEVICE;
+  }
+  int st = g_device_state[dev].load(std::memory_order_acquire);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return MOE_ERR_DEVICE;
+    }
+    st = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_device_state[dev].store(st, std::memory_order_release);
+  }
+  return st == 1 ? MOE_OK : MOE_ERR_DEVICE;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t round256(size_t n) { return (n + 255) & ~size_t(255); }
+
+bool valid_bm(int BM) { return BM == 16 || BM == 32 || BM == 64 || BM == 128; }
+
+moe_status finish_launches() {
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+hipStream_t as_stream(struct ihipStream_t* s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK: success";
+    case MOE_ERR_NULL: return "MOE_ERR_NULL: a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "MOE_ERR_SHAPE: a size is outside the supported range";
+    case MOE_ERR_ALIGN: return "MOE_ERR_ALIGN: a pointer is not 16-byte aligned";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace is too small";
+    case MOE_ERR_DEVICE: return "MOE_ERR_DEVICE: current device is not gfx950 or not usable";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP: a kernel launch failed";
+    default: return "unknown moe_status";
+  }
+}
+
+const char* moe_version(void) { return "0.1.0"; }
+
+int moe_pick_bm(int T, int k, int E) {
+  if (T <= 0 || k <= 0 || E <= 0) return 16;
+  const double m = (double)T * (double)k / (double)E;
+  if (m <= 16.0) return 16;
+  if (m <= 48.0) return 32;
+  return 64;
+}
+
+int64_t moe_tiles_max(int T, int k, int E, int BM) {
+  if (T <= 0 || k <= 0 || E <= 0 || BM <= 0) return 0;
+  const int64_t n = (int64_t)T * k;
+  const int64_t a = (n + BM - 1) / BM + (E < n ? E : n);
+  return a < n ? a : n;
+}
+
+size_t moe_route_workspace_bytes(int T, int H, int E) {
+  if (T <= 0 || H <= 0 || E <= 0) return 0;
+  return round256(moe::router_partial_bytes(T, H, E));
+}
+
+size_t moe_forward_workspace_bytes(int T, int H, int I, int k) {
+  if (T <= 0 || H <= 0 || I <= 0 || k <= 0) return 0;
+  const size_t n = (size_t)T * (size_t)k;
+  return round256(n * (size_t)I * 2) + round256(n * (size_t)H * 4);
+}
+
+moe_status moe_route(const uint16_t* x, const float* w_router, const float* bias, int T, int H,
+                     int E, int k, int32_t* topk_ids, float* topk_weights, double* logits,
+                     void* workspace, size_t workspace_bytes, struct ihipStream_t* stream) {
+  if (T < 0 || H <= 0 || H % 32 != 0 || H > MOE_MAX_DIM || E < 1 || E > MOE_MAX_EXPERTS || k < 1 ||
+      k > MOE_MAX_TOPK || k > E || (int64_t)T * E >= (int64_t(1) << 31) ||
+      (int64_t)T * H >= (int64_t(1) << 40))
+    return MOE_ERR_SHAPE;
+  if (T == 0) return MOE_OK;
+  if (!x || !w_router || !topk_ids || !topk_weights || !workspace) return MOE_ERR_NULL;
+  if (!aligned16(x) || !aligned16(w_router) || !aligned16(workspace)) return MOE_ERR_ALIGN;
+  if (workspace_bytes < moe_route_workspace_bytes(T, H, E)) return MOE_ERR_WORKSPACE;
+  moe_status st = check_device();
+  if (st != MOE_OK) return st;
+  (void)hipGetLastError();
+  const moe::RouterPlan plan = moe::router_plan(T, H, E);
+  double* partial = static_cast<double*>(workspace);
+  moe::launch_router_logits(x, w_router, T, H, E, plan, partial, as_stream(stream));
+  moe::launch_router_topk(partial, bias, T, E, k, plan.splits, topk_ids, topk_weights, logits,
+                          as_stream(stream));
+  return finish_launches();
+}
+
+moe_status moe_build_tiles(const int32_t* topk_ids, int T, int k, int E, int BM,
+                           int32_t* expert_offsets, int32_t* sorted_ids, int32_t* tiles,
+                           int32_t* num_tiles, struct ihipStream_t* stream) {
+  if (T < 0 || k < 1 || k > MOE_MAX_TOPK || E < 1 || E > MOE_MAX_EXPERTS || !valid_bm(BM) ||
+      (int64_t)T * k >= (int64_t(1) << 31))
+    return MOE_ERR_SHAPE;
+  if (T == 0) return MOE_OK;
+  if (!topk_ids || !expert_offsets || !sorted_ids || !tiles || !num_tiles) return MOE_ERR_NULL;
+  moe_status st = check_device();
+  if (st != MOE_OK) return st;
+  (void)hipGetLastError();
+  moe::launch_build_tiles(topk_ids, T * k, E, BM, expert_offsets, sorted_ids, tiles, num_tiles,
+                          as_stream(stream));
+  return finish_launches();
+}
+
+namespace {
+
+bool forward_shape_ok(int T, int H, int I, int E, int k, int BM) {
+  return T >= 0 && H > 0 && I > 0 && H % 32 == 0 && I % 32 == 0 && H <= MOE_MAX_DIM &&
+         I <= MOE_MAX_DIM && E >= 1 && E <= MOE_MAX_EXPERTS && k >= 1 && k <= MOE_MAX_TOPK &&
+         k <= E && valid_bm(BM) && (int64_t)T * k < (int64_t(1) << 31) &&
+         (int64_t)E * 2 * I < (int64_t(1) << 31) && (int64_t)E * H < (int64_t(1) << 31);
+}
+
+}  // namespace
+
+moe_status moe_gateup_swiglu(const uint16_t* x, const uint8_t* w13_q, const uint8_t* w13_s,
+                             const int32_t* sorted_ids, const int32_t* tiles,
+                             const int32_t* num_tiles, int T, int H, int I, int E, int k, int BM,
+                             uint16_t* h, struct ihipStream_t* stream) {
+  if (!forward_shape_ok(T, H, I, E, k, BM)) return MOE_ERR_SHAPE;
+  if (T == 0) return MOE_OK;
+  if (!x || !w13_q || !w13_s || !sorted_ids || !tiles || !num_tiles || !h) return MOE_ERR_NULL;
+  if (!aligned16(x) || !aligned16(w13_q)) return MOE_ERR_ALIGN;
+  moe_status st = check_device();
+  if (st != MOE_OK) return st;
+  (void)hipGetLastError();
+  moe::launch_gateup_swiglu(x, w13_q, w13_s, sorted_ids, tiles, num_tiles,
+                            (int)moe_tiles_max(T, k, E, BM), T, H, I, E, k, h, as_stream(stream));
+  return finish_launches();
+}
+
+moe_status moe_down(const uint16_t* h, const uint8_t* w2_q, const uint8_t* w2_s,
+                    const int32_t* sorted_ids, const int32_t* tiles, const int32_t* num_tiles,
+                    int T, int H, int I, int E, int k, int BM, float* y,
+                    struct ihipStream_t* stream) {
+  if (!forward_shape_ok(T, H, I, E, k, BM)) return MOE_ERR_SHAPE;
+  if (T == 0) return MOE_OK;
+  if (!h || !w2_q || !w2_s || !sorted_ids || !tiles || !num_tiles || !y) return MOE_ERR_NULL;
+  if (!aligned16(h) || !aligned16(w2_q)) return MOE_ERR_ALIGN;
+  moe_status st = check_device();
+  if (st != MOE_OK) return st;
+  (void)hipGetLastError();
+  moe::launch_down(h, w2_q, w2_s, sorted_ids, tiles, num_tiles, (int)moe_tiles_max(T, k, E, BM),
+                   T, H, I, E, k, y, as_stream(stream));
+  return finish_launches();
+}
+
+moe_status moe_combine(const float* y, const float* topk_weights, int T, int H, int k,
+                       uint16_t* out, struct ihipStream_t* stream) {
+  if (T < 0 || H <= 0 || H % 32 != 0 || H > MOE_MAX_DIM || k < 1 || k > MOE_MAX_TOPK ||
+      (int64_t)T * k >= (int64_t(1) << 31))
+    return MOE_ERR_SHAPE;
+  if (T == 0) return MOE_OK;
+  if (!y || !topk_weights || !out) return MOE_ERR_NULL;
+  if (!aligned16(y)) return MOE_ERR_ALIGN;
+  moe_status st = check_device();
+  if (st != MOE_OK) return st;
+  (void)hipGetLastError();
+  moe::launch_combine(y, topk_weights, T, H, k, out, as_stream(stream));
+  return finish_launches();
+}
+
+moe_status moe_forward(const uint16_t* x, const uint8_t* w13_q, const uint8_t* w13_s,
+                       const uint8_t* w2_q, const uint8_t* w2_s, const float* topk_weights,
+                       const int32_t* sorted_ids, const int32_t* tiles, const int32_t* num_tiles,
+                       int T, int H, int I, int E, int k, int BM, void* workspace,
+                       size_t workspace_bytes, uint16_t* out, struct ihipStream_t* stream) {
+  if (!forward_shape_ok(T, H, I, E, k, BM)) return MOE_ERR_SHAPE;
+  if (T == 0) return MOE_OK;
+  if (!x || !w13_q || !w13_s || !w2_q || !w2_s || !topk_weights || !sorted_ids || !tiles ||
+      !num_tiles || !workspace || !out)
+    return MOE_ERR_NULL;
+  if (!aligned16(x) || !aligned16(w13_q) || !aligned16(w2_q) || !aligned16(workspace))
+    return MOE_ERR_ALIGN;
+  if (workspace_bytes < moe_forward_workspace_bytes(T, H, I, k)) return MOE_ERR_WORKSPACE;
+  moe_status st = check_device();
+  if (st != MOE_OK) return st;
+  (void)hipGetLastError();
+  const int64_t tmax = moe_tiles_max(T, k, E, BM);
+  const size_t nslots = (size_t)T * (size_t)k;
+  uint16_t* h = static_cast<uint16_t*>(workspace);
+  float* y = reinterpret_cast<float*>(static_cast<char*>(workspace) + round256(nslots * I * 2));
+  hipStream_t s = as_stream(stream);
+  moe::launch_gateup_swiglu(x, w13_q, w13_s, sorted_ids, tiles, num_tiles, (int)tmax, T, H, I, E,
+                            k, h, s);
+  moe::launch_down(h, w2_q, w2_s, sorted_ids, tiles, num_tiles, (int)tmax, T, H, I, E, k, y, s);
+  moe::launch_combine(y, topk_weights, T, H, k, out, s);
+  return finish_launches();
+}
+
+}  // extern "C"

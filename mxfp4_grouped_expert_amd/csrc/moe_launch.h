@@ -1,0 +1,43 @@
+// Internal launchers, one per kernel.  Callers (moe_api.hip) validate every
+// argument first; these only size grids and enqueue on `stream`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Router: fp64 partial logits over `splits` K-ranges, then top-k + softmax.
+struct RouterPlan {
+  int splits;      // number of K-ranges
+  int split_len;   // elements per K-range (multiple of 4)
+};
+RouterPlan router_plan(int T, int H, int E);
+size_t router_partial_bytes(int T, int H, int E);
+void launch_router_logits(const uint16_t* x, const float* w_router, int T, int H, int E,
+                          const RouterPlan& plan, double* partial, hipStream_t stream);
+void launch_router_topk(const double* partial, const float* bias, int T, int E, int k,
+                        int splits, int32_t* topk_ids, float* topk_weights, double* logits,
+                        hipStream_t stream);
+
+// Tile table: one workgroup counts, scans and scatters.
+void launch_build_tiles(const int32_t* topk_ids, int N, int E, int BM, int32_t* expert_offsets,
+                        int32_t* sorted_ids, int32_t* tiles, int32_t* num_tiles,
+                        hipStream_t stream);
+
+// Grouped expert GEMMs over the tile table.
+void launch_gateup_swiglu(const uint16_t* x, const uint8_t* w13_q, const uint8_t* w13_s,
+                          const int32_t* sorted_ids, const int32_t* tiles,
+                          const int32_t* num_tiles, int tiles_max, int T, int H, int I, int E,
+                          int k, uint16_t* h, hipStream_t stream);
+void launch_down(const uint16_t* h, const uint8_t* w2_q, const uint8_t* w2_s,
+                 const int32_t* sorted_ids, const int32_t* tiles, const int32_t* num_tiles,
+                 int tiles_max, int T, int H, int I, int E, int k, float* y,
+                 hipStream_t stream);
+
+// Weighted combine back to token order.
+void launch_combine(const float* y, const float* topk_weights, int T, int H, int k,
+                    uint16_t* out, hipStream_t stream);
+
+}  // namespace moe

@@ -1,0 +1,124 @@
+"""MoeLayer: one MXFP4 MoE layer with every buffer allocated up front.
+
+A call enqueues the library's three entry points (moe_route,
+moe_build_tiles, moe_forward) on the current stream with preallocated
+outputs and workspaces, so it allocates nothing per call and can be
+captured in a HIP graph.  Weights are device tensors in the library's
+canonical layout (see include/moe_mxfp4.h).
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import torch
+
+from . import binding as B
+
+
+class MoeLayer:
+    def __init__(self, w_router: torch.Tensor, bias: Optional[torch.Tensor],
+                 w13_q: torch.Tensor, w13_s: torch.Tensor, w2_q: torch.Tensor,
+                 w2_s: torch.Tensor, k: int):
+        self.device = w13_q.device
+        self.E, I2, Hh = w13_q.shape
+        self.H, self.I, self.k = Hh * 2, I2 // 2, int(k)
+        self.w_router, self.bias = w_router, bias
+        self.w13_q, self.w13_s, self.w2_q, self.w2_s = w13_q, w13_s, w2_q, w2_s
+        self.T = None
+
+    def set_weights(self, w13_q, w13_s, w2_q, w2_s):
+        """Point the layer at another copy of the expert weights (same shapes)."""
+        self.w13_q, self.w13_s, self.w2_q, self.w2_s = w13_q, w13_s, w2_q, w2_s
+
+    def plan(self, T: int, BM: Optional[int] = None):
+        """Allocate every buffer for batches of T tokens."""
+        dev, E, H, I, k = self.device, self.E, self.H, self.I, self.k
+        self.T = T
+        self.BM = B.pick_bm(T, k, E) if BM is None else BM
+        self.topk_ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+        self.topk_weights = torch.empty((T, k), dtype=torch.float32, device=dev)
+        self.route_ws = torch.empty(max(B.route_workspace_bytes(T, H, E), 16), dtype=torch.uint8,
+                                    device=dev)
+        self.offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+        self.sorted_ids = torch.empty(max(T * k, 1), dtype=torch.int32, device=dev)
+        self.tiles_max = B.tiles_max(T, k, E, self.BM)
+        self.tiles = torch.empty((max(self.tiles_max, 1), 3), dtype=torch.int32, device=dev)
+        self.num_tiles = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.fwd_ws = torch.empty(max(B.forward_workspace_bytes(T, H, I, k), 16),
+                                  dtype=torch.uint8, device=dev)
+        self.out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        return self
+
+    def _args(self):
+        lib = B.load()
+        s = ctypes.c_void_p(torch.cuda.current_stream(self.device).cuda_stream)
+        return lib, s
+
+    @staticmethod
+    def _p(t):
+        return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+    def route_only(self, x: torch.Tensor):
+        """moe_route into the layer's buffers."""
+        lib, s = self._args()
+        p = self._p
+        T, E, H, k = x.shape[0], self.E, self.H, self.k
+        B._check(lib.moe_route(p(x), p(self.w_router), p(self.bias), T, H, E, k,
+                               p(self.topk_ids), p(self.topk_weights), None, p(self.route_ws),
+                               self.route_ws.numel(), s), "moe_route")
+
+    def tiles_only(self):
+        """moe_build_tiles from the layer's topk_ids."""
+        lib, s = self._args()
+        p = self._p
+        B._check(lib.moe_build_tiles(p(self.topk_ids), self.T, self.k, self.E, self.BM,
+                                     p(self.offsets), p(self.sorted_ids), p(self.tiles),
+                                     p(self.num_tiles), s), "moe_build_tiles")
+
+    def _h_y(self):
+        n = self.T * self.k
+        h_bytes = (n * self.I * 2 + 255) // 256 * 256
+        return (self.fwd_ws[:h_bytes], self.fwd_ws[h_bytes:])
+
+    def gateup_only(self, x: torch.Tensor):
+        """moe_gateup_swiglu into the layer's h workspace."""
+        lib, s = self._args()
+        p = self._p
+        h, _ = self._h_y()
+        B._check(lib.moe_gateup_swiglu(p(x), p(self.w13_q), p(self.w13_s), p(self.sorted_ids),
+                                       p(self.tiles), p(self.num_tiles), self.T, self.H, self.I,
+                                       self.E, self.k, self.BM, p(h), s), "moe_gateup_swiglu")
+
+    def down_only(self):
+        """moe_down from the h workspace into the y workspace."""
+        lib, s = self._args()
+        p = self._p
+        h, y = self._h_y()
+        B._check(lib.moe_down(p(h), p(self.w2_q), p(self.w2_s), p(self.sorted_ids), p(self.tiles),
+                              p(self.num_tiles), self.T, self.H, self.I, self.E, self.k, self.BM,
+                              p(y), s), "moe_down")
+
+    def combine_only(self):
+        """moe_combine from the y workspace into the layer's output."""
+        lib, s = self._args()
+        p = self._p
+        _, y = self._h_y()
+        B._check(lib.moe_combine(p(y), p(self.topk_weights), self.T, self.H, self.k, p(self.out),
+                                 s), "moe_combine")
+
+    def __call__(self, x: torch.Tensor) -> torch.Tensor:
+        """One layer call: moe_route, moe_build_tiles, moe_forward."""
+        T = x.shape[0]
+        if self.T != T:
+            self.plan(T)
+        lib, s = self._args()
+        p = self._p
+        E, H, I, k, BM = self.E, self.H, self.I, self.k, self.BM
+        self.route_only(x)
+        self.tiles_only()
+        B._check(lib.moe_forward(p(x), p(self.w13_q), p(self.w13_s), p(self.w2_q), p(self.w2_s),
+                                 p(self.topk_weights), p(self.sorted_ids), p(self.tiles),
+                                 p(self.num_tiles), T, H, I, E, k, BM, p(self.fwd_ws),
+                                 self.fwd_ws.numel(), p(self.out), s), "moe_forward")
+        return self.out

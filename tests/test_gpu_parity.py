@@ -1,0 +1,172 @@
+"""GPU parity: the HIP library against the float64 oracle (needs a gfx950 GPU).
+
+Covers the five gpt-oss-shaped workloads (tiny; 20b decode T=1; 20b decode
+T=64 with a skewed router; 120b decode T=64; 120b prefill T=4096), small
+random shapes with ragged K-block counts and multi-chunk tile scatters, and
+the method's degenerate cases.  At the two 120b workloads routing and the
+tile table are compared in full and the output on sampled tokens.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mxfp4_grouped_expert_amd as moe
+import oracle
+from moe_inputs import (identical_experts, make_activations, make_random, make_weights,
+                        make_workload, WORKLOADS)
+
+from gpu_helpers import (assert_out_close, assert_routing_equal, assert_tiles_equal, check_all,
+                         log, run_gpu, to_device)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    moe.load()  # fails loudly if the HIP library is missing
+
+
+@pytest.fixture(scope="module")
+def w120b():
+    w = WORKLOADS[3]
+    return make_weights(w.E, w.H, w.I, w.model_id)
+
+
+# ------------------------------------------------------------- workloads --
+
+@pytest.mark.parametrize("BM", [16, 32, 64, 128])
+def test_tiny_workload(BM):
+    check_all(make_workload(0), BM)
+
+
+@pytest.mark.parametrize("wid", [1, 2])
+def test_gptoss20b_decode(wid):
+    inp = make_workload(wid)
+    check_all(inp, moe.pick_bm(inp["T"], inp["k"], inp["E"]))
+
+
+def test_gptoss120b_decode_T64(w120b):
+    inp = make_workload(3, weights=False)
+    inp.update(w120b)
+    check_all(inp, moe.pick_bm(inp["T"], inp["k"], inp["E"]), tokens=np.arange(0, 64, 4))
+
+
+def test_gptoss120b_prefill_T4096(w120b):
+    inp = make_workload(4, weights=False)
+    inp.update(w120b)
+    BM = moe.pick_bm(inp["T"], inp["k"], inp["E"])
+    toks = np.array([0, 1, 511, 1024, 2047, 2048, 3000, 4095])
+    res = check_all(inp, BM, tokens=toks)
+    # every token has k distinct experts and the table covers every slot once
+    ids = res["gpu"]["topk_ids"]
+    assert all(len(set(r)) == inp["k"] for r in ids)
+    assert sorted(res["gpu"]["sorted_ids"].tolist()) == list(range(inp["T"] * inp["k"]))
+
+
+@pytest.mark.parametrize("BM", [16, 32, 64, 128])
+def test_tile_table_all_bm_at_prefill(w120b, BM):
+    inp = make_workload(4, weights=False)
+    log(f"prefill tile table BM={BM}")
+    d = {"x": torch.from_numpy(inp["x"].view(np.int16)).cuda(),
+         "w_router": torch.from_numpy(inp["w_router"]).cuda()}
+    ids, wts, _ = moe.moe_route(d["x"], d["w_router"], None, inp["k"])
+    off, srt, tiles, nt = moe.moe_build_tiles(ids, inp["E"], BM)
+    torch.cuda.synchronize()
+    ref = oracle.build_tiles(ids.cpu().numpy(), inp["E"], BM)
+    n = int(nt.item())
+    assert n == ref[3]
+    np.testing.assert_array_equal(off.cpu().numpy(), ref[0])
+    np.testing.assert_array_equal(srt.cpu().numpy(), ref[1])
+    np.testing.assert_array_equal(tiles[:n].cpu().numpy(), ref[2])
+
+
+# ------------------------------------------------------ random / ragged --
+
+RANDOM_CASES = [
+    # T, H, E, k, I, bias, router_std, BM
+    (1, 64, 1, 1, 32, False, 0.02, 16),
+    (3, 96, 2, 2, 160, True, 0.3, 16),
+    (17, 544, 8, 4, 96, False, 0.3, 16),     # 17 K-blocks: ragged last step
+    (64, 256, 33, 4, 512, True, 0.3, 16),
+    (257, 128, 8, 2, 64, False, 0.5, 64),    # several M-blocks per tile
+    (700, 64, 33, 2, 32, True, 0.5, 32),     # tile scatter over 2 chunks
+    (4100, 32, 256, 8, 32, False, 1.0, 128), # E and k at their maxima, 33 chunks
+    (40, 2880, 4, 4, 64, False, 0.02, 32),   # k = E: every expert used
+]
+
+
+@pytest.mark.parametrize("case", RANDOM_CASES, ids=lambda c: "T{}_H{}_E{}_k{}_I{}".format(*c[:5]))
+def test_random_shapes(case):
+    T, H, E, k, I, bias, std, BM = case
+    inp = make_random(T=T, H=H, E=E, k=k, I=I, seed=T + H + E, router_bias=bias, router_std=std)
+    check_all(inp, BM)
+
+
+def test_wide_scale_range():
+    T, H, E, k, I = 9, 192, 4, 2, 96
+    inp = make_random(T=T, H=H, E=E, k=k, I=I, seed=5, router_std=0.3)
+    inp.update(make_weights(E, H, I, 77, scale_lo=112, scale_hi=134))
+    inp["name"] = "wide_scales_112_134"
+    check_all(inp, 16)
+
+
+# ------------------------------------------------------ degenerate cases --
+
+def test_zero_tokens_is_a_noop():
+    inp = make_random(T=1, H=64, E=4, k=2, I=32, seed=1)
+    d = to_device(inp)
+    x0 = d["x"][:0]
+    ids, wts, _ = moe.moe_route(x0, d["w_router"], None, 2)
+    off, srt, tiles, nt = moe.moe_build_tiles(ids, 4, 16)
+    out = moe.moe_forward(x0, d["w13_q"], d["w13_s"], d["w2_q"], d["w2_s"], wts, srt, tiles, nt,
+                          16)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 64) and ids.shape == (0, 2)
+
+
+def test_all_zero_router_ties_go_to_lower_experts():
+    inp = make_random(T=5, H=64, E=6, k=3, I=32, seed=2)
+    inp["w_router"] = np.zeros_like(inp["w_router"])
+    inp["name"] = "zero_router"
+    res = check_all(inp, 16)
+    assert np.all(res["gpu"]["topk_ids"] == np.arange(3))
+    np.testing.assert_allclose(res["gpu"]["topk_weights"], 1 / 3, rtol=0, atol=1e-7)
+
+
+def test_identical_experts_output_independent_of_routing():
+    inp = identical_experts(make_random(T=12, H=128, E=5, k=2, I=64, seed=3, router_std=0.5))
+    inp["name"] = "identical_experts"
+    res = check_all(inp, 16)
+    one = make_random(T=12, H=128, E=5, k=2, I=64, seed=3, router_std=0.5)
+    one = identical_experts(one)
+    one["w_router"] = np.zeros_like(one["w_router"])
+    one["name"] = "identical_experts_zero_router"
+    res2 = check_all(one, 16)
+    assert_out_close(res["gpu"]["out"], res2["ref"]["out"], "identical experts vs fixed routing")
+
+
+def test_single_expert_k1():
+    check_all(make_random(T=33, H=96, E=1, k=1, I=64, seed=4), 16)
+
+
+def test_deterministic_bitwise():
+    inp = make_workload(2)
+    d = to_device(inp)
+    log("determinism: two runs of the 20b T=64 layer")
+    a = run_gpu(d, inp["k"], 16)
+    b = run_gpu(d, inp["k"], 16)
+    for key in ("topk_ids", "topk_weights", "logits", "sorted_ids", "tiles", "out"):
+        np.testing.assert_array_equal(a[key], b[key], err_msg=key)
+
+
+def test_logits_match_oracle_in_fp64():
+    inp = make_workload(2, weights=False)
+    d = {"x": torch.from_numpy(inp["x"].view(np.int16)).cuda(),
+         "w_router": torch.from_numpy(inp["w_router"]).cuda(),
+         "bias": torch.from_numpy(inp["bias"]).cuda()}
+    log("router logits vs float64")
+    _, _, logits = moe.moe_route(d["x"], d["w_router"], d["bias"], inp["k"], want_logits=True)
+    ref = oracle.router_logits(inp["x"], inp["w_router"], inp["bias"])
+    np.testing.assert_allclose(logits.cpu().numpy(), ref, rtol=0, atol=1e-12)
