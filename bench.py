@@ -14,10 +14,9 @@ k=4, I=2880).  Timing:
     stream, synchronised on both sides.  R copies of the expert weights are
     rotated so that R x (bytes one call touches) >= 3 x the 256 MB Infinity
     Cache, which keeps repeated calls from being served by it;
-  * per-kernel durations: the same calls issued eagerly behind a GPU-side
-    blocker (so the host is never the bottleneck), with HIP events on the
-    launch stream around each entry point; the dominant kernel's average
-    duration gives the roofline fraction;
+  * per-kernel durations: for each entry point a HIP graph of back-to-back
+    launches of it alone, timed with HIP events on the launch stream; the
+    dominant kernel's average launch duration gives the roofline fraction;
   * cpu_baseline: the float64 oracle on this host's cores, on a bounded
     sample of the same workload.
 Prints one JSON line.
@@ -51,6 +50,8 @@ def parse_args():
     ap.add_argument("--no-graph", action="store_true", help="time eager calls instead of graphs")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 256 MiB device copy (known bytes) for counter scaling")
     return ap.parse_args()
 
 
@@ -188,35 +189,50 @@ def main():
     ms_per_step = start.elapsed_time(end) / steps
     us = ms_per_step * 1e3
 
-    # ---- per-kernel durations: eager calls queued behind a GPU-side blocker
-    kt = {"route": [], "tiles": [], "gateup": [], "down": [], "combine": []}
-    n_kernel_steps = min(steps, 64)
-    big = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-    with torch.cuda.stream(stream):
-        for _ in range(8):                      # ~GB of copies: the host runs ahead
-            big.copy_(big.flip(0))
-        evs = []
-        for i in range(n_kernel_steps):
-            layer.set_weights(*copies[i % R])
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
-            e[0].record(stream)
-            layer.route_only(x)
-            e[1].record(stream)
-            layer.tiles_only()
-            e[2].record(stream)
-            layer.gateup_only(x)
-            e[3].record(stream)
-            layer.down_only()
-            e[4].record(stream)
-            layer.combine_only()
-            e[5].record(stream)
-            evs.append(e)
-    torch.cuda.synchronize()
-    for e in evs:
-        for j, name in enumerate(kt):
-            kt[name].append(e[j].elapsed_time(e[j + 1]) * 1e3)
-    kernel_us = {name: float(np.mean(v)) for name, v in kt.items()}
-    del big
+    # ---- per-kernel durations: for each entry point, a HIP graph of R
+    # back-to-back launches of it alone (weights rotating as in the headline
+    # loop), replayed between two events on the launch stream.  The layer
+    # buffers hold a valid routing and tile table from the calls above.
+    parts = {
+        "route": lambda r: layer.route_only(x),
+        "tiles": lambda r: layer.tiles_only(),
+        "gateup": lambda r: (layer.set_weights(*copies[r]), layer.gateup_only(x)),
+        "down": lambda r: (layer.set_weights(*copies[r]), layer.down_only()),
+        "combine": lambda r: layer.combine_only(),
+    }
+    kernel_us = {}
+    reps = max(1, min(steps, 256) // R)
+    for name, fn in parts.items():
+        with torch.cuda.stream(stream):
+            if graphs:
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    for r in range(R):
+                        fn(r)
+                g.replay()
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(reps):
+                    g.replay()
+                e1.record(stream)
+            else:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(reps):
+                    for r in range(R):
+                        fn(r)
+                e1.record(stream)
+        torch.cuda.synchronize()
+        kernel_us[name] = e0.elapsed_time(e1) * 1e3 / (reps * R)
+
+    if args.calibrate_copy:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     gu_us = kernel_us["gateup"]
     if T <= 64:

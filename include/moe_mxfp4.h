@@ -89,11 +89,14 @@ const char* moe_version(void);
 #define MOE_MAX_DIM 65536 /* largest H or I */
 
 /* Token tile for the tile table (host, pure function).  The SimpleLLM
- * write-up pins the decode tile rather than autotuning it ("Fixed decode
- * tiles") and grows the token tile with tokens per expert ("MoE token tile
- * follows tokens per expert": 16 for decode, 32 or 64 for prefill).  Rule:
- * with m = T*k/E expected rows per expert, 16 if m <= 16, 32 if m <= 48,
- * else 64.  Returns 16 for degenerate inputs. */
+ * write-up pins the tile rather than autotuning it ("Fixed decode tiles")
+ * and grows the token tile with tokens per expert ("MoE token tile follows
+ * tokens per expert"), so that an expert's weights are unpacked once rather
+ * than once per small tile.  An expert receives at most one slot per token,
+ * so BM >= T keeps every expert in one tile.  Rule: the smallest of
+ * 16, 32, 64, 128 that is >= T (128 when T > 64).  The kernels process a
+ * tile's rows in passes of at most 16 while its weights stay in registers,
+ * so a large BM costs nothing at small T.  Returns 16 for T <= 16. */
 int moe_pick_bm(int T, int k, int E);
 
 /* Upper bound on num_tiles for any routing (host, pure function):

@@ -23,14 +23,24 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   if (idx >= (long long)T * cols4) return;
   const int t = (int)(idx / cols4);
   const int c = (int)(idx % cols4);
+  float wj[kMaxTopk];
+  float4 v[kMaxTopk];
+#pragma unroll
+  for (int j = 0; j < kMaxTopk; ++j) {  // all k loads in flight together
+    if (j < k) {
+      wj[j] = w[(size_t)t * k + j];
+      v[j] = reinterpret_cast<const float4*>(y + ((size_t)t * k + j) * H)[c];
+    }
+  }
   float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-  for (int j = 0; j < k; ++j) {
-    const float wj = w[(size_t)t * k + j];
-    const float4 v = reinterpret_cast<const float4*>(y + ((size_t)t * k + j) * H)[c];
-    a0 = fmaf(wj, v.x, a0);
-    a1 = fmaf(wj, v.y, a1);
-    a2 = fmaf(wj, v.z, a2);
-    a3 = fmaf(wj, v.w, a3);
+#pragma unroll
+  for (int j = 0; j < kMaxTopk; ++j) {
+    if (j < k) {
+      a0 = fmaf(wj[j], v[j].x, a0);
+      a1 = fmaf(wj[j], v[j].y, a1);
+      a2 = fmaf(wj[j], v[j].z, a2);
+      a3 = fmaf(wj[j], v[j].w, a3);
+    }
   }
   uint2 o;
   o.x = (uint32_t)float_to_bf16(a0) | ((uint32_t)float_to_bf16(a1) << 16);

@@ -10,20 +10,27 @@
 // v_cvt_scalef32_pk_bf16_fp4, which turns one byte (two e2m1 codes) into two
 // bf16 already multiplied by the block's E8M0 scale.
 //
-// Work split.  A workgroup (4 waves) owns one tile (<= BM slots of one
-// expert) and 16 output rows of the weight matrix (for gate/up: gate rows
-// n..n+15 and the matching up rows I+n..I+n+15, so SwiGLU fuses into the
-// epilogue).  The reduction dimension is cut into 32-element MX blocks; block
-// b = 16*step + 4*wave + group goes to lane group `group` (lanes 16*group ..
-// 16*group+15) of wave `wave`.  Each lane then issues one 16-byte load per
-// weight row per step: exactly one MX block (32 codes) plus its scale byte,
-// and the 16 lanes of a group read 16 rows while the 4 groups of a wave read
-// 64 contiguous bytes of each row.  Since an MFMA sums over its whole K
-// range, the order in which K elements are assigned to lanes is free as long
-// as the activation operand uses the same assignment: for MFMA j (0..3) of a
-// step, group g supplies elements 32*b + 8*j .. +8 of both operands.
-// The four waves' partial sums meet in LDS in a fixed order, so results are
-// bit-reproducible.
+// Work split.  A workgroup owns one tile (<= BM slots of one expert) and
+// NBW blocks of 16 output rows of the weight matrix (for gate/up: gate rows
+// n..n+15 with the matching up rows I+n..I+n+15, so SwiGLU fuses into the
+// epilogue).  Each 16-row block is served by 4 waves that split the
+// reduction dimension: it is cut into 32-element MX blocks and block
+// b = 16*step + 4*kq + group goes to lane group `group` (lanes 16*group ..
+// +15) of the block's wave kq.  A lane thus loads exactly one MX block (16
+// bytes, 32 codes) plus its scale byte per weight row and step, and a wave
+// reads 64 contiguous bytes of each of its 16 rows.  An MFMA sums over its
+// whole K range, so the K order is free as long as the activation operand
+// uses the same assignment: for MFMA j (0..3) of a step, group g supplies
+// elements 32*b + 8*j .. +8 of both operands.
+//
+// Memory behaviour.  All weight loads of a wave (up to kChunk steps) are
+// issued branch-free before the first MFMA (out-of-range blocks read a
+// clamped address and get a zero scale), and they stay in registers across
+// the tile's M-passes, so each weight byte is fetched once per tile.  The
+// activation rows of a pass (XR rows, XR = 1..16) are staged once per
+// workgroup in LDS with a 16-byte row pad (conflict-free 128-bit reads; at
+// XR = 1 every lane reads the same row, a broadcast).  The split-K partial
+// sums meet in LDS in a fixed order, so results are bit-reproducible.
 #include "moe_device.h"
 #include "moe_launch.h"
 
@@ -31,188 +38,278 @@ namespace moe {
 
 namespace {
 
-constexpr int kRowsPerBlock = 16;  // weight rows per workgroup (MFMA N)
-constexpr int kTokPerMfma = 16;    // tokens per MFMA (MFMA M)
-constexpr int kBlocksPerStep = 16; // MX blocks per workgroup step (4 waves x 4 groups)
-
-struct Operand16 {
-  uint4 q;     // 32 e2m1 codes of one MX block
-  float scale; // its E8M0 scale as fp32
-};
-
-__device__ __forceinline__ Operand16 load_block(const uint8_t* q_row, const uint8_t* s_row, int b,
-                                                bool valid) {
-  Operand16 o;
-  if (valid) {
-    o.q = *reinterpret_cast<const uint4*>(q_row + (size_t)b * 16);
-    o.scale = e8m0_to_float(s_row[b]);
-  } else {
-    o.q = make_uint4(0u, 0u, 0u, 0u);
-    o.scale = 1.0f;
-  }
-  return o;
-}
-
-// Four 8-element bf16 slices of a 32-element block of a bf16 row.
-struct Act32 {
-  uint4 v[4];
-};
-
-__device__ __forceinline__ Act32 load_act(const uint16_t* row, int b, bool valid) {
-  Act32 a;
-  if (valid) {
-    const uint4* p = reinterpret_cast<const uint4*>(row + (size_t)b * 32);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) a.v[j] = p[j];
-  } else {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) a.v[j] = make_uint4(0u, 0u, 0u, 0u);
-  }
-  return a;
-}
+constexpr int kRowsPerBlock = 16;   // weight rows per 16-row block (MFMA N)
+constexpr int kBlocksPerStep = 16;  // MX blocks per step (4 waves x 4 lane groups)
+constexpr int kChunk = 6;           // steps whose weights a wave holds at once (K = 3072)
 
 // A tile row that does not describe slots of one valid expert is skipped, so
 // a corrupted table cannot send loads or stores out of bounds.
+constexpr int kMaxRows = 128;       // largest token tile (BM)
+
 __device__ __forceinline__ bool tile_ok(int e, int r0, int rows, int E, long long nslots) {
-  return e >= 0 && e < E && r0 >= 0 && rows > 0 && (long long)r0 + rows <= nslots;
+  return e >= 0 && e < E && r0 >= 0 && rows > 0 && rows <= kMaxRows &&
+         (long long)r0 + rows <= nslots;
 }
 
 __device__ __forceinline__ uint32_t word(const uint4& q, int j) {
   return j == 0 ? q.x : j == 1 ? q.y : j == 2 ? q.z : q.w;
 }
 
-// ----------------------------------------------------------- gate/up + SwiGLU
-__global__ __launch_bounds__(256) void gateup_swiglu_kernel(
-    const uint16_t* __restrict__ x, const uint8_t* __restrict__ w13_q,
-    const uint8_t* __restrict__ w13_s, const int32_t* __restrict__ sorted_ids,
-    const int32_t* __restrict__ tiles, const int32_t* __restrict__ num_tiles, int T, int H, int I,
-    int E, int k, uint16_t* __restrict__ h_out) {
-  __shared__ float red[4][2][kTokPerMfma * kRowsPerBlock];
+// Row stride of the staged activations in LDS: K bf16 plus a 16-byte pad.
+__host__ __device__ __forceinline__ int act_stride_bytes(int K) { return K * 2 + 16; }
+
+// GATEUP: A rows are x[token of sorted_ids[r]], K = H, weights are the gate
+//         and up rows of w13, output h[r][n] = bf16(silu(g) * u).
+// !GATEUP: A rows are h[r], K = I, weights are rows of w2, output
+//         y[sorted_ids[r]][n] in fp32.
+template <bool GATEUP, int NBW, int XR, bool ONECHUNK>
+__global__ __launch_bounds__(256 * NBW) void expert_gemm_kernel(
+    const uint16_t* __restrict__ act, const uint8_t* __restrict__ wq,
+    const uint8_t* __restrict__ ws, const int32_t* sorted_ids,  // not restrict: see below
+    const int32_t* __restrict__ tiles, const int32_t* __restrict__ num_tiles, int T, int H,
+    int I, int E, int k, void* __restrict__ out) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  constexpr int NW = GATEUP ? 2 : 1;  // weight rows per lane per step (gate + up)
 
   const int tile = blockIdx.x;
   if (tile >= num_tiles[0]) return;  // uniform over the workgroup
   const int e = tiles[3 * tile + 0];
   const int r0 = tiles[3 * tile + 1];
   const int rows = tiles[3 * tile + 2];
-  if (!tile_ok(e, r0, rows, E, (long long)T * k)) return;  // uniform
-  const int n_base = blockIdx.y * kRowsPerBlock;
+  const long long nslots = (long long)T * k;
+  if (!tile_ok(e, r0, rows, E, nslots)) return;  // uniform
 
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
+  const int K = GATEUP ? H : I;       // reduction length
+  const int N = GATEUP ? I : H;       // output rows (row pairs for gate/up)
+  const int KB = K / 32;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
   const int li = lane & 15;
   const int grp = lane >> 4;
-  const int KB = H / 32;
+  const int nb = wave >> 2;           // 16-row block within the workgroup
+  const int kq = wave & 3;            // K quarter of this wave
+  const int n_base = (blockIdx.y * NBW + nb) * kRowsPerBlock;
+  const int n_row = n_base < N ? n_base + li : li;  // blocks past N compute, never store
 
-  const size_t q_stride = (size_t)H / 2;
-  const size_t s_stride = (size_t)H / 32;
-  const size_t gate_row = (size_t)e * 2 * I + n_base + li;
-  const size_t up_row = gate_row + I;
-  const uint8_t* qg = w13_q + gate_row * q_stride;
-  const uint8_t* qu = w13_q + up_row * q_stride;
-  const uint8_t* sg = w13_s + gate_row * s_stride;
-  const uint8_t* su = w13_s + up_row * s_stride;
+  // weight rows of this lane
+  const size_t q_stride = (size_t)K / 2;
+  const size_t s_stride = (size_t)K / 32;
+  size_t wrow[NW];
+  if (GATEUP) {
+    wrow[0] = (size_t)e * 2 * I + n_row;
+    if (NW > 1) wrow[NW - 1] = (size_t)e * 2 * I + I + n_row;
+  } else {
+    wrow[0] = (size_t)e * H + n_row;
+  }
 
-  for (int mb = 0; mb < rows; mb += kTokPerMfma) {
-    const int m = min(mb + li, rows - 1);
-    int t = sorted_ids[r0 + m] / k;
-    t = min(max(t, 0), T - 1);
-    const uint16_t* xr = x + (size_t)t * H;
+  const int nsteps = (KB + kBlocksPerStep - 1) / kBlocksPerStep;
+  const int nchunks = ONECHUNK ? 1 : (nsteps + kChunk - 1) / kChunk;
+  const int stride = act_stride_bytes(K);
+  const int npass = (rows + XR - 1) / XR;
 
-    floatx4 acc_g = {0.f, 0.f, 0.f, 0.f};
-    floatx4 acc_u = {0.f, 0.f, 0.f, 0.f};
-    for (int step = 0; step * kBlocksPerStep < KB; ++step) {
-      const int b = step * kBlocksPerStep + wave * 4 + grp;
-      const bool valid = b < KB;
-      const Operand16 g = load_block(qg, sg, b, valid);
-      const Operand16 u = load_block(qu, su, b, valid);
-      const Act32 a = load_act(xr, b, valid);
+  uint4 wreg[kChunk][NW];
+  uint32_t sreg[kChunk][NW];
+
+  auto load_weights = [&](int ch) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bf16x8 av = as_bf16x8(a.v[j]);
-        acc_g = mfma16x16x32(av, dequant8_bf16(word(g.q, j), g.scale), acc_g);
-        acc_u = mfma16x16x32(av, dequant8_bf16(word(u.q, j), u.scale), acc_u);
+    for (int c = 0; c < kChunk; ++c) {
+      const int b = (ch * kChunk + c) * kBlocksPerStep + kq * 4 + grp;
+      const int bc = min(b, KB - 1);  // clamped: always a valid address
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        wreg[c][w] = *reinterpret_cast<const uint4*>(wq + wrow[w] * q_stride + (size_t)bc * 16);
+        sreg[c][w] = ws[wrow[w] * s_stride + bc];
+      }
+    }
+  };
+
+  // Per-tile row table in LDS: the element offset of each row's activations
+  // and (down) the slot id its output goes to.  The index loads are issued
+  // before the weight stream so they never wait behind it.
+  __shared__ long long s_rowoff[kMaxRows];
+  __shared__ int s_slot[kMaxRows];
+  // Branch-free and in bounds.  The memory clobber keeps this load ahead of
+  // the weight stream (sorted_ids is deliberately not __restrict__, which
+  // would let the compiler sink the load past the clobber).
+  const int my_slot = sorted_ids[r0 + min(tid, rows - 1)];
+  asm volatile("" ::: "memory");
+
+  // Stage activation rows [p0, p0 + nrows) of this tile into LDS with
+  // direct global->LDS 128-bit loads (no registers hold the data).  The
+  // padded rows form one array of 16-byte slots, K/8 + 1 per row (the last is
+  // the pad, filled with a copy of the row's last chunk); one wave
+  // instruction fills 64 consecutive slots = 1 KB.  Slots past the last row
+  // repeat it; the LDS allocation is rounded up to whole kilobytes.
+  constexpr int kWavesWG = 4 * NBW;
+  auto stage_acts = [&](int p0, int nrows) {
+    const int cpr = K / 8;
+    const int spr = cpr + 1;
+    const int ninst = (nrows * spr + 63) / 64;
+    for (int ins = wave; ins < ninst; ins += kWavesWG) {  // wave-uniform
+      const int slot = ins * 64 + lane;
+      const int r = min(slot / spr, nrows - 1);
+      const int c = min(slot - (slot / spr) * spr, cpr - 1);
+      __builtin_amdgcn_global_load_lds(
+          act + s_rowoff[p0 + r] + (long long)c * 8,
+          (__attribute__((address_space(3))) void*)(smem + (size_t)ins * 1024), 16, 0, 0);
+    }
+  };
+
+  if constexpr (ONECHUNK) load_weights(0);  // depends only on the tile row
+  if (tid < rows) {
+    long long off;
+    if (GATEUP) {
+      const int t = min(max(my_slot / k, 0), T - 1);
+      off = (long long)t * H;
+    } else {
+      off = (long long)(r0 + tid) * I;
+    }
+    s_rowoff[tid] = off;
+    s_slot[tid] = my_slot;
+  }
+  __syncthreads();
+
+  // Pass 0's activations are staged while the weight stream is in flight;
+  // one wait covers both.  With K <= kChunk*512 (ONECHUNK) a wave's whole
+  // share of the weights is loaded once and reused by every pass.
+  stage_acts(0, min(XR, rows));
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  for (int pass = 0; pass < npass; ++pass) {
+    const int p0 = pass * XR;
+    const int prow = min(XR, rows - p0);
+    if (pass > 0) {
+      __syncthreads();  // previous pass done with LDS
+      stage_acts(p0, prow);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
+
+    if constexpr (ONECHUNK) {
+      // The weights are decoded only after the staging barrier (an empty
+      // asm that "modifies" them stops the compiler from hoisting the
+      // decode, which would quadruple their register footprint).
+#pragma unroll
+      for (int c = 0; c < kChunk; ++c)
+#pragma unroll
+        for (int w = 0; w < NW; ++w)
+          asm volatile("" : "+v"(wreg[c][w].x), "+v"(wreg[c][w].y), "+v"(wreg[c][w].z),
+                       "+v"(wreg[c][w].w), "+v"(sreg[c][w]));
+    }
+    floatx4 acc[NW];
+#pragma unroll
+    for (int w = 0; w < NW; ++w) acc[w] = floatx4{0.f, 0.f, 0.f, 0.f};
+    const unsigned char* arow = smem + min(li, prow - 1) * stride;
+
+    for (int ch = 0; ch < nchunks; ++ch) {
+      if constexpr (!ONECHUNK) load_weights(ch);
+#pragma unroll
+      for (int c = 0; c < kChunk; ++c) {
+        const int b = (ch * kChunk + c) * kBlocksPerStep + kq * 4 + grp;
+        const bool valid = b < KB;
+        const int bc = min(b, KB - 1);
+        float scale[NW];
+#pragma unroll
+        for (int w = 0; w < NW; ++w) scale[w] = valid ? e8m0_to_float(sreg[c][w]) : 0.f;
+        const uint4* ap = reinterpret_cast<const uint4*>(arow + bc * 64);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bf16x8 a = as_bf16x8(ap[j]);
+#pragma unroll
+          for (int w = 0; w < NW; ++w)
+            acc[w] = mfma16x16x32(a, dequant8_bf16(word(wreg[c][w], j), scale[w]), acc[w]);
+        }
       }
     }
 
-    // lane holds D[4*grp + r][li]: token row 4*grp + r, weight row li
+    // split-K reduction: waves kq = 0..3 of each 16-row block, fixed order
+    __syncthreads();  // every wave done reading the staged activations
+    float* red = reinterpret_cast<float*>(smem);  // [NBW][4][NW][256]
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      red[wave][0][(4 * grp + r) * kRowsPerBlock + li] = acc_g[r];
-      red[wave][1][(4 * grp + r) * kRowsPerBlock + li] = acc_u[r];
-    }
+    for (int w = 0; w < NW; ++w)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        red[((nb * 4 + kq) * NW + w) * 256 + (4 * grp + r) * kRowsPerBlock + li] = acc[w][r];
     __syncthreads();
     {
-      const int idx = threadIdx.x;  // 256 = 16 tokens x 16 rows
+      const int obl = tid >> 8;       // output block handled by this thread
+      const int idx = tid & 255;      // 16 tokens x 16 rows
       const int tm = idx / kRowsPerBlock;
       const int tn = idx % kRowsPerBlock;
-      float gs = red[0][0][idx], us = red[0][1][idx];
+      const int on = (blockIdx.y * NBW + obl) * kRowsPerBlock + tn;
+      float v[NW];
 #pragma unroll
-      for (int w = 1; w < 4; ++w) { gs += red[w][0][idx]; us += red[w][1][idx]; }
-      if (mb + tm < rows)
-        h_out[(size_t)(r0 + mb + tm) * I + n_base + tn] = float_to_bf16(silu(gs) * us);
+      for (int w = 0; w < NW; ++w) {
+        v[w] = red[((obl * 4 + 0) * NW + w) * 256 + idx];
+#pragma unroll
+        for (int q = 1; q < 4; ++q) v[w] += red[((obl * 4 + q) * NW + w) * 256 + idx];
+      }
+      if (tm < prow && on < N) {
+        const int r = r0 + p0 + tm;
+        if (GATEUP) {
+          reinterpret_cast<uint16_t*>(out)[(size_t)r * I + on] =
+              float_to_bf16(silu(v[0]) * v[NW - 1]);
+        } else {
+          const long long p = s_slot[p0 + tm];
+          if (p >= 0 && p < nslots) reinterpret_cast<float*>(out)[(size_t)p * H + on] = v[0];
+        }
+      }
     }
-    __syncthreads();
   }
 }
 
-// --------------------------------------------------------------------- down
-__global__ __launch_bounds__(256) void down_kernel(
-    const uint16_t* __restrict__ h, const uint8_t* __restrict__ w2_q,
-    const uint8_t* __restrict__ w2_s, const int32_t* __restrict__ sorted_ids,
-    const int32_t* __restrict__ tiles, const int32_t* __restrict__ num_tiles, int T, int H, int I,
-    int E, int k, float* __restrict__ y) {
-  __shared__ float red[4][kTokPerMfma * kRowsPerBlock];
+// Rows of activations staged per pass: twice the expected rows per expert
+// (T*k/E), bounded by the tile's row bound (an expert gets at most one slot
+// per token, so rows <= min(BM, T)), rounded up to a power of two, at most
+// 16, and small enough that the staged rows fit in 96 KB.  Small passes keep
+// the LDS footprint low enough for several workgroups per CU (one's loads
+// overlap another's compute); tiles with more rows take extra passes over
+// weights held in registers.
+int pick_xr(int T, int BM, int K, int E, int k) {
+  int cap = T < BM ? T : BM;
+  const long long want = (2LL * T * k + E - 1) / E;
+  if (want < cap) cap = (int)want;
+  int xr = 1;
+  while (xr < cap && xr < 16) xr <<= 1;
+  while (xr > 1 && (size_t)xr * act_stride_bytes(K) > 96 * 1024) xr >>= 1;
+  return xr;
+}
 
-  const int tile = blockIdx.x;
-  if (tile >= num_tiles[0]) return;
-  const int e = tiles[3 * tile + 0];
-  const int r0 = tiles[3 * tile + 1];
-  const int rows = tiles[3 * tile + 2];
-  if (!tile_ok(e, r0, rows, E, (long long)T * k)) return;  // uniform
-  const int n_base = blockIdx.y * kRowsPerBlock;
-
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
-  const int li = lane & 15;
-  const int grp = lane >> 4;
-  const int KB = I / 32;
-
-  const size_t wrow = (size_t)e * H + n_base + li;
-  const uint8_t* q = w2_q + wrow * ((size_t)I / 2);
-  const uint8_t* s = w2_s + wrow * ((size_t)I / 32);
-  const long long nslots = (long long)T * k;
-
-  for (int mb = 0; mb < rows; mb += kTokPerMfma) {
-    const int m = min(mb + li, rows - 1);
-    const uint16_t* hr = h + (size_t)(r0 + m) * I;
-
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int step = 0; step * kBlocksPerStep < KB; ++step) {
-      const int b = step * kBlocksPerStep + wave * 4 + grp;
-      const bool valid = b < KB;
-      const Operand16 w = load_block(q, s, b, valid);
-      const Act32 a = load_act(hr, b, valid);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc = mfma16x16x32(as_bf16x8(a.v[j]), dequant8_bf16(word(w.q, j), w.scale), acc);
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) red[wave][(4 * grp + r) * kRowsPerBlock + li] = acc[r];
-    __syncthreads();
-    {
-      const int idx = threadIdx.x;
-      const int tm = idx / kRowsPerBlock;
-      const int tn = idx % kRowsPerBlock;
-      float v = red[0][idx];
-#pragma unroll
-      for (int w = 1; w < 4; ++w) v += red[w][idx];
-      if (mb + tm < rows) {
-        const long long p = sorted_ids[r0 + mb + tm];
-        if (p >= 0 && p < nslots) y[(size_t)p * H + n_base + tn] = v;
-      }
-    }
-    __syncthreads();
+template <bool GATEUP>
+void launch_expert_gemm(const uint16_t* act, const uint8_t* wq, const uint8_t* ws,
+                        const int32_t* sorted_ids, const int32_t* tiles,
+                        const int32_t* num_tiles, int tiles_max, int T, int H, int I, int E,
+                        int k, int BM, void* out, hipStream_t stream) {
+  const int K = GATEUP ? H : I;
+  const int N = GATEUP ? I : H;
+  const int xr = pick_xr(T, BM, K, E, k);
+  const int nblk16 = N / kRowsPerBlock;
+  const bool one_chunk = K <= kChunk * kBlocksPerStep * 32;
+  const size_t red_bytes_1 = (size_t)4 * (GATEUP ? 2 : 1) * 256 * sizeof(float);
+#define MOE_LAUNCH(NBW_, XR_)                                                                  \
+  do {                                                                                          \
+    size_t lds = ((size_t)(XR_) * act_stride_bytes(K) + 1023) / 1024 * 1024;                    \
+    if (lds < red_bytes_1 * (NBW_)) lds = red_bytes_1 * (NBW_);                                 \
+    dim3 grid(tiles_max, (nblk16 + (NBW_) - 1) / (NBW_));                                       \
+    if (one_chunk)                                                                              \
+      hipLaunchKernelGGL((expert_gemm_kernel<GATEUP, NBW_, XR_, true>), grid, dim3(256 * (NBW_)), \
+                         lds, stream, act, wq, ws, sorted_ids, tiles, num_tiles, T, H, I, E, k,  \
+                         out);                                                                  \
+    else                                                                                        \
+      hipLaunchKernelGGL((expert_gemm_kernel<GATEUP, NBW_, XR_, false>), grid,                  \
+                         dim3(256 * (NBW_)), lds, stream, act, wq, ws, sorted_ids, tiles,       \
+                         num_tiles, T, H, I, E, k, out);                                        \
+  } while (0)
+  switch (xr) {
+    case 1: MOE_LAUNCH(1, 1); break;
+    case 2: MOE_LAUNCH(1, 2); break;
+    case 4: MOE_LAUNCH(1, 4); break;
+    case 8: MOE_LAUNCH(4, 8); break;
+    default: MOE_LAUNCH(4, 16); break;
   }
+#undef MOE_LAUNCH
 }
 
 }  // namespace
@@ -220,19 +317,17 @@ __global__ __launch_bounds__(256) void down_kernel(
 void launch_gateup_swiglu(const uint16_t* x, const uint8_t* w13_q, const uint8_t* w13_s,
                           const int32_t* sorted_ids, const int32_t* tiles,
                           const int32_t* num_tiles, int tiles_max, int T, int H, int I, int E,
-                          int k, uint16_t* h, hipStream_t stream) {
-  dim3 grid(tiles_max, I / kRowsPerBlock);
-  hipLaunchKernelGGL(gateup_swiglu_kernel, grid, dim3(256), 0, stream, x, w13_q, w13_s,
-                     sorted_ids, tiles, num_tiles, T, H, I, E, k, h);
+                          int k, int BM, uint16_t* h, hipStream_t stream) {
+  launch_expert_gemm<true>(x, w13_q, w13_s, sorted_ids, tiles, num_tiles, tiles_max, T, H, I, E,
+                           k, BM, h, stream);
 }
 
 void launch_down(const uint16_t* h, const uint8_t* w2_q, const uint8_t* w2_s,
                  const int32_t* sorted_ids, const int32_t* tiles, const int32_t* num_tiles,
-                 int tiles_max, int T, int H, int I, int E, int k, float* y,
+                 int tiles_max, int T, int H, int I, int E, int k, int BM, float* y,
                  hipStream_t stream) {
-  dim3 grid(tiles_max, H / kRowsPerBlock);
-  hipLaunchKernelGGL(down_kernel, grid, dim3(256), 0, stream, h, w2_q, w2_s, sorted_ids, tiles,
-                     num_tiles, T, H, I, E, k, y);
+  launch_expert_gemm<false>(h, w2_q, w2_s, sorted_ids, tiles, num_tiles, tiles_max, T, H, I, E,
+                            k, BM, y, stream);
 }
 
 }  // namespace moe

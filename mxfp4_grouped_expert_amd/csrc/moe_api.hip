@@ -67,11 +67,11 @@ const char* moe_status_string(int status) {
 const char* moe_version(void) { return "0.1.0"; }
 
 int moe_pick_bm(int T, int k, int E) {
-  if (T <= 0 || k <= 0 || E <= 0) return 16;
-  const double m = (double)T * (double)k / (double)E;
-  if (m <= 16.0) return 16;
-  if (m <= 48.0) return 32;
-  return 64;
+  (void)k;
+  (void)E;
+  int bm = 16;
+  while (bm < 128 && bm < T) bm <<= 1;
+  return bm;
 }
 
 int64_t moe_tiles_max(int T, int k, int E, int BM) {
@@ -153,7 +153,8 @@ moe_status moe_gateup_swiglu(const uint16_t* x, const uint8_t* w13_q, const uint
   if (st != MOE_OK) return st;
   (void)hipGetLastError();
   moe::launch_gateup_swiglu(x, w13_q, w13_s, sorted_ids, tiles, num_tiles,
-                            (int)moe_tiles_max(T, k, E, BM), T, H, I, E, k, h, as_stream(stream));
+                            (int)moe_tiles_max(T, k, E, BM), T, H, I, E, k, BM, h,
+                            as_stream(stream));
   return finish_launches();
 }
 
@@ -169,7 +170,7 @@ moe_status moe_down(const uint16_t* h, const uint8_t* w2_q, const uint8_t* w2_s,
   if (st != MOE_OK) return st;
   (void)hipGetLastError();
   moe::launch_down(h, w2_q, w2_s, sorted_ids, tiles, num_tiles, (int)moe_tiles_max(T, k, E, BM),
-                   T, H, I, E, k, y, as_stream(stream));
+                   T, H, I, E, k, BM, y, as_stream(stream));
   return finish_launches();
 }
 
@@ -210,8 +211,9 @@ moe_status moe_forward(const uint16_t* x, const uint8_t* w13_q, const uint8_t* w
   float* y = reinterpret_cast<float*>(static_cast<char*>(workspace) + round256(nslots * I * 2));
   hipStream_t s = as_stream(stream);
   moe::launch_gateup_swiglu(x, w13_q, w13_s, sorted_ids, tiles, num_tiles, (int)tmax, T, H, I, E,
-                            k, h, s);
-  moe::launch_down(h, w2_q, w2_s, sorted_ids, tiles, num_tiles, (int)tmax, T, H, I, E, k, y, s);
+                            k, BM, h, s);
+  moe::launch_down(h, w2_q, w2_s, sorted_ids, tiles, num_tiles, (int)tmax, T, H, I, E, k, BM, y,
+                   s);
   moe::launch_combine(y, topk_weights, T, H, k, out, s);
   return finish_launches();
 }

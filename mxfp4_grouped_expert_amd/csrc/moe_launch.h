@@ -30,10 +30,10 @@ void launch_build_tiles(const int32_t* topk_ids, int N, int E, int BM, int32_t* 
 void launch_gateup_swiglu(const uint16_t* x, const uint8_t* w13_q, const uint8_t* w13_s,
                           const int32_t* sorted_ids, const int32_t* tiles,
                           const int32_t* num_tiles, int tiles_max, int T, int H, int I, int E,
-                          int k, uint16_t* h, hipStream_t stream);
+                          int k, int BM, uint16_t* h, hipStream_t stream);
 void launch_down(const uint16_t* h, const uint8_t* w2_q, const uint8_t* w2_s,
                  const int32_t* sorted_ids, const int32_t* tiles, const int32_t* num_tiles,
-                 int tiles_max, int T, int H, int I, int E, int k, float* y,
+                 int tiles_max, int T, int H, int I, int E, int k, int BM, float* y,
                  hipStream_t stream);
 
 // Weighted combine back to token order.

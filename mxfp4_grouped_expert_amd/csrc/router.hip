@@ -122,7 +122,15 @@ __global__ __launch_bounds__(256) void router_topk_softmax(
     const int e = lane + kWave * i;
     double v = 0.0;
     if (e < E) {
-      for (int s = 0; s < splits; ++s) v += partial[((size_t)s * T + t) * E + e];
+      // eight K-range partials in flight at a time, summed in ascending order
+      for (int s0 = 0; s0 < splits; s0 += 8) {
+        double p[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+          p[c] = (s0 + c < splits) ? partial[((size_t)(s0 + c) * T + t) * E + e] : 0.0;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) v += p[c];
+      }
       if (bias) v += (double)bias[e];
       if (logits) logits[(size_t)t * E + e] = v;
       key[i] = order_key(v);

@@ -42,11 +42,11 @@ def test_status_strings_and_version():
     assert re.match(r"\d+\.\d+\.\d+", moe.version())
 
 
-@pytest.mark.parametrize("T,k,E,want", [(1, 4, 32, 16), (64, 4, 32, 16), (64, 4, 128, 16),
-                                        (4096, 4, 128, 64), (512, 4, 128, 16), (513, 4, 128, 32),
-                                        (1536, 4, 128, 32), (1537, 4, 128, 64), (0, 4, 8, 16)])
+@pytest.mark.parametrize("T,k,E,want", [(1, 4, 32, 16), (16, 4, 32, 16), (17, 4, 32, 32),
+                                        (64, 4, 32, 64), (64, 4, 128, 64), (65, 4, 128, 128),
+                                        (4096, 4, 128, 128), (0, 4, 8, 16)])
 def test_pick_bm_rule(T, k, E, want):
-    # 16 if T*k/E <= 16, 32 if <= 48, else 64
+    # the smallest of 16/32/64/128 that is >= T
     assert moe.pick_bm(T, k, E) == want
 
 
