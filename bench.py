@@ -194,8 +194,8 @@ def main():
     # loop), replayed between two events on the launch stream.  The layer
     # buffers hold a valid routing and tile table from the calls above.
     parts = {
-        "route": lambda r: layer.route_only(x),
-        "tiles": lambda r: layer.tiles_only(),
+        ("route_tiles" if layer.fused else "route"): lambda r: layer.route_only(x),
+        **({} if layer.fused else {"tiles": lambda r: layer.tiles_only()}),
         "gateup": lambda r: (layer.set_weights(*copies[r]), layer.gateup_only(x)),
         "down": lambda r: (layer.set_weights(*copies[r]), layer.down_only()),
         "combine": lambda r: layer.combine_only(),
@@ -266,7 +266,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded gpt-oss-shaped MXFP4 layer, no checkpoint)",
         "config": {"workload": inp["name"], "T": T, "H": H, "E": E, "k": k, "I": I, "BM": BM,
-                   "experts_touched": n_touched, "weight_rotations": R, "timing": mode},
+                   "experts_touched": n_touched, "weight_rotations": R, "timing": mode,
+                   "routing": "moe_route_tiles" if layer.fused else "moe_route+moe_build_tiles"},
         "tokens_per_s": round(T / (us * 1e-6), 1),
         "hbm_gbps": round(gbps, 1),
         "hbm_frac": round(gbps / HBM_PEAK_GBS, 4),

@@ -193,6 +193,32 @@ moe_status moe_forward(const uint16_t* x,
                        void* workspace, size_t workspace_bytes,
                        uint16_t* out, struct ihipStream_t* stream);
 
+/* ------------------------------------------------------- moe_route_tiles
+ * moe_route followed by moe_build_tiles in a single launch, for decode-sized
+ * batches (T <= 16; otherwise MOE_ERR_SHAPE).  The
+ * write-up counts launch and host gaps as their own cost of a decode step
+ * ("Where the time went": "Launch and host gaps"), and at one token the
+ * routing work is too small to hide them.  The workgroups computing partial
+ * logits take tickets from a counter; the last one sums the partials in a
+ * fixed order and runs top-k, softmax and the tile table.  Outputs are
+ * bit-identical to moe_route + moe_build_tiles with the same arguments.
+ *
+ *   arguments as for moe_route and moe_build_tiles
+ *   workspace   >= moe_route_tiles_workspace_bytes(T, H, E), 16-byte aligned.
+ *               Its first 256 bytes hold the ticket counter: they must be
+ *               zero before the first call, and every call leaves them zero.
+ *               Calls that share a workspace must not overlap in time.
+ */
+size_t moe_route_tiles_workspace_bytes(int T, int H, int E);
+
+moe_status moe_route_tiles(const uint16_t* x, const float* w_router, const float* bias,
+                           int T, int H, int E, int k, int BM,
+                           int32_t* topk_ids, float* topk_weights, double* logits,
+                           int32_t* expert_offsets, int32_t* sorted_ids,
+                           int32_t* tiles, int32_t* num_tiles,
+                           void* workspace, size_t workspace_bytes,
+                           struct ihipStream_t* stream);
+
 /* --------------------------------------------- the three steps of moe_forward
  * moe_forward is exactly these three calls in order; they are exported so a
  * caller can time or overlap them separately.  Arguments and constraints are

@@ -7,9 +7,13 @@ and streams only.
 """
 from .binding import (MoeError, LIB_PATH, load, version, status_string, pick_bm, tiles_max,
                       route_workspace_bytes, forward_workspace_bytes, moe_route,
-                      moe_build_tiles, moe_forward, moe_gateup_swiglu, moe_down, moe_combine)
+                      moe_build_tiles, moe_forward, moe_gateup_swiglu, moe_down, moe_combine,
+                      moe_route_tiles, route_tiles_ok, route_tiles_workspace_bytes,
+                      zeroed_route_tiles_workspace)
 from .layer import MoeLayer
 
 __all__ = ["MoeError", "LIB_PATH", "load", "version", "status_string", "pick_bm", "tiles_max",
            "route_workspace_bytes", "forward_workspace_bytes", "moe_route", "moe_build_tiles",
-           "moe_forward", "moe_gateup_swiglu", "moe_down", "moe_combine", "MoeLayer"]
+           "moe_forward", "moe_gateup_swiglu", "moe_down", "moe_combine", "moe_route_tiles",
+           "route_tiles_ok", "route_tiles_workspace_bytes", "zeroed_route_tiles_workspace",
+           "MoeLayer"]

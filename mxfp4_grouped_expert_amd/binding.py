@@ -60,6 +60,11 @@ def load() -> ctypes.CDLL:
     lib.moe_forward.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _p,
                                 _i, _i, _i, _i, _i, _i, _p, _sz, _p, _p]
     lib.moe_forward.restype = _i
+    lib.moe_route_tiles_workspace_bytes.argtypes = [_i, _i, _i]
+    lib.moe_route_tiles_workspace_bytes.restype = _sz
+    lib.moe_route_tiles.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p,
+                                    _p, _sz, _p]
+    lib.moe_route_tiles.restype = _i
     lib.moe_gateup_swiglu.argtypes = [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p, _p]
     lib.moe_gateup_swiglu.restype = _i
     lib.moe_down.argtypes = [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p, _p]
@@ -154,6 +159,49 @@ def moe_route(x: torch.Tensor, w_router: torch.Tensor, bias: Optional[torch.Tens
                             _ptr(wts), _ptr(logits), _ptr(workspace), workspace.numel(),
                             _stream(dev)), "moe_route")
     return ids, wts, logits
+
+
+def route_tiles_workspace_bytes(T: int, H: int, E: int) -> int:
+    return int(load().moe_route_tiles_workspace_bytes(T, H, E))
+
+
+def route_tiles_ok(T: int, E: int, k: int) -> bool:
+    """Whether the fused decode routing entry point accepts this batch."""
+    return T <= 16
+
+
+def zeroed_route_tiles_workspace(T: int, H: int, E: int, device) -> torch.Tensor:
+    """A workspace for moe_route_tiles whose ticket counter starts at zero."""
+    return torch.zeros(max(route_tiles_workspace_bytes(T, H, E), 256), dtype=torch.uint8,
+                       device=device)
+
+
+def moe_route_tiles(x: torch.Tensor, w_router: torch.Tensor, bias: Optional[torch.Tensor],
+                    k: int, BM: int, want_logits: bool = False,
+                    workspace: Optional[torch.Tensor] = None):
+    """Fused decode routing + tile table.  Returns (topk_ids, topk_weights,
+    logits or None, expert_offsets, sorted_ids, tiles, num_tiles)."""
+    _need(x, "x", _BF16)
+    dev = x.device
+    _need(w_router, "w_router", (torch.float32,), dev)
+    if bias is not None:
+        _need(bias, "bias", (torch.float32,), dev)
+    T, H = x.shape
+    E = w_router.shape[0]
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    wts = torch.empty((T, k), dtype=torch.float32, device=dev)
+    logits = torch.empty((T, E), dtype=torch.float64, device=dev) if want_logits else None
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    sorted_ids = torch.empty(max(T * k, 1), dtype=torch.int32, device=dev)[:T * k]
+    tiles = torch.empty((max(tiles_max(T, k, E, BM), 1), 3), dtype=torch.int32, device=dev)
+    num_tiles = torch.zeros(1, dtype=torch.int32, device=dev)
+    if workspace is None:
+        workspace = zeroed_route_tiles_workspace(T, H, E, dev)
+    _check(load().moe_route_tiles(_ptr(x), _ptr(w_router), _ptr(bias), T, H, E, k, BM, _ptr(ids),
+                                  _ptr(wts), _ptr(logits), _ptr(offsets), _ptr(sorted_ids),
+                                  _ptr(tiles), _ptr(num_tiles), _ptr(workspace),
+                                  workspace.numel(), _stream(dev)), "moe_route_tiles")
+    return ids, wts, logits, offsets, sorted_ids, tiles, num_tiles
 
 
 def moe_build_tiles(topk_ids: torch.Tensor, E: int, BM: int):

@@ -114,6 +114,34 @@ moe_status moe_route(const uint16_t* x, const float* w_router, const float* bias
   return finish_launches();
 }
 
+size_t moe_route_tiles_workspace_bytes(int T, int H, int E) {
+  if (T <= 0 || H <= 0 || E <= 0) return 0;
+  return round256(moe::router_fused_bytes(T, H, E));
+}
+
+moe_status moe_route_tiles(const uint16_t* x, const float* w_router, const float* bias, int T,
+                           int H, int E, int k, int BM, int32_t* topk_ids, float* topk_weights,
+                           double* logits, int32_t* expert_offsets, int32_t* sorted_ids,
+                           int32_t* tiles, int32_t* num_tiles, void* workspace,
+                           size_t workspace_bytes, struct ihipStream_t* stream) {
+  if (T < 0 || H <= 0 || H % 32 != 0 || H > MOE_MAX_DIM || E < 1 || E > MOE_MAX_EXPERTS ||
+      k < 1 || k > MOE_MAX_TOPK || k > E || !valid_bm(BM) || !moe::router_fused_ok(T, E, k))
+    return MOE_ERR_SHAPE;
+  if (T == 0) return MOE_OK;
+  if (!x || !w_router || !topk_ids || !topk_weights || !expert_offsets || !sorted_ids || !tiles ||
+      !num_tiles || !workspace)
+    return MOE_ERR_NULL;
+  if (!aligned16(x) || !aligned16(w_router) || !aligned16(workspace)) return MOE_ERR_ALIGN;
+  if (workspace_bytes < moe_route_tiles_workspace_bytes(T, H, E)) return MOE_ERR_WORKSPACE;
+  moe_status st = check_device();
+  if (st != MOE_OK) return st;
+  (void)hipGetLastError();
+  moe::launch_router_fused(x, w_router, bias, T, H, E, k, BM, workspace, topk_ids, topk_weights,
+                           logits, expert_offsets, sorted_ids, tiles, num_tiles,
+                           as_stream(stream));
+  return finish_launches();
+}
+
 moe_status moe_build_tiles(const int32_t* topk_ids, int T, int k, int E, int BM,
                            int32_t* expert_offsets, int32_t* sorted_ids, int32_t* tiles,
                            int32_t* num_tiles, struct ihipStream_t* stream) {

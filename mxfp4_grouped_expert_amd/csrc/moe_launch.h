@@ -21,6 +21,17 @@ void launch_router_topk(const double* partial, const float* bias, int T, int E, 
                         int splits, int32_t* topk_ids, float* topk_weights, double* logits,
                         hipStream_t stream);
 
+// Fused decode path: partial logits, then in the last workgroup the sum,
+// top-k, softmax and tile table (T*E <= 8192, T*k <= 1024).  The workspace
+// starts with a 256-byte counter block that must be zero before first use.
+bool router_fused_ok(int T, int E, int k);
+size_t router_fused_bytes(int T, int H, int E);
+void launch_router_fused(const uint16_t* x, const float* w_router, const float* bias, int T,
+                         int H, int E, int k, int BM, void* workspace, int32_t* topk_ids,
+                         float* topk_weights, double* logits, int32_t* expert_offsets,
+                         int32_t* sorted_ids, int32_t* tiles, int32_t* num_tiles,
+                         hipStream_t stream);
+
 // Tile table: one workgroup counts, scans and scatters.
 void launch_build_tiles(const int32_t* topk_ids, int N, int E, int BM, int32_t* expert_offsets,
                         int32_t* sorted_ids, int32_t* tiles, int32_t* num_tiles,
@@ -35,6 +46,14 @@ void launch_down(const uint16_t* h, const uint8_t* w2_q, const uint8_t* w2_s,
                  const int32_t* sorted_ids, const int32_t* tiles, const int32_t* num_tiles,
                  int tiles_max, int T, int H, int I, int E, int k, int BM, float* y,
                  hipStream_t stream);
+
+// Large-tile (prefill) form of the grouped GEMMs: 128-row tiles, LDS-staged
+// operands.  expert_mma_ok says when the launchers above use it.
+bool expert_mma_ok(int T, int H, int I, int E, int k, int BM);
+void launch_expert_mma(bool gateup, const uint16_t* act, const uint8_t* wq, const uint8_t* ws,
+                       const int32_t* sorted_ids, const int32_t* tiles, const int32_t* num_tiles,
+                       int tiles_max, int T, int H, int I, int E, int k, void* out,
+                       hipStream_t stream);
 
 // Weighted combine back to token order.
 void launch_combine(const float* y, const float* topk_weights, int T, int H, int k,

@@ -22,6 +22,7 @@
 //      expert index); lane 0 takes the softmax of the k winners in fp64.
 #include "moe_device.h"
 #include "moe_launch.h"
+#include "tiles_block.h"
 
 namespace moe {
 
@@ -32,15 +33,20 @@ constexpr int kExpPerWave = 4;
 constexpr int kWavesPerBlock = 4;
 constexpr int kExpPerBlock = kExpPerWave * kWavesPerBlock;
 
-__global__ __launch_bounds__(256) void router_logits_partial(
-    const uint16_t* __restrict__ x, const float* __restrict__ w_router, int T, int H, int E,
-    int split_len, double* __restrict__ partial) {
-  const int wave = threadIdx.x >> 6;
+// One workgroup's share of the partial logits: tokens [4*bx, +4), experts
+// [16*by, +16) (4 per wave), K-range bz.  ATOMIC_OUT stores with agent-scope
+// atomics so another workgroup of the same launch may read them.
+template <bool ATOMIC_OUT>
+__device__ void logits_partial_body(const uint16_t* __restrict__ x,
+                                    const float* __restrict__ w_router, int T, int H, int E,
+                                    int split_len, double* __restrict__ partial, int bx, int by,
+                                    int bz) {
+  const int wave = (threadIdx.x >> 6) & 3;  // wave within this 256-thread expert block
   const int lane = threadIdx.x & 63;
-  const int t0 = blockIdx.x * kTokPerWave;
-  const int e0 = blockIdx.y * kExpPerBlock + wave * kExpPerWave;
-  const int s = blockIdx.z;
-  if (e0 >= E) return;  // wave-uniform; this kernel has no barrier
+  const int t0 = bx * kTokPerWave;
+  const int e0 = by * kExpPerBlock + wave * kExpPerWave;
+  const int s = bz;
+  if (e0 >= E) return;  // wave-uniform; no barrier in this body
   const int kbeg = s * split_len;
   const int kend = min(H, kbeg + split_len);
 
@@ -90,10 +96,22 @@ __global__ __launch_bounds__(256) void router_logits_partial(
       double v = acc[t][e];
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-      if (lane == 0 && t0 + t < T && e0 + e < E)
-        partial[((size_t)s * T + (t0 + t)) * E + (e0 + e)] = v;
+      if (lane == 0 && t0 + t < T && e0 + e < E) {
+        double* dst = &partial[((size_t)s * T + (t0 + t)) * E + (e0 + e)];
+        if (ATOMIC_OUT)
+          __hip_atomic_store(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else
+          *dst = v;
+      }
     }
   }
+}
+
+__global__ __launch_bounds__(256) void router_logits_partial(
+    const uint16_t* __restrict__ x, const float* __restrict__ w_router, int T, int H, int E,
+    int split_len, double* __restrict__ partial) {
+  logits_partial_body<false>(x, w_router, T, H, E, split_len, partial, blockIdx.x, blockIdx.y,
+                             blockIdx.z);
 }
 
 // Total order on doubles as int64 (larger key = larger value); -0 is folded
@@ -105,54 +123,30 @@ __device__ __forceinline__ long long order_key(double v) {
   return b >= 0 ? b : (b ^ 0x7fffffffffffffffLL);
 }
 
-__global__ __launch_bounds__(256) void router_topk_softmax(
-    const double* __restrict__ partial, const float* __restrict__ bias, int T, int E, int k,
-    int splits, int32_t* __restrict__ topk_ids, float* __restrict__ topk_weights,
-    double* __restrict__ logits) {
-  const int wave = threadIdx.x >> 6;
+// Top-k and softmax of one token by one wave.  Lane l holds the logits of
+// experts l, l+64, l+128, l+192 in val[] (entries >= E are ignored).  k
+// rounds of a wave-wide argmax on (higher logit, then lower expert index);
+// lane 0 takes the softmax of the winners in fp64 and writes them (and, if
+// ids_lds is given, the ids there too).
+__device__ void topk_softmax_wave(const double (&val)[4], int E, int k, int t,
+                                  int32_t* __restrict__ topk_ids,
+                                  float* __restrict__ topk_weights, int* ids_lds) {
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * kWavesPerBlock + wave;
-  if (t >= T) return;  // wave-uniform; no barrier below
-
-  // lane owns experts lane, lane+64, lane+128, lane+192
-  double val[4];
   long long key[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = lane + kWave * i;
-    double v = 0.0;
-    if (e < E) {
-      // eight K-range partials in flight at a time, summed in ascending order
-      for (int s0 = 0; s0 < splits; s0 += 8) {
-        double p[8];
-#pragma unroll
-        for (int c = 0; c < 8; ++c)
-          p[c] = (s0 + c < splits) ? partial[((size_t)(s0 + c) * T + t) * E + e] : 0.0;
-#pragma unroll
-        for (int c = 0; c < 8; ++c) v += p[c];
-      }
-      if (bias) v += (double)bias[e];
-      if (logits) logits[(size_t)t * E + e] = v;
-      key[i] = order_key(v);
-    } else {
-      key[i] = LLONG_MIN;  // absent expert: never chosen
-    }
-    val[i] = v;
-  }
+  for (int i = 0; i < 4; ++i) key[i] = (lane + kWave * i < E) ? order_key(val[i]) : LLONG_MIN;
 
   int sel_e[kMaxTopk];
   double sel_v[kMaxTopk];
 #pragma unroll
   for (int j = 0; j < kMaxTopk; ++j) {
     if (j >= k) break;
-    // best candidate of this lane: highest key, then lowest expert index
     long long bk = LLONG_MIN;
     int be = 0x7fffffff;
     double bv = 0.0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int e = lane + kWave * i;
-      if (key[i] > bk) { bk = key[i]; be = e; bv = val[i]; }
+      if (key[i] > bk) { bk = key[i]; be = lane + kWave * i; bv = val[i]; }
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
@@ -183,9 +177,119 @@ __global__ __launch_bounds__(256) void router_topk_softmax(
       if (j < k) {
         topk_ids[(size_t)t * k + j] = sel_e[j];
         topk_weights[(size_t)t * k + j] = (float)(z[j] / sum);
+        if (ids_lds) ids_lds[t * k + j] = sel_e[j];
       }
     }
   }
+}
+
+__global__ __launch_bounds__(256) void router_topk_softmax(
+    const double* __restrict__ partial, const float* __restrict__ bias, int T, int E, int k,
+    int splits, int32_t* __restrict__ topk_ids, float* __restrict__ topk_weights,
+    double* __restrict__ logits) {
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * kWavesPerBlock + wave;
+  if (t >= T) return;  // wave-uniform; no barrier below
+
+  double val[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = lane + kWave * i;
+    double v = 0.0;
+    if (e < E) {
+      // eight K-range partials in flight at a time, summed in ascending order
+      for (int s0 = 0; s0 < splits; s0 += 8) {
+        double p[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+          p[c] = (s0 + c < splits) ? partial[((size_t)(s0 + c) * T + t) * E + e] : 0.0;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) v += p[c];
+      }
+      if (bias) v += (double)bias[e];
+      if (logits) logits[(size_t)t * E + e] = v;
+    }
+    val[i] = v;
+  }
+  topk_softmax_wave(val, E, k, t, topk_ids, topk_weights, nullptr);
+}
+
+// ------------------------------------------------------------ fused decode
+// Logits partials, then (in the last workgroup to finish) the fixed-order
+// sum, top-k, softmax and the tile table, all in one launch.  The workgroups
+// take tickets from a counter at the start of the workspace; the last one
+// resets it to zero, so the counter must be zero before the first call.
+constexpr int kFusedThreads = 1024;  // 16 waves: one token per wave in the tail
+constexpr int kFusedMaxT = 16;
+constexpr int kFusedMaxTE = kFusedMaxT * kMaxExperts;  // logits staged in LDS as fp64
+constexpr int kFusedMaxSlots = kFusedMaxT * kMaxTopk;
+constexpr int kFusedMaxSplits = 32;
+
+__global__ __launch_bounds__(kFusedThreads) void router_decode_fused(
+    const uint16_t* __restrict__ x, const float* __restrict__ w_router,
+    const float* __restrict__ bias, int T, int H, int E, int k, int BM, int split_len,
+    int splits, int* __restrict__ counter, double* __restrict__ partial,
+    int32_t* __restrict__ topk_ids, float* __restrict__ topk_weights,
+    double* __restrict__ logits, int32_t* __restrict__ expert_offsets,
+    int32_t* __restrict__ sorted_ids, int32_t* __restrict__ tiles,
+    int32_t* __restrict__ num_tiles) {
+  __shared__ double s_logits[kFusedMaxTE];
+  __shared__ int s_ids[kFusedMaxSlots];
+  __shared__ TilesScratch<kFusedThreads> S;
+  __shared__ int s_last;
+
+  // Partials are written with agent-scope atomic stores, which are coherent
+  // across the XCDs' L2 caches; waiting for their completion before taking a
+  // ticket orders them before it.  (A full __threadfence would also write
+  // back every dirty line of the L2, in every workgroup.)  The 16 waves
+  // cover 4 expert blocks of the partial grid.
+  logits_partial_body<true>(x, w_router, T, H, E, split_len, partial, blockIdx.x,
+                            blockIdx.y * 4 + (threadIdx.x >> 8), blockIdx.z);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  const int nwg = gridDim.x * gridDim.y * gridDim.z;
+  if (threadIdx.x == 0) s_last = (atomicAdd(counter, 1) == nwg - 1);
+  __syncthreads();
+  if (!s_last) return;  // uniform over the workgroup
+
+  // fixed-order sum of the K-range partials (+ bias); all loads independent
+  const int TE = T * E;
+  for (int i = threadIdx.x; i < TE; i += kFusedThreads) {
+    const int t = i / E;
+    const int e = i - t * E;
+    // every K-range partial of the entry in flight at once, summed in order
+    double p[kFusedMaxSplits];
+#pragma unroll
+    for (int c = 0; c < kFusedMaxSplits; ++c) {
+      const int sc = min(c, splits - 1);  // in bounds; surplus terms dropped below
+      p[c] = __hip_atomic_load(&partial[((size_t)sc * T + t) * E + e], __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    }
+    double v = 0.0;
+#pragma unroll
+    for (int c = 0; c < kFusedMaxSplits; ++c)
+      if (c < splits) v += p[c];
+    if (bias) v += (double)bias[e];
+    s_logits[i] = v;
+    if (logits) logits[i] = v;
+  }
+  __syncthreads();
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  for (int t = wave; t < T; t += kFusedThreads / kWave) {
+    double val[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = lane + kWave * i;
+      val[i] = (e < E) ? s_logits[t * E + e] : 0.0;
+    }
+    topk_softmax_wave(val, E, k, t, topk_ids, topk_weights, s_ids);
+  }
+  __syncthreads();
+  build_tiles_block<kFusedThreads>(static_cast<const int*>(s_ids), T * k, E, BM, S,
+                                   expert_offsets, sorted_ids, tiles, num_tiles);
+  if (threadIdx.x == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace
@@ -193,9 +297,11 @@ __global__ __launch_bounds__(256) void router_topk_softmax(
 RouterPlan router_plan(int T, int H, int E) {
   const long long tb = (T + kTokPerWave - 1) / kTokPerWave;
   const long long eb = (E + kExpPerBlock - 1) / kExpPerBlock;
-  // aim for >= 512 workgroups; keep each K-range >= 128 elements
+  // aim for >= 512 waves of 4x4 (token, expert) pairs; keep each K-range
+  // >= 128 elements and at most 32 of them
   int splits = (int)(512 / (tb * eb));
-  const int max_splits = H / 128 > 0 ? H / 128 : 1;
+  int max_splits = H / 128 > 0 ? H / 128 : 1;
+  if (max_splits > kFusedMaxSplits) max_splits = kFusedMaxSplits;
   if (splits > max_splits) splits = max_splits;
   if (splits < 1) splits = 1;
   int split_len = (H + splits - 1) / splits;
@@ -216,6 +322,32 @@ void launch_router_logits(const uint16_t* x, const float* w_router, int T, int H
             plan.splits);
   hipLaunchKernelGGL(router_logits_partial, grid, dim3(256), 0, stream, x, w_router, T, H, E,
                      plan.split_len, partial);
+}
+
+bool router_fused_ok(int T, int E, int k) {
+  (void)E;
+  (void)k;
+  return T <= kFusedMaxT;
+}
+
+size_t router_fused_bytes(int T, int H, int E) {
+  // 256-byte counter block, then the K-range partials
+  return 256 + router_partial_bytes(T, H, E);
+}
+
+void launch_router_fused(const uint16_t* x, const float* w_router, const float* bias, int T,
+                         int H, int E, int k, int BM, void* workspace, int32_t* topk_ids,
+                         float* topk_weights, double* logits, int32_t* expert_offsets,
+                         int32_t* sorted_ids, int32_t* tiles, int32_t* num_tiles,
+                         hipStream_t stream) {
+  const RouterPlan plan = router_plan(T, H, E);
+  int* counter = static_cast<int*>(workspace);
+  double* partial = reinterpret_cast<double*>(static_cast<char*>(workspace) + 256);
+  const int eb = (E + kExpPerBlock - 1) / kExpPerBlock;
+  dim3 grid((T + kTokPerWave - 1) / kTokPerWave, (eb + 3) / 4, plan.splits);
+  hipLaunchKernelGGL(router_decode_fused, grid, dim3(kFusedThreads), 0, stream, x, w_router, bias,
+                     T, H, E, k, BM, plan.split_len, plan.splits, counter, partial, topk_ids,
+                     topk_weights, logits, expert_offsets, sorted_ids, tiles, num_tiles);
 }
 
 void launch_router_topk(const double* partial, const float* bias, int T, int E, int k,

@@ -1,0 +1,145 @@
+// Block-level builder of the per-expert tile table (shared by the standalone
+// tile kernel and the fused decode router).
+//
+// The SimpleLLM write-up ("A 297-line kernel file that decodes faster than
+// vLLM", section "Optimizations", "Per-expert routing tile table") has each
+// expert write its own tiles instead of the expert GEMM searching a
+// tiles x experts grid.  One workgroup of NT threads does it in LDS, with no
+// order-dependent atomics, so the result is bit-exact and deterministic:
+//   1. count slots per expert (LDS integer adds: totals do not depend on
+//      order); ids outside [0, E) go to a trash bucket E;
+//   2. exclusive scans of the counts (row offsets) and of ceil(count/BM)
+//      (tile offsets), one wave each;
+//   3. stable scatter in chunks of NT slots: within a wave, lanes with the
+//      same expert find each other with nine ballots (one per bit of the
+//      bucket index) and rank themselves with mbcnt; per-wave counts give
+//      each wave's base; a running count per expert carries across chunks,
+//      so slot order inside an expert is ascending;
+//   4. each tile index finds its expert by binary search over the tile
+//      offsets and writes (expert, row_start, rows).
+#pragma once
+
+#include "moe_device.h"
+
+namespace moe {
+
+constexpr int kBuckets = kMaxExperts + 1;  // experts + trash bucket
+
+template <int NT>
+struct TilesScratch {
+  int cnt[kBuckets];
+  int ntile[kBuckets];
+  int off[kBuckets + 1];
+  int toff[kBuckets + 1];
+  int run[kBuckets];
+  int wcnt[NT / kWave][kBuckets];
+};
+
+// Exclusive scan of n <= 320 ints by one wave (5 per lane); writes out[0..n]
+// with out[n] = total.
+__device__ inline void wave_exclusive_scan(const int* in, int* out, int n, int lane) {
+  const int base = lane * 5;
+  int loc[5];
+  int sum = 0;
+#pragma unroll
+  for (int j = 0; j < 5; ++j) {
+    loc[j] = (base + j < n) ? in[base + j] : 0;
+    sum += loc[j];
+  }
+  int incl = sum;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int o = __shfl_up(incl, d);
+    if (lane >= d) incl += o;
+  }
+  int run = incl - sum;
+#pragma unroll
+  for (int j = 0; j < 5; ++j) {
+    if (base + j < n) out[base + j] = run;
+    run += loc[j];
+  }
+  if (lane == kWave - 1) out[n] = incl;
+}
+
+// Builds the table from ids[0..N) (any address space).  Every thread of the
+// NT-thread workgroup must call it; it ends with a barrier.
+template <int NT, typename IdPtr>
+__device__ void build_tiles_block(IdPtr ids, int N, int E, int BM, TilesScratch<NT>& S,
+                                  int32_t* __restrict__ expert_offsets,
+                                  int32_t* __restrict__ sorted_ids, int32_t* __restrict__ tiles,
+                                  int32_t* __restrict__ num_tiles) {
+  constexpr int kW = NT / kWave;
+  static_assert(kW >= 2, "needs two waves for the scans");
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int NB = E + 1;  // buckets in use
+
+  for (int i = tid; i < NB; i += NT) { S.cnt[i] = 0; S.run[i] = 0; }
+  __syncthreads();
+  for (int p = tid; p < N; p += NT) {
+    int e = ids[p];
+    e = (e < 0 || e >= E) ? E : e;
+    atomicAdd(&S.cnt[e], 1);
+  }
+  __syncthreads();
+  for (int i = tid; i < NB; i += NT) S.ntile[i] = (i < E) ? (S.cnt[i] + BM - 1) / BM : 0;
+  __syncthreads();
+  if (wave == 0) wave_exclusive_scan(S.cnt, S.off, NB, lane);
+  if (wave == 1) wave_exclusive_scan(S.ntile, S.toff, NB, lane);
+  __syncthreads();
+  for (int i = tid; i <= E; i += NT) expert_offsets[i] = S.off[i];
+
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int c0 = 0; c0 < N; c0 += NT) {
+    for (int i = tid; i < kW * NB; i += NT) S.wcnt[i / NB][i % NB] = 0;
+    const int p = c0 + tid;
+    const bool valid = p < N;
+    int e = 0;
+    if (valid) {
+      e = ids[p];
+      e = (e < 0 || e >= E) ? E : e;
+    }
+    uint64_t same = __ballot(valid);
+#pragma unroll
+    for (int bit = 0; bit < 9; ++bit) {
+      const bool b = (e >> bit) & 1;
+      const uint64_t bal = __ballot(b);
+      same &= b ? bal : ~bal;
+    }
+    const int rank = lanes_below(same);
+    __syncthreads();  // wcnt zeroed
+    if (valid && (same & ~lt_mask & ~(1ull << lane)) == 0)  // last lane of its group
+      S.wcnt[wave][e] = rank + 1;
+    __syncthreads();
+    if (valid) {
+      int before = S.off[e] + S.run[e] + rank;
+      for (int w = 0; w < wave; ++w) before += S.wcnt[w][e];
+      sorted_ids[before] = p;
+    }
+    __syncthreads();
+    for (int i = tid; i < NB; i += NT) {
+      int add = 0;
+      for (int w = 0; w < kW; ++w) add += S.wcnt[w][i];
+      S.run[i] += add;
+    }
+    __syncthreads();
+  }
+
+  const int total = S.toff[E];
+  for (int i = tid; i < total; i += NT) {
+    int lo = 0, hi = E - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (S.toff[mid] <= i) lo = mid; else hi = mid - 1;
+    }
+    const int j = i - S.toff[lo];
+    tiles[3 * i + 0] = lo;
+    tiles[3 * i + 1] = S.off[lo] + j * BM;
+    tiles[3 * i + 2] = min(BM, S.cnt[lo] - j * BM);
+  }
+  if (tid == 0) num_tiles[0] = total;
+  __syncthreads();
+}
+
+}  // namespace moe

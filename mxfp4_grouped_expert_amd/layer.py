@@ -38,8 +38,11 @@ class MoeLayer:
         self.BM = B.pick_bm(T, k, E) if BM is None else BM
         self.topk_ids = torch.empty((T, k), dtype=torch.int32, device=dev)
         self.topk_weights = torch.empty((T, k), dtype=torch.float32, device=dev)
-        self.route_ws = torch.empty(max(B.route_workspace_bytes(T, H, E), 16), dtype=torch.uint8,
-                                    device=dev)
+        # small batches route and tile in one launch (moe_route_tiles); its
+        # workspace must start zeroed, and every call leaves it that way
+        self.fused = B.route_tiles_ok(T, E, k)
+        ws = B.route_tiles_workspace_bytes(T, H, E) if self.fused else B.route_workspace_bytes(T, H, E)
+        self.route_ws = torch.zeros(max(ws, 256), dtype=torch.uint8, device=dev)
         self.offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
         self.sorted_ids = torch.empty(max(T * k, 1), dtype=torch.int32, device=dev)
         self.tiles_max = B.tiles_max(T, k, E, self.BM)
@@ -60,16 +63,25 @@ class MoeLayer:
         return None if t is None else ctypes.c_void_p(t.data_ptr())
 
     def route_only(self, x: torch.Tensor):
-        """moe_route into the layer's buffers."""
+        """moe_route (or, for small batches, moe_route_tiles) into the layer's buffers."""
         lib, s = self._args()
         p = self._p
         T, E, H, k = x.shape[0], self.E, self.H, self.k
+        if self.fused:
+            B._check(lib.moe_route_tiles(p(x), p(self.w_router), p(self.bias), T, H, E, k, self.BM,
+                                         p(self.topk_ids), p(self.topk_weights), None,
+                                         p(self.offsets), p(self.sorted_ids), p(self.tiles),
+                                         p(self.num_tiles), p(self.route_ws),
+                                         self.route_ws.numel(), s), "moe_route_tiles")
+            return
         B._check(lib.moe_route(p(x), p(self.w_router), p(self.bias), T, H, E, k,
                                p(self.topk_ids), p(self.topk_weights), None, p(self.route_ws),
                                self.route_ws.numel(), s), "moe_route")
 
     def tiles_only(self):
-        """moe_build_tiles from the layer's topk_ids."""
+        """moe_build_tiles from the layer's topk_ids (already done when fused)."""
+        if self.fused:
+            return
         lib, s = self._args()
         p = self._p
         B._check(lib.moe_build_tiles(p(self.topk_ids), self.T, self.k, self.E, self.BM,

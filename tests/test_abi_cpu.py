@@ -128,6 +128,29 @@ def test_forward_validation(kw, want):
     assert _forward(**kw) == want
 
 
+def _route_tiles(**kw):
+    a = dict(x=P, w=P, bias=None, T=4, H=256, E=8, k=2, BM=16, ids=P, wts=P, logits=None, off=P,
+             srt=P, tiles=P, nt=P, ws=P, wsb=1 << 20)
+    a.update(kw)
+    return B.load().moe_route_tiles(a["x"], a["w"], a["bias"], a["T"], a["H"], a["E"], a["k"],
+                                    a["BM"], a["ids"], a["wts"], a["logits"], a["off"], a["srt"],
+                                    a["tiles"], a["nt"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(x=None), NULL), (dict(tiles=None), NULL), (dict(ws=None), NULL), (dict(nt=None), NULL),
+    (dict(T=17, E=128), SHAPE), (dict(T=64, k=4, E=8), SHAPE), (dict(BM=8), SHAPE),
+    (dict(H=48), SHAPE), (dict(x=PMIS), ALIGN), (dict(wsb=16), WORKSPACE), (dict(T=0, x=None), OK),
+])
+def test_route_tiles_validation(kw, want):
+    assert _route_tiles(**kw) == want
+
+
+def test_route_tiles_limits_and_workspace():
+    assert moe.route_tiles_ok(16, 256, 8) and not moe.route_tiles_ok(17, 8, 1)
+    assert moe.route_tiles_workspace_bytes(1, 2880, 32) >= 256 + moe.route_workspace_bytes(1, 2880, 32) - 256
+
+
 def _steps(which, **kw):
     a = dict(x=P, q=P, s=P, srt=P, tiles=P, nt=P, T=4, H=256, I=512, E=8, k=2, BM=16, o=P, w=P)
     a.update(kw)
@@ -161,6 +184,7 @@ def test_valid_arguments_reach_the_device_check():
     assert _forward() == DEVICE
     for which in ("gateup", "down", "combine"):
         assert _steps(which) == DEVICE
+    assert _route_tiles() == DEVICE
 
 
 def test_binding_raises_on_error_status():

@@ -94,6 +94,11 @@ RANDOM_CASES = [
     (700, 64, 33, 2, 32, True, 0.5, 32),     # tile scatter over 2 chunks
     (4100, 32, 256, 8, 32, False, 1.0, 128), # E and k at their maxima, 33 chunks
     (40, 2880, 4, 4, 64, False, 0.02, 32),   # k = E: every expert used
+    # large token tiles (128-row MFMA kernel): two tiles per expert, a K tail
+    # (5 MX blocks), partial column blocks (224 and 160 outputs)
+    (300, 160, 4, 2, 224, False, 0.3, 128),
+    (512, 2880, 16, 2, 2880, True, 0.5, 128),
+    (160, 96, 2, 1, 32, False, 0.3, 128),
 ]
 
 
