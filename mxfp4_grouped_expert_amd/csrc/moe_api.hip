@@ -176,7 +176,7 @@ moe_status moe_gateup_swiglu(const uint16_t* x, const uint8_t* w13_q, const uint
   if (!forward_shape_ok(T, H, I, E, k, BM)) return MOE_ERR_SHAPE;
   if (T == 0) return MOE_OK;
   if (!x || !w13_q || !w13_s || !sorted_ids || !tiles || !num_tiles || !h) return MOE_ERR_NULL;
-  if (!aligned16(x) || !aligned16(w13_q)) return MOE_ERR_ALIGN;
+  if (!aligned16(x) || !aligned16(w13_q) || !aligned16(w13_s)) return MOE_ERR_ALIGN;
   moe_status st = check_device();
   if (st != MOE_OK) return st;
   (void)hipGetLastError();
@@ -193,7 +193,7 @@ moe_status moe_down(const uint16_t* h, const uint8_t* w2_q, const uint8_t* w2_s,
   if (!forward_shape_ok(T, H, I, E, k, BM)) return MOE_ERR_SHAPE;
   if (T == 0) return MOE_OK;
   if (!h || !w2_q || !w2_s || !sorted_ids || !tiles || !num_tiles || !y) return MOE_ERR_NULL;
-  if (!aligned16(h) || !aligned16(w2_q)) return MOE_ERR_ALIGN;
+  if (!aligned16(h) || !aligned16(w2_q) || !aligned16(w2_s)) return MOE_ERR_ALIGN;
   moe_status st = check_device();
   if (st != MOE_OK) return st;
   (void)hipGetLastError();
@@ -227,7 +227,8 @@ moe_status moe_forward(const uint16_t* x, const uint8_t* w13_q, const uint8_t* w
   if (!x || !w13_q || !w13_s || !w2_q || !w2_s || !topk_weights || !sorted_ids || !tiles ||
       !num_tiles || !workspace || !out)
     return MOE_ERR_NULL;
-  if (!aligned16(x) || !aligned16(w13_q) || !aligned16(w2_q) || !aligned16(workspace))
+  if (!aligned16(x) || !aligned16(w13_q) || !aligned16(w13_s) || !aligned16(w2_q) ||
+      !aligned16(w2_s) || !aligned16(workspace))
     return MOE_ERR_ALIGN;
   if (workspace_bytes < moe_forward_workspace_bytes(T, H, I, k)) return MOE_ERR_WORKSPACE;
   moe_status st = check_device();

@@ -121,8 +121,8 @@ def test_build_tiles_validation(kw, want):
     (dict(x=None), NULL), (dict(q13=None), NULL), (dict(s2=None), NULL), (dict(ws=None), NULL),
     (dict(out=None), NULL), (dict(nt=None), NULL),
     (dict(H=100), SHAPE), (dict(I=48), SHAPE), (dict(k=3, E=2), SHAPE), (dict(BM=24), SHAPE),
-    (dict(q13=PMIS), ALIGN), (dict(ws=PMIS), ALIGN), (dict(wsb=1000), WORKSPACE),
-    (dict(T=0, x=None), OK),
+    (dict(q13=PMIS), ALIGN), (dict(s13=PMIS), ALIGN), (dict(s2=PMIS), ALIGN),
+    (dict(ws=PMIS), ALIGN), (dict(wsb=1000), WORKSPACE), (dict(T=0, x=None), OK),
 ])
 def test_forward_validation(kw, want):
     assert _forward(**kw) == want
@@ -167,9 +167,11 @@ def _steps(which, **kw):
 @pytest.mark.parametrize("which", ["gateup", "down", "combine"])
 @pytest.mark.parametrize("kw,want", [
     (dict(x=None), NULL), (dict(o=None), NULL), (dict(H=48), SHAPE), (dict(k=0), SHAPE),
-    (dict(x=PMIS), ALIGN), (dict(T=0, x=None), OK),
+    (dict(x=PMIS), ALIGN), (dict(s=PMIS), ALIGN), (dict(T=0, x=None), OK),
 ])
 def test_step_entry_points_validation(which, kw, want):
+    if which == "combine" and "s" in kw:
+        pytest.skip("moe_combine takes no scale array")
     assert _steps(which, **kw) == want
 
 
