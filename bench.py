@@ -93,6 +93,29 @@ def cpu_baseline(inp, seconds):
             "sample": f"{what}; {calls} call(s) in {el:.1f} s of float64 numpy"}
 
 
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` at `workload` from the rocprofv3
+    FETCH_SIZE/WRITE_SIZE summary in profiles/, or None when there is no row
+    or the kernel source changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                        "traffic_counters.md")
+    if not os.path.exists(path):
+        return None
+    root = os.path.dirname(path)[: -len("profiles")]
+    for line in open(path):
+        cells = [c.strip() for c in line.strip().strip("|").split("|")]
+        if len(cells) != 9 or cells[0] != workload or cells[1] != kernel:
+            continue
+        src = os.path.join(root, cells[7])
+        if not os.path.exists(src):
+            return None
+        if hashlib.sha256(open(src, "rb").read()).hexdigest()[:16] != cells[8]:
+            return None
+        return int(cells[6])
+    return None
+
+
 def main():
     args = parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -238,16 +261,19 @@ def main():
     if T <= 64:
         gu_bytes = n_touched * gateup_bytes(H, I) + T * H * 2 + T * k * I * 2
         achieved = gu_bytes / (gu_us * 1e-6) / 1e9
-        roof = {"kernel": "gateup_swiglu_kernel", "bound": "hbm", "achieved": round(achieved, 1),
+        kname = "expert_gemm_kernel<gate/up>"
+        roof = {"kernel": kname, "bound": "hbm", "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": None, "algorithmic_bytes_per_launch": gu_bytes,
-                "avg_launch_us": round(gu_us, 2)}
+                "traffic": measured_traffic(inp["name"], kname),
+                "algorithmic_bytes_per_launch": gu_bytes, "avg_launch_us": round(gu_us, 2)}
     else:
         gu_flops = 2 * T * k * 2 * I * H
         achieved = gu_flops / (gu_us * 1e-6) / 1e12
-        roof = {"kernel": "gateup_swiglu_kernel", "bound": "mfma", "achieved": round(achieved, 1),
+        kname = "expert_mma_kernel<gate/up>" if BM == 128 else "expert_gemm_kernel<gate/up>"
+        roof = {"kernel": kname, "bound": "mfma", "achieved": round(achieved, 1),
                 "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+                "traffic": measured_traffic(inp["name"], kname),
                 "algorithmic_flops_per_launch": gu_flops, "avg_launch_us": round(gu_us, 2)}
 
     gbps = touched / (us * 1e-6) / 1e9
