@@ -168,7 +168,11 @@ __global__ __launch_bounds__(256 * NBW) void expert_gemm_kernel(
     s_rowoff[tid] = off;
     s_slot[tid] = my_slot;
   }
-  __syncthreads();
+  // LDS-only barrier: __syncthreads would also wait for the whole weight
+  // stream issued above, and the activation staging below would no longer
+  // overlap it (the slot-id load was issued first, so using it waited only
+  // for that load)
+  lds_barrier();
 
   // Pass 0's activations are staged while the weight stream is in flight;
   // one wait covers both.  With K <= kChunk*512 (ONECHUNK) a wave's whole

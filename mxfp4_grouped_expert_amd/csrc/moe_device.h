@@ -63,6 +63,14 @@ __device__ __forceinline__ floatx4 mfma16x16x32(bf16x8 a, bf16x8 b, floatx4 c) {
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
+// Workgroup barrier for phases that exchange data through LDS only: waits
+// for this wave's LDS operations, not for its global stores (__syncthreads
+// also waits for every outstanding global access, i.e. for store
+// acknowledgements from memory).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Number of lanes below this one whose bit is set in `mask`.
 __device__ __forceinline__ int lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),

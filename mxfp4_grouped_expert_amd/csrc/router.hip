@@ -33,40 +33,40 @@ constexpr int kExpPerWave = 4;
 constexpr int kWavesPerBlock = 4;
 constexpr int kExpPerBlock = kExpPerWave * kWavesPerBlock;
 
-// One workgroup's share of the partial logits: tokens [4*bx, +4), experts
+// One workgroup's share of the partial logits: tokens [TPW*bx, +TPW), experts
 // [16*by, +16) (4 per wave), K-range bz.  ATOMIC_OUT stores with agent-scope
 // atomics so another workgroup of the same launch may read them.
-template <bool ATOMIC_OUT>
+template <bool ATOMIC_OUT, int TPW = kTokPerWave>
 __device__ void logits_partial_body(const uint16_t* __restrict__ x,
                                     const float* __restrict__ w_router, int T, int H, int E,
                                     int split_len, double* __restrict__ partial, int bx, int by,
                                     int bz) {
   const int wave = (threadIdx.x >> 6) & 3;  // wave within this 256-thread expert block
   const int lane = threadIdx.x & 63;
-  const int t0 = bx * kTokPerWave;
+  const int t0 = bx * TPW;
   const int e0 = by * kExpPerBlock + wave * kExpPerWave;
   const int s = bz;
   if (e0 >= E) return;  // wave-uniform; no barrier in this body
   const int kbeg = s * split_len;
   const int kend = min(H, kbeg + split_len);
 
-  const uint16_t* xr[kTokPerWave];
+  const uint16_t* xr[TPW];
 #pragma unroll
-  for (int t = 0; t < kTokPerWave; ++t) xr[t] = x + (size_t)min(t0 + t, T - 1) * H;
+  for (int t = 0; t < TPW; ++t) xr[t] = x + (size_t)min(t0 + t, T - 1) * H;
   const float* wr[kExpPerWave];
 #pragma unroll
   for (int e = 0; e < kExpPerWave; ++e) wr[e] = w_router + (size_t)min(e0 + e, E - 1) * H;
 
-  double acc[kTokPerWave][kExpPerWave];
+  double acc[TPW][kExpPerWave];
 #pragma unroll
-  for (int t = 0; t < kTokPerWave; ++t)
+  for (int t = 0; t < TPW; ++t)
 #pragma unroll
     for (int e = 0; e < kExpPerWave; ++e) acc[t][e] = 0.0;
 
   for (int kk = kbeg + 4 * lane; kk < kend; kk += 4 * kWave) {
-    double xv[kTokPerWave][4];
+    double xv[TPW][4];
 #pragma unroll
-    for (int t = 0; t < kTokPerWave; ++t) {
+    for (int t = 0; t < TPW; ++t) {
       const uint2 v = *reinterpret_cast<const uint2*>(xr[t] + kk);
       xv[t][0] = (double)bf16_to_float(v.x & 0xffffu);
       xv[t][1] = (double)bf16_to_float(v.x >> 16);
@@ -78,7 +78,7 @@ __device__ void logits_partial_body(const uint16_t* __restrict__ x,
       const float4 w = *reinterpret_cast<const float4*>(wr[e] + kk);
       const double w0 = w.x, w1 = w.y, w2 = w.z, w3 = w.w;
 #pragma unroll
-      for (int t = 0; t < kTokPerWave; ++t) {
+      for (int t = 0; t < TPW; ++t) {
         double a = acc[t][e];
         a = fma(xv[t][0], w0, a);
         a = fma(xv[t][1], w1, a);
@@ -90,7 +90,7 @@ __device__ void logits_partial_body(const uint16_t* __restrict__ x,
   }
 
 #pragma unroll
-  for (int t = 0; t < kTokPerWave; ++t) {
+  for (int t = 0; t < TPW; ++t) {
 #pragma unroll
     for (int e = 0; e < kExpPerWave; ++e) {
       double v = acc[t][e];
@@ -121,6 +121,32 @@ __device__ __forceinline__ long long order_key(double v) {
   if (v != v) return LLONG_MIN + 1;
   long long b = __double_as_longlong(v);
   return b >= 0 ? b : (b ^ 0x7fffffffffffffffLL);
+}
+
+// Softmax over the k selected logits of token t (in selection order), in
+// fp64; writes ids and weights (and the ids to ids_lds when given).  Both
+// routing paths use it, so their weights are bit-identical.
+__device__ __forceinline__ void softmax_selected(const int* sel_e, const double* sel_v, int k,
+                                                 int t, int32_t* __restrict__ topk_ids,
+                                                 float* __restrict__ topk_weights,
+                                                 int* ids_lds) {
+  double m = sel_v[0];
+#pragma unroll
+  for (int j = 1; j < kMaxTopk; ++j)
+    if (j < k) m = fmax(m, sel_v[j]);
+  double z[kMaxTopk];
+  double sum = 0.0;
+#pragma unroll
+  for (int j = 0; j < kMaxTopk; ++j)
+    if (j < k) { z[j] = exp(sel_v[j] - m); sum += z[j]; }
+#pragma unroll
+  for (int j = 0; j < kMaxTopk; ++j) {
+    if (j < k) {
+      topk_ids[(size_t)t * k + j] = sel_e[j];
+      topk_weights[(size_t)t * k + j] = (float)(z[j] / sum);
+      if (ids_lds) ids_lds[t * k + j] = sel_e[j];
+    }
+  }
 }
 
 // Top-k and softmax of one token by one wave.  Lane l holds the logits of
@@ -162,25 +188,7 @@ __device__ void topk_softmax_wave(const double (&val)[4], int E, int k, int t,
       if (lane + kWave * i == be) key[i] = LLONG_MIN;
   }
 
-  if (lane == 0) {
-    double m = sel_v[0];
-#pragma unroll
-    for (int j = 1; j < kMaxTopk; ++j)
-      if (j < k) m = fmax(m, sel_v[j]);
-    double z[kMaxTopk];
-    double sum = 0.0;
-#pragma unroll
-    for (int j = 0; j < kMaxTopk; ++j)
-      if (j < k) { z[j] = exp(sel_v[j] - m); sum += z[j]; }
-#pragma unroll
-    for (int j = 0; j < kMaxTopk; ++j) {
-      if (j < k) {
-        topk_ids[(size_t)t * k + j] = sel_e[j];
-        topk_weights[(size_t)t * k + j] = (float)(z[j] / sum);
-        if (ids_lds) ids_lds[t * k + j] = sel_e[j];
-      }
-    }
-  }
+  if (lane == 0) softmax_selected(sel_e, sel_v, k, t, topk_ids, topk_weights, ids_lds);
 }
 
 __global__ __launch_bounds__(256) void router_topk_softmax(
@@ -236,6 +244,10 @@ __global__ __launch_bounds__(kFusedThreads) void router_decode_fused(
     int32_t* __restrict__ num_tiles) {
   __shared__ double s_logits[kFusedMaxTE];
   __shared__ int s_ids[kFusedMaxSlots];
+  __shared__ long long s_key[kFusedMaxTE];
+  __shared__ int s_sel_e[kFusedMaxSlots];
+  __shared__ double s_sel_v[kFusedMaxSlots];
+  __shared__ double s_z[kFusedMaxSlots];
   __shared__ TilesScratch<kFusedThreads> S;
   __shared__ int s_last;
 
@@ -244,8 +256,13 @@ __global__ __launch_bounds__(kFusedThreads) void router_decode_fused(
   // ticket orders them before it.  (A full __threadfence would also write
   // back every dirty line of the L2, in every workgroup.)  The 16 waves
   // cover 4 expert blocks of the partial grid.
-  logits_partial_body<true>(x, w_router, T, H, E, split_len, partial, blockIdx.x,
-                            blockIdx.y * 4 + (threadIdx.x >> 8), blockIdx.z);
+  // (one token: one token per wave, so no wave computes copies of it)
+  if (T == 1)
+    logits_partial_body<true, 1>(x, w_router, T, H, E, split_len, partial, blockIdx.x,
+                                 blockIdx.y * 4 + (threadIdx.x >> 8), blockIdx.z);
+  else
+    logits_partial_body<true>(x, w_router, T, H, E, split_len, partial, blockIdx.x,
+                              blockIdx.y * 4 + (threadIdx.x >> 8), blockIdx.z);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   const int nwg = gridDim.x * gridDim.y * gridDim.z;
@@ -274,20 +291,54 @@ __global__ __launch_bounds__(kFusedThreads) void router_decode_fused(
     s_logits[i] = v;
     if (logits) logits[i] = v;
   }
-  __syncthreads();
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
-  for (int t = wave; t < T; t += kFusedThreads / kWave) {
-    double val[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = lane + kWave * i;
-      val[i] = (e < E) ? s_logits[t * E + e] : 0.0;
+  // top-k by rank: an entry's rank is the number of its token's experts
+  // with a larger order key, or an equal one and a lower index (the order of
+  // the k argmax rounds of the unfused path), so ranks < k are the picks in
+  // selection order
+  for (int i = threadIdx.x; i < TE; i += kFusedThreads) s_key[i] = order_key(s_logits[i]);
+  lds_barrier();
+  for (int i = threadIdx.x; i < TE; i += kFusedThreads) {
+    const int t = i / E;
+    const int e = i - t * E;
+    const long long ki = s_key[i];
+    const long long* kt = s_key + t * E;
+    int rank = 0;
+#pragma unroll 8
+    for (int j = 0; j < E; ++j) {
+      const long long kj = kt[j];
+      rank += (kj > ki) | ((kj == ki) & (j < e));
     }
-    topk_softmax_wave(val, E, k, t, topk_ids, topk_weights, s_ids);
+    if (rank < k) {
+      s_sel_e[t * kMaxTopk + rank] = e;
+      s_sel_v[t * kMaxTopk + rank] = s_logits[i];
+    }
   }
-  __syncthreads();
-  build_tiles_block<kFusedThreads>(static_cast<const int*>(s_ids), T * k, E, BM, S,
+  lds_barrier();
+  // softmax: the k exponentials of a token in parallel, then each of its
+  // threads sums them in ascending j, the order of softmax_selected, so the
+  // weights are bit-identical to the unfused path
+  for (int i = threadIdx.x; i < T * k; i += kFusedThreads) {
+    const int t = i / k;
+    const int j = i - t * k;
+    const double* v = s_sel_v + t * kMaxTopk;
+    double m = v[0];
+    for (int q = 1; q < k; ++q) m = fmax(m, v[q]);
+    s_z[t * kMaxTopk + j] = exp(v[j] - m);
+  }
+  lds_barrier();
+  for (int i = threadIdx.x; i < T * k; i += kFusedThreads) {
+    const int t = i / k;
+    const int j = i - t * k;
+    const double* z = s_z + t * kMaxTopk;
+    double sum = 0.0;
+    for (int q = 0; q < k; ++q) sum += z[q];
+    const int e = s_sel_e[t * kMaxTopk + j];
+    topk_ids[(size_t)t * k + j] = e;
+    topk_weights[(size_t)t * k + j] = (float)(z[j] / sum);
+    s_ids[t * k + j] = e;
+  }
+  lds_barrier();
+  build_tiles_small<kFusedThreads>(static_cast<const int*>(s_ids), T * k, E, BM, S,
                                    expert_offsets, sorted_ids, tiles, num_tiles);
   if (threadIdx.x == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

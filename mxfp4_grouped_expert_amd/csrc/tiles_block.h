@@ -62,7 +62,8 @@ __device__ inline void wave_exclusive_scan(const int* in, int* out, int n, int l
 }
 
 // Builds the table from ids[0..N) (any address space).  Every thread of the
-// NT-thread workgroup must call it; it ends with a barrier.
+// NT-thread workgroup must call it; it ends with a barrier.  Phases exchange
+// data through LDS only, so the barriers do not wait for global stores.
 template <int NT, typename IdPtr>
 __device__ void build_tiles_block(IdPtr ids, int N, int E, int BM, TilesScratch<NT>& S,
                                   int32_t* __restrict__ expert_offsets,
@@ -76,18 +77,18 @@ __device__ void build_tiles_block(IdPtr ids, int N, int E, int BM, TilesScratch<
   const int NB = E + 1;  // buckets in use
 
   for (int i = tid; i < NB; i += NT) { S.cnt[i] = 0; S.run[i] = 0; }
-  __syncthreads();
+  lds_barrier();
   for (int p = tid; p < N; p += NT) {
     int e = ids[p];
     e = (e < 0 || e >= E) ? E : e;
     atomicAdd(&S.cnt[e], 1);
   }
-  __syncthreads();
+  lds_barrier();
   for (int i = tid; i < NB; i += NT) S.ntile[i] = (i < E) ? (S.cnt[i] + BM - 1) / BM : 0;
-  __syncthreads();
+  lds_barrier();
   if (wave == 0) wave_exclusive_scan(S.cnt, S.off, NB, lane);
   if (wave == 1) wave_exclusive_scan(S.ntile, S.toff, NB, lane);
-  __syncthreads();
+  lds_barrier();
   for (int i = tid; i <= E; i += NT) expert_offsets[i] = S.off[i];
 
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
@@ -108,22 +109,22 @@ __device__ void build_tiles_block(IdPtr ids, int N, int E, int BM, TilesScratch<
       same &= b ? bal : ~bal;
     }
     const int rank = lanes_below(same);
-    __syncthreads();  // wcnt zeroed
+    lds_barrier();  // wcnt zeroed
     if (valid && (same & ~lt_mask & ~(1ull << lane)) == 0)  // last lane of its group
       S.wcnt[wave][e] = rank + 1;
-    __syncthreads();
+    lds_barrier();
     if (valid) {
       int before = S.off[e] + S.run[e] + rank;
       for (int w = 0; w < wave; ++w) before += S.wcnt[w][e];
       sorted_ids[before] = p;
     }
-    __syncthreads();
+    lds_barrier();
     for (int i = tid; i < NB; i += NT) {
       int add = 0;
       for (int w = 0; w < kW; ++w) add += S.wcnt[w][i];
       S.run[i] += add;
     }
-    __syncthreads();
+    lds_barrier();
   }
 
   const int total = S.toff[E];
@@ -139,7 +140,72 @@ __device__ void build_tiles_block(IdPtr ids, int N, int E, int BM, TilesScratch<
     tiles[3 * i + 2] = min(BM, S.cnt[lo] - j * BM);
   }
   if (tid == 0) num_tiles[0] = total;
-  __syncthreads();
+  lds_barrier();
+}
+
+// The same table for small slot counts (N <= NT slots, e.g. a decode batch)
+// with the ids already in LDS, in all-pairs form: every quantity is an
+// independent count over LDS, so the table takes two barriers and no scans.
+//   slot p:    position = #{q : (b_q, q) < (b_p, p)}, b = bucket of the id
+//              (ids outside [0, E) go to bucket E), so sorted_ids is the
+//              stable counting sort of build_tiles_block;
+//   expert e:  offset = #{q : b_q < e}, count = #{q : b_q = e};
+//   expert e:  tile offset = sum over e' < e of ceil(count_e' / BM).
+// Results are identical to build_tiles_block.  Every thread of the
+// NT-thread workgroup must call it (NT > E); it ends with a barrier.
+template <int NT>
+__device__ void build_tiles_small(const int* ids, int N, int E, int BM, TilesScratch<NT>& S,
+                                  int32_t* __restrict__ expert_offsets,
+                                  int32_t* __restrict__ sorted_ids, int32_t* __restrict__ tiles,
+                                  int32_t* __restrict__ num_tiles) {
+  static_assert(NT > kMaxExperts, "one thread per bucket");
+  const int tid = threadIdx.x;
+  int* bk = &S.wcnt[0][0];  // bucket of each slot (N <= NT <= NT/64 * kBuckets)
+  for (int p = tid; p < N; p += NT) {
+    const int e = ids[p];
+    bk[p] = (e < 0 || e >= E) ? E : e;
+  }
+  lds_barrier();
+  for (int p = tid; p < N; p += NT) {
+    const int b = bk[p];
+    int pos = 0;
+#pragma unroll 8
+    for (int q = 0; q < N; ++q) {
+      const int c = bk[q];
+      pos += (c < b) | ((c == b) & (q < p));
+    }
+    sorted_ids[pos] = p;
+  }
+  if (tid <= E) {
+    int off = 0, cnt = 0;
+#pragma unroll 8
+    for (int q = 0; q < N; ++q) {
+      const int c = bk[q];
+      off += c < tid;
+      cnt += c == tid;
+    }
+    expert_offsets[tid] = off;
+    S.off[tid] = off;
+    S.cnt[tid] = cnt;
+    S.ntile[tid] = (tid < E) ? (cnt + BM - 1) / BM : 0;
+  }
+  lds_barrier();
+  if (tid <= E) {
+    int toff = 0;
+#pragma unroll 8
+    for (int e = 0; e < tid; ++e) toff += S.ntile[e];
+    if (tid == E) {
+      num_tiles[0] = toff;
+    } else {
+      const int off = S.off[tid], cnt = S.cnt[tid];
+      for (int j = 0; j < S.ntile[tid]; ++j) {
+        tiles[3 * (toff + j) + 0] = tid;
+        tiles[3 * (toff + j) + 1] = off + j * BM;
+        tiles[3 * (toff + j) + 2] = min(BM, cnt - j * BM);
+      }
+    }
+  }
+  lds_barrier();
 }
 
 }  // namespace moe
