@@ -55,6 +55,14 @@ __device__ __forceinline__ uint32_t word(const uint4& q, int j) {
   return j == 0 ? q.x : j == 1 ? q.y : j == 2 ? q.z : q.w;
 }
 
+// Scale table: the E8M0 bytes of a workgroup's weight rows.  The 16 rows of
+// one (16-row block, gate/up half) are consecutive rows of the matrix, so
+// their scales are one contiguous run of 16*KB bytes; the runs are loaded
+// with byte loads in which a wave instruction reads 64 consecutive bytes
+// (one or two cache lines, where per-lane loads of each row's byte touch a
+// line per row).  ONECHUNK kernels only (K <= kChunk * 512, KB <= 96).
+constexpr int kScaleRunMax = kRowsPerBlock * kChunk * kBlocksPerStep;  // 1536 bytes
+
 // Row stride of the staged activations in LDS: K bf16 plus a 16-byte pad.
 __host__ __device__ __forceinline__ int act_stride_bytes(int K) { return K * 2 + 16; }
 
@@ -119,9 +127,41 @@ __global__ __launch_bounds__(256 * NBW) void expert_gemm_kernel(
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
         wreg[c][w] = *reinterpret_cast<const uint4*>(wq + wrow[w] * q_stride + (size_t)bc * 16);
-        sreg[c][w] = ws[wrow[w] * s_stride + bc];
+        if constexpr (!ONECHUNK) sreg[c][w] = ws[wrow[w] * s_stride + bc];
       }
     }
+  };
+
+  // ONECHUNK: the workgroup's scale runs (run nb*NW + w: rows of block nb,
+  // half w), kSrun bytes per thread and run, every load issued before any
+  // wait (clamped addresses), written to LDS after the stream has landed
+  constexpr int kRuns = ONECHUNK ? NBW * NW : 1;
+  constexpr int kThreads = 256 * NBW;
+  constexpr int kSrun = (kScaleRunMax + kThreads - 1) / kThreads;
+  __shared__ unsigned char s_sc[ONECHUNK ? NBW * NW * kScaleRunMax : 1];
+  uint32_t srun[kRuns][kSrun];
+  const int runlen = kRowsPerBlock * KB;
+  auto load_scale_runs = [&]() {
+#pragma unroll
+    for (int r = 0; r < kRuns; ++r) {
+      const int rb = r / NW, rw = r % NW;
+      const int nb0 = (blockIdx.y * NBW + rb) * kRowsPerBlock;
+      const int row0 = nb0 < N ? nb0 : 0;  // blocks past N read block 0's rows
+      const size_t grow0 = GATEUP ? (size_t)e * 2 * I + (size_t)rw * I + row0
+                                  : (size_t)e * H + row0;
+      const uint8_t* src = ws + grow0 * s_stride;
+#pragma unroll
+      for (int u = 0; u < kSrun; ++u) srun[r][u] = src[min(tid + u * kThreads, runlen - 1)];
+    }
+  };
+  auto store_scale_runs = [&]() {
+#pragma unroll
+    for (int r = 0; r < kRuns; ++r)
+#pragma unroll
+      for (int u = 0; u < kSrun; ++u) {
+        const int i = tid + u * kThreads;
+        if (i < runlen) s_sc[r * kScaleRunMax + i] = (unsigned char)srun[r][u];
+      }
   };
 
   // Per-tile row table in LDS: the element offset of each row's activations
@@ -156,7 +196,10 @@ __global__ __launch_bounds__(256 * NBW) void expert_gemm_kernel(
     }
   };
 
-  if constexpr (ONECHUNK) load_weights(0);  // depends only on the tile row
+  if constexpr (ONECHUNK) {  // depends only on the tile row
+    load_weights(0);
+    load_scale_runs();
+  }
   if (tid < rows) {
     long long off;
     if (GATEUP) {
@@ -179,6 +222,7 @@ __global__ __launch_bounds__(256 * NBW) void expert_gemm_kernel(
   // share of the weights is loaded once and reused by every pass.
   stage_acts(0, min(XR, rows));
   __builtin_amdgcn_s_waitcnt(0);
+  if constexpr (ONECHUNK) store_scale_runs();
   __syncthreads();
 
   for (int pass = 0; pass < npass; ++pass) {
@@ -192,6 +236,13 @@ __global__ __launch_bounds__(256 * NBW) void expert_gemm_kernel(
     }
 
     if constexpr (ONECHUNK) {
+      // scale bytes of this lane's rows from the table
+#pragma unroll
+      for (int c = 0; c < kChunk; ++c) {
+        const int bc = min(c * kBlocksPerStep + kq * 4 + grp, KB - 1);
+#pragma unroll
+        for (int w = 0; w < NW; ++w) sreg[c][w] = s_sc[(nb * NW + w) * kScaleRunMax + li * KB + bc];
+      }
       // The weights are decoded only after the staging barrier (an empty
       // asm that "modifies" them stops the compiler from hoisting the
       // decode, which would quadruple their register footprint).
