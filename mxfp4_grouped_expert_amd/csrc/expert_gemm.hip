@@ -57,10 +57,13 @@ __device__ __forceinline__ uint32_t word(const uint4& q, int j) {
 
 // Scale table: the E8M0 bytes of a workgroup's weight rows.  The 16 rows of
 // one (16-row block, gate/up half) are consecutive rows of the matrix, so
-// their scales are one contiguous run of 16*KB bytes; the runs are loaded
-// with byte loads in which a wave instruction reads 64 consecutive bytes
-// (one or two cache lines, where per-lane loads of each row's byte touch a
-// line per row).  ONECHUNK kernels only (K <= kChunk * 512, KB <= 96).
+// their scales are one contiguous run of 16*KB bytes: a multiple of 16
+// bytes that starts 16-byte aligned (the run starts at row index
+// (expert*rows_per_expert + half*I + block*16), and I*KB, H*KB and 16*KB are
+// multiples of 16).  Each thread fetches one 16-byte piece of some run, so a
+// wave instruction reads 1 KB of consecutive bytes, where per-lane loads of
+// each row's byte touch a cache line per row.  ONECHUNK kernels only
+// (K <= kChunk * 512, KB <= 96).
 constexpr int kScaleRunMax = kRowsPerBlock * kChunk * kBlocksPerStep;  // 1536 bytes
 
 // Row stride of the staged activations in LDS: K bf16 plus a 16-byte pad.
@@ -133,35 +136,29 @@ __global__ __launch_bounds__(256 * NBW) void expert_gemm_kernel(
   };
 
   // ONECHUNK: the workgroup's scale runs (run nb*NW + w: rows of block nb,
-  // half w), kSrun bytes per thread and run, every load issued before any
-  // wait (clamped addresses), written to LDS after the stream has landed
+  // half w; KB pieces of 16 bytes each), piece `tid` of the concatenation
+  // per thread, loaded with the weight stream and written to LDS after it
+  // has landed
   constexpr int kRuns = ONECHUNK ? NBW * NW : 1;
-  constexpr int kThreads = 256 * NBW;
-  constexpr int kSrun = (kScaleRunMax + kThreads - 1) / kThreads;
-  __shared__ unsigned char s_sc[ONECHUNK ? NBW * NW * kScaleRunMax : 1];
-  uint32_t srun[kRuns][kSrun];
-  const int runlen = kRowsPerBlock * KB;
+  static_assert(!ONECHUNK || kRuns * kChunk * kBlocksPerStep <= 256 * NBW,
+                "one scale piece per thread");
+  __shared__ __align__(16) unsigned char s_sc[ONECHUNK ? NBW * NW * kScaleRunMax : 16];
+  uint4 spiece = uint4{0u, 0u, 0u, 0u};
+  const int pr = min(tid / KB, kRuns - 1);  // this thread's run and piece
+  const int pp = tid - pr * KB;
+  const bool has_piece = tid < kRuns * KB;
   auto load_scale_runs = [&]() {
-#pragma unroll
-    for (int r = 0; r < kRuns; ++r) {
-      const int rb = r / NW, rw = r % NW;
-      const int nb0 = (blockIdx.y * NBW + rb) * kRowsPerBlock;
-      const int row0 = nb0 < N ? nb0 : 0;  // blocks past N read block 0's rows
-      const size_t grow0 = GATEUP ? (size_t)e * 2 * I + (size_t)rw * I + row0
-                                  : (size_t)e * H + row0;
-      const uint8_t* src = ws + grow0 * s_stride;
-#pragma unroll
-      for (int u = 0; u < kSrun; ++u) srun[r][u] = src[min(tid + u * kThreads, runlen - 1)];
-    }
+    const int rb = pr / NW, rw = pr % NW;
+    const int nb0 = (blockIdx.y * NBW + rb) * kRowsPerBlock;
+    const int row0 = nb0 < N ? nb0 : 0;  // blocks past N read block 0's rows
+    const size_t grow0 = GATEUP ? (size_t)e * 2 * I + (size_t)rw * I + row0
+                                : (size_t)e * H + row0;
+    const int piece = min(pp, KB - 1);  // threads past the runs repeat a piece
+    spiece = *reinterpret_cast<const uint4*>(ws + grow0 * s_stride + (size_t)piece * 16);
   };
   auto store_scale_runs = [&]() {
-#pragma unroll
-    for (int r = 0; r < kRuns; ++r)
-#pragma unroll
-      for (int u = 0; u < kSrun; ++u) {
-        const int i = tid + u * kThreads;
-        if (i < runlen) s_sc[r * kScaleRunMax + i] = (unsigned char)srun[r][u];
-      }
+    if (has_piece)
+      *reinterpret_cast<uint4*>(s_sc + pr * kScaleRunMax + pp * 16) = spiece;
   };
 
   // Per-tile row table in LDS: the element offset of each row's activations
@@ -200,16 +197,19 @@ __global__ __launch_bounds__(256 * NBW) void expert_gemm_kernel(
     load_weights(0);
     load_scale_runs();
   }
+  // Row offsets: for down they are the tile's own rows of h, and with one
+  // token every gate/up row is token 0, so neither waits for the slot ids
+  // (which queue behind the weight stream); the slot ids go to LDS once the
+  // stream has landed.
   if (tid < rows) {
     long long off;
     if (GATEUP) {
-      const int t = min(max(my_slot / k, 0), T - 1);
+      const int t = T == 1 ? 0 : min(max(my_slot / k, 0), T - 1);
       off = (long long)t * H;
     } else {
       off = (long long)(r0 + tid) * I;
     }
     s_rowoff[tid] = off;
-    s_slot[tid] = my_slot;
   }
   // LDS-only barrier: __syncthreads would also wait for the whole weight
   // stream issued above, and the activation staging below would no longer
@@ -223,6 +223,7 @@ __global__ __launch_bounds__(256 * NBW) void expert_gemm_kernel(
   stage_acts(0, min(XR, rows));
   __builtin_amdgcn_s_waitcnt(0);
   if constexpr (ONECHUNK) store_scale_runs();
+  if (tid < rows) s_slot[tid] = my_slot;
   __syncthreads();
 
   for (int pass = 0; pass < npass; ++pass) {
