@@ -212,7 +212,7 @@ def main():
     ms_per_step = start.elapsed_time(end) / steps
     us = ms_per_step * 1e3
 
-    # ---- per-kernel durations: for each entry point, a HIP graph of R
+    # ---- per-kernel durations: for each entry point, a HIP graph of max(R, 16)
     # back-to-back launches of it alone (weights rotating as in the headline
     # loop), replayed between two events on the launch stream.  The layer
     # buffers hold a valid routing and tile table from the calls above.
@@ -224,14 +224,17 @@ def main():
         "combine": lambda r: layer.combine_only(),
     }
     kernel_us = {}
-    reps = max(1, min(steps, 256) // R)
+    # at least 16 launches per graph, so one replay's fixed cost does not
+    # land on a short kernel (weights still rotate over the R copies)
+    L = max(R, 16)
+    reps = max(1, min(steps, 256) // L)
     for name, fn in parts.items():
         with torch.cuda.stream(stream):
             if graphs:
                 g = torch.cuda.CUDAGraph()
                 with torch.cuda.graph(g, stream=stream):
-                    for r in range(R):
-                        fn(r)
+                    for r in range(L):
+                        fn(r % R)
                 g.replay()
                 torch.cuda.synchronize()
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -243,11 +246,11 @@ def main():
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record(stream)
                 for _ in range(reps):
-                    for r in range(R):
-                        fn(r)
+                    for r in range(L):
+                        fn(r % R)
                 e1.record(stream)
         torch.cuda.synchronize()
-        kernel_us[name] = e0.elapsed_time(e1) * 1e3 / (reps * R)
+        kernel_us[name] = e0.elapsed_time(e1) * 1e3 / (reps * L)
 
     if args.calibrate_copy:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)

@@ -63,27 +63,30 @@ __device__ void logits_partial_body(const uint16_t* __restrict__ x,
 #pragma unroll
     for (int e = 0; e < kExpPerWave; ++e) acc[t][e] = 0.0;
 
+  // The wave's 4x4 router weights of a K step stay in registers while each
+  // token's 4 activations stream past (each accumulator sees the same FMA
+  // sequence whatever TPW is).
   for (int kk = kbeg + 4 * lane; kk < kend; kk += 4 * kWave) {
-    double xv[TPW][4];
-#pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-      const uint2 v = *reinterpret_cast<const uint2*>(xr[t] + kk);
-      xv[t][0] = (double)bf16_to_float(v.x & 0xffffu);
-      xv[t][1] = (double)bf16_to_float(v.x >> 16);
-      xv[t][2] = (double)bf16_to_float(v.y & 0xffffu);
-      xv[t][3] = (double)bf16_to_float(v.y >> 16);
-    }
+    double wv[kExpPerWave][4];
 #pragma unroll
     for (int e = 0; e < kExpPerWave; ++e) {
       const float4 w = *reinterpret_cast<const float4*>(wr[e] + kk);
-      const double w0 = w.x, w1 = w.y, w2 = w.z, w3 = w.w;
+      wv[e][0] = w.x; wv[e][1] = w.y; wv[e][2] = w.z; wv[e][3] = w.w;
+    }
 #pragma unroll
-      for (int t = 0; t < TPW; ++t) {
+    for (int t = 0; t < TPW; ++t) {
+      const uint2 v = *reinterpret_cast<const uint2*>(xr[t] + kk);
+      const double x0 = (double)bf16_to_float(v.x & 0xffffu);
+      const double x1 = (double)bf16_to_float(v.x >> 16);
+      const double x2 = (double)bf16_to_float(v.y & 0xffffu);
+      const double x3 = (double)bf16_to_float(v.y >> 16);
+#pragma unroll
+      for (int e = 0; e < kExpPerWave; ++e) {
         double a = acc[t][e];
-        a = fma(xv[t][0], w0, a);
-        a = fma(xv[t][1], w1, a);
-        a = fma(xv[t][2], w2, a);
-        a = fma(xv[t][3], w3, a);
+        a = fma(x0, wv[e][0], a);
+        a = fma(x1, wv[e][1], a);
+        a = fma(x2, wv[e][2], a);
+        a = fma(x3, wv[e][3], a);
         acc[t][e] = a;
       }
     }
@@ -107,11 +110,12 @@ __device__ void logits_partial_body(const uint16_t* __restrict__ x,
   }
 }
 
+template <int TPW>
 __global__ __launch_bounds__(256) void router_logits_partial(
     const uint16_t* __restrict__ x, const float* __restrict__ w_router, int T, int H, int E,
     int split_len, double* __restrict__ partial) {
-  logits_partial_body<false>(x, w_router, T, H, E, split_len, partial, blockIdx.x, blockIdx.y,
-                             blockIdx.z);
+  logits_partial_body<false, TPW>(x, w_router, T, H, E, split_len, partial, blockIdx.x,
+                                  blockIdx.y, blockIdx.z);
 }
 
 // Total order on doubles as int64 (larger key = larger value); -0 is folded
@@ -371,8 +375,8 @@ void launch_router_logits(const uint16_t* x, const float* w_router, int T, int H
                           const RouterPlan& plan, double* partial, hipStream_t stream) {
   dim3 grid((T + kTokPerWave - 1) / kTokPerWave, (E + kExpPerBlock - 1) / kExpPerBlock,
             plan.splits);
-  hipLaunchKernelGGL(router_logits_partial, grid, dim3(256), 0, stream, x, w_router, T, H, E,
-                     plan.split_len, partial);
+  hipLaunchKernelGGL(router_logits_partial<kTokPerWave>, grid, dim3(256), 0, stream, x,
+                     w_router, T, H, E, plan.split_len, partial);
 }
 
 bool router_fused_ok(int T, int E, int k) {

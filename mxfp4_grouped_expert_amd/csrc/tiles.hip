@@ -1,5 +1,6 @@
 // Per-expert routing tile table as its own launch (any T): one workgroup of
-// 1024 threads runs the block-level builder of tiles_block.h over topk_ids.
+// 1024 threads runs a builder of tiles_block.h over topk_ids (the all-pairs
+// one for a few slots, the chunked one otherwise).
 #include "moe_device.h"
 #include "moe_launch.h"
 #include "tiles_block.h"
@@ -9,14 +10,26 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 1024;
+// The all-pairs builder costs O(N) dependent LDS reads per thread; above
+// this many slots the chunked builder is faster (measured at 256 slots:
+// 4 us against 13 us).
+constexpr int kSmallN = 128;
 
 __global__ __launch_bounds__(kThreads) void build_tiles_kernel(
     const int32_t* __restrict__ topk_ids, int N, int E, int BM,
     int32_t* __restrict__ expert_offsets, int32_t* __restrict__ sorted_ids,
     int32_t* __restrict__ tiles, int32_t* __restrict__ num_tiles) {
   __shared__ TilesScratch<kThreads> S;
-  build_tiles_block<kThreads>(topk_ids, N, E, BM, S, expert_offsets, sorted_ids, tiles,
-                              num_tiles);
+  __shared__ int s_ids[kSmallN];
+  if (N <= kSmallN) {  // uniform: few slots, all-pairs form
+    if (threadIdx.x < N) s_ids[threadIdx.x] = topk_ids[threadIdx.x];
+    lds_barrier();
+    build_tiles_small<kThreads>(static_cast<const int*>(s_ids), N, E, BM, S, expert_offsets,
+                                sorted_ids, tiles, num_tiles);
+  } else {
+    build_tiles_block<kThreads>(topk_ids, N, E, BM, S, expert_offsets, sorted_ids, tiles,
+                                num_tiles);
+  }
 }
 
 }  // namespace
