@@ -10,18 +10,20 @@
 //
 // Unit of work: one workgroup of 8 waves takes a tile of up to 128 token
 // rows of one expert and 384 weight rows (4 slices of 96).  Waves w and w+4
-// (the two waves of one SIMD) share slice w & 3 and take three of its six
-// 16-row weight fragments each, against all of the tile's token fragments
-// (16 rows each, as many as the tile has rows): every weight is decoded by
-// one wave only, and while one wave of a SIMD waits (on LDS, a barrier or its
-// decoding) the other keeps the matrix core busy.
+// (the two waves of one SIMD) share slice w & 3: each decodes all six 16-row
+// weight fragments of the slice and multiplies them against its own half of
+// the tile's token fragments (16 rows each; the first ceil(n/2) of the n
+// fragments go to the wave with mg = 0).  The two waves of a SIMD run
+// ping-pong: while one issues the MFMAs of a stage the other reads and
+// decodes its operands of the next one, and the roles swap at every
+// workgroup barrier.
 //   gate/up: a fragment holds 8 output columns, gate and up rows interleaved
 //     (even row: gate, odd row: up, of the same column), so a lane and its
 //     neighbour hold the two halves of SwiGLU; 192 output columns per unit.
 //   down: a fragment is 16 rows of w2; 384 output columns per unit.
 //
-// K loop: 64 K per stage (two MX blocks), four stages in LDS, all of them in
-// flight.  MFMA 16x16x32: lane group g supplies K elements
+// K loop: 64 K per stage (two MX blocks), four stage buffers in LDS: the
+// stage being read and the next three in flight.  MFMA 16x16x32: lane group g supplies K elements
 // 32*(g>>1) + 16*(g&1) + 8j .. +8 of the stage for step j = 0, 1 (any K order
 // works as long as both operands use it), so a lane's weight operand is one
 // 8-byte half of one MX block and its scale is one byte.  All loads in the
@@ -36,8 +38,8 @@
 //     block ^ ((r >> 3) & 1) (conflict-free 64-bit reads).
 // The E8M0 scales of the unit's rows (contiguous runs of the scale matrix)
 // are loaded once, as raw 16-byte pieces, into an LDS slab.  Weights are
-// decoded to bf16 in registers (v_cvt_scalef32_pk_bf16_fp4) right before
-// their MFMAs.
+// decoded to bf16 in registers (v_cvt_scalef32_pk_bf16_fp4) in the load
+// phase before their MFMAs.
 //
 // Grid: one workgroup per (tile, column block) unit, 1-D.  Workgroup w runs
 // on XCD w % 8; units are renumbered so that each XCD takes a contiguous
@@ -64,13 +66,13 @@ constexpr int kMaxKB = 96;                         // K <= 3072
 constexpr int kSlabUnits = 5;                      // of kThreads pieces of 16 B
 constexpr int kSlabBytes = kSlabUnits * kThreads * 16;  // 40 KB of raw scale bytes
 constexpr int kLdsBytes = kStages * kStage + kSlabBytes + kMT * 8 + kMT * 4;
-constexpr int kNFW = 3;                            // weight fragments per wave
+constexpr int kNFW = 6;                            // weight fragments per wave
 constexpr int kColsGateUp = 48;                    // output columns per slice
 constexpr int kColsDown = 96;
 
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 static_assert(kWLoadsSlice == 3, "slice loads split 2 + 1 between the two waves of a SIMD");
-static_assert(2 * kNFW * 16 == kWRowsSlice, "two waves of three fragments per slice");
+static_assert(kNFW * 16 == kWRowsSlice, "one wave decodes a whole slice");
 // slab pieces: gate/up two runs of 192 rows, down one run of 384 rows
 static_assert(2 * ((15 + 4 * kColsGateUp * kMaxKB + 15) / 16) <= kSlabUnits * kThreads, "slab");
 static_assert((15 + 4 * kColsDown * kMaxKB + 15) / 16 <= kSlabUnits * kThreads, "slab size");
@@ -154,33 +156,39 @@ __device__ __forceinline__ void issue_w(const UnitCtx& c, int it, int st) {
 
 __device__ __forceinline__ void lds_wait_all() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-// K loop and epilogue of one wave: its kNFW weight fragments (3*mg .. +2 of
-// slice wn) against NM token fragments, XCW activation loads per wave and
-// stage (1: rows 0..63 of the tile, 2: rows 0..127).  NM and XCW are
-// compile-time constants so the loop body is straight-line code.
+// K loop and epilogue of one wave: all kNFW weight fragments of slice wn
+// against NMW token fragments of the tile's half mg (rows 64*mg + 16*i ..),
+// with XCW activation loads per wave and stage (1: rows 0..63 of the tile,
+// 2: rows 0..127).  NMW (0..4) and XCW are compile-time constants so the
+// loop body is straight-line code; a wave with NMW = 0 only loads and syncs.
 //
 // Software pipeline, per iteration it (stage it in buffer it % 4):
-//   step 0: read the step-1 activation operands of stage it; dequantize the
-//           weights of step 0 and run its MFMAs;
-//   sync:   stage it is fully read (lgkmcnt 0) and stage it+1 has landed
-//           (vmcnt): barrier;
-//   step 1: refill buffer it % 4 with stage it+4; read the step-0 operands
-//           and the weights of stage it+1; dequantize and run the MFMAs of
-//           step 1.
-// LDS reads of the next step are in flight under the MFMAs of the current
-// one, and one barrier per iteration both publishes a stage and frees a
-// buffer.  Scheduling fences keep MFMAs from drifting across the sync.
-template <bool GATEUP, int NM, int XCW>
-__device__ __forceinline__ void unit_main(const UnitCtx& c) {
+//   region 1: read the step-1 activation operands of stage it; MFMAs of
+//             step 0 (operands already in registers);
+//   sync:     stage it is fully read (lgkmcnt 0) and stage it+1 has landed
+//             (vmcnt): barrier;
+//   region 2: refill buffer it % 4 with stage it+4; read the weights, scale
+//             bytes and step-0 activation operands of stage it+1; MFMAs of
+//             step 1; decode both steps' weights of stage it+1 to bf16.
+// The MFMAs of a region never wait for the LDS reads issued in it, and one
+// barrier per iteration both publishes a stage and frees a buffer.
+// Scheduling fences keep instructions from drifting across the sync.
+template <bool GATEUP, int NMW, int XCW>
+__device__ __forceinline__ void unit_main(const UnitCtx& c, int mrow0) {
   constexpr int NF = kNFW;
+  constexpr int NA = NMW > 0 ? NMW : 1;  // array extent
   const int li = c.lane & 15;
   const int grp = c.lane >> 4;
   const int half = grp >> 1;  // MX block of the stage this lane feeds
   const int sub = grp & 1;    // which 8-byte half of it
   const int ww = 2 - c.mg;    // weight loads of this wave per stage
   const int niters = c.niters;
-  // loads per stage of this wave; stages 0..3 had their weights in the prologue
-  auto loads = [&](int s) { return s >= niters ? 0 : (s <= 3 ? XCW : XCW + ww); };
+  // loads per stage of this wave: stages 0..2 are issued before the loop
+  // (their weights, and stage 3's, came with the prologue); stage s >= 3 is
+  // issued in iteration s - 3 with its weights.  Stages past the last one are
+  // loaded too (clamped, in-bounds addresses, into a buffer that is not read
+  // again), so the loop issues a fixed number of loads per iteration.
+  auto loads = [&](int s) { return s <= 2 ? XCW : XCW + ww; };
 
   // this lane's source rows of the activation loads (load t covers rows
   // 8L .. 8L+7, L = 8t + wave, the lane's row being 8L + (lane >> 3)); its
@@ -198,119 +206,175 @@ __device__ __forceinline__ void unit_main(const UnitCtx& c) {
     for (int t = 0; t < XCW; ++t) lds_load16(xsrc[t] + kel, xs + (8 * t + c.wave) * 1024);
   };
 
-  // LDS operand reads
-  auto read_a = [&](const unsigned char* xs, int j, bf16x8 (&a)[NM]) {
+  // activation operands of step j of a stage
+  auto read_a = [&](const unsigned char* xs, int j, bf16x8 (&a)[NA]) {
 #pragma unroll
-    for (int i = 0; i < NM; ++i) {
-      const int r = 16 * i + li;
+    for (int i = 0; i < NMW; ++i) {
+      const int r = mrow0 + 16 * i + li;
       a[i] = as_bf16x8(*reinterpret_cast<const uint4*>(
           xs + r * 128 + 16 * ((2 * grp + j) ^ ((r >> 1) & 7))));
     }
   };
-  auto read_w = [&](const unsigned char* xs, int it, uint2 (&wr)[NF], float (&sc)[NF]) {
+  // weights (8-byte halves of MX blocks) and raw E8M0 bytes of stage `it`
+  auto read_w = [&](const unsigned char* xs, int it, uint2 (&wr)[NF], uint32_t (&sr)[NF]) {
     const unsigned char* wsb = xs + kXStage + c.wn * kWSlice;
     const int blk = 2 * it + half;
-    const uint32_t vmask = blk < c.KB ? ~0u : 0u;  // a missing last block scales to 0
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
-      const int rl = 16 * (NF * c.mg + f) + li;  // staged row within the slice
+      const int rl = 16 * f + li;  // staged row within the slice
       wr[f] = *reinterpret_cast<const uint2*>(wsb + rl * 32 + 16 * (half ^ ((rl >> 3) & 1)) +
                                               8 * sub);
-      const uint32_t sbits = __float_as_uint(e8m0_to_float(c.slab[c.soff[f] + blk]));
-      sc[f] = __uint_as_float(sbits & vmask);
+      sr[f] = c.slab[c.soff[f] + blk];
     }
   };
-
-  floatx4 acc[NM][NF];
+  // E8M0 bytes -> float scales of stage `it`; a missing last MX block (odd
+  // K / 32) scales to 0
+  auto scales = [&](int it, const uint32_t (&sr)[NF], float (&sc)[NF]) {
+    const uint32_t vmask = 2 * it + half < c.KB ? ~0u : 0u;
 #pragma unroll
-  for (int i = 0; i < NM; ++i)
+    for (int f = 0; f < NF; ++f) sc[f] = __uint_as_float(__float_as_uint(e8m0_to_float(sr[f])) & vmask);
+  };
+  // bf16 weight operands of step j
+  auto decode = [&](int j, const uint2 (&wr)[NF], const float (&sc)[NF], bf16x8 (&b)[NF]) {
+#pragma unroll
+    for (int f = 0; f < NF; ++f) b[f] = dequant8_bf16(j ? wr[f].y : wr[f].x, sc[f]);
+  };
+
+  floatx4 acc[NA][NF];
+#pragma unroll
+  for (int i = 0; i < NA; ++i)
 #pragma unroll
     for (int f = 0; f < NF; ++f) acc[i][f] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  auto step = [&](const bf16x8 (&a)[NM], const uint2 (&wr)[NF], const float (&sc)[NF], int j) {
-    bf16x8 b[NF];
+  // MFMAs of weight fragments f0 .. f1-1 against the wave's token fragments
+  auto mfmas = [&](const bf16x8 (&a)[NA], const bf16x8 (&b)[NF], int f0, int f1) {
 #pragma unroll
-    for (int f = 0; f < NF; ++f) b[f] = dequant8_bf16(j ? wr[f].y : wr[f].x, sc[f]);
+    for (int f = f0; f < f1; ++f)
 #pragma unroll
-    for (int f = 0; f < NF; ++f)
-#pragma unroll
-      for (int i = 0; i < NM; ++i) acc[i][f] = mfma16x16x32(a[i], b[f], acc[i][f]);
+      for (int i = 0; i < NMW; ++i) acc[i][f] = mfma16x16x32(a[i], b[f], acc[i][f]);
   };
 
-  // stages 0..3 in flight (their weights were loaded in the prologue)
-  for (int s = 0; s < 4 && s < niters; ++s) issue_x(s, s);
-  wait_vm(loads(1) + loads(2) + loads(3));
-  wg_barrier();  // stage 0 landed
-
-  bf16x8 a0[NM], a1[NM];
-  uint2 wcur[NF];
-  float scur[NF];
-  read_a(c.smem, 0, a0);
-  read_w(c.smem, 0, wcur, scur);
-
-  for (int it = 0; it < niters; ++it) {
-    const unsigned char* xs = c.smem + (it & (kStages - 1)) * kStage;
-    read_a(xs, 1, a1);
-    step(a0, wcur, scur, 0);
-    __builtin_amdgcn_sched_barrier(0);
-
-    lds_wait_all();  // this wave is done reading stage it
-    // its share of stage it+1 landed: only stages it+2, it+3 may be pending
-    if (it >= 2 && it + 3 < niters) {
-      if (c.mg == 0)
-        vm_wait<2 * (XCW + 2)>();
-      else
-        vm_wait<2 * (XCW + 1)>();
-    } else {
-      wait_vm(loads(it + 2) + loads(it + 3));
+  // Ping-pong between the two waves of a SIMD.  Phases are separated by
+  // workgroup barriers; in every phase one group of waves (one wave per
+  // SIMD) runs MFMAs while the other reads and decodes the operands of its
+  // next stage, so each SIMD's matrix core and its VALU/LDS work overlap
+  // without relying on the two waves drifting apart.  Group 0 (mg = 0)
+  // loads stage it in phase 2it and multiplies it in phase 2it+1; group 1
+  // runs half a stage behind (load in 2it+1, multiply in 2it+2).
+  bf16x8 a[2][NA], b[2][NF];
+  // load phase: all operands of stage `it`, decoded, in registers
+  auto load_phase = [&](int it) {
+    if (NMW > 0) {
+      const unsigned char* xs = c.smem + (it & (kStages - 1)) * kStage;
+      uint2 wr[NF];
+      uint32_t sr[NF];
+      float sc[NF];
+      read_w(xs, it, wr, sr);
+      read_a(xs, 0, a[0]);
+      read_a(xs, 1, a[1]);
+      scales(it, sr, sc);
+      decode(0, wr, sc, b[0]);
+      decode(1, wr, sc, b[1]);
+      lds_wait_all();  // the stage may be refilled two phases on
+      // the decoded operands are complete here, not sunk into the MFMA phase
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int f = 0; f < NF; ++f) asm volatile("" : "+v"(b[j][f]));
     }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // MFMA phase: stage `it`; this wave also issues its share of stage it+3,
+  // into the buffer of stage it-1 (read by both groups before the previous
+  // barrier)
+  auto mfma_phase = [&](int it) {
+    const int st = (it + 3) & (kStages - 1);
+    issue_x(it + 3, st);
+    issue_w(c, it + 3, st);
+    if (NMW > 0) {
+      __builtin_amdgcn_s_setprio(1);
+      mfmas(a[0], b[0], 0, NF);
+      mfmas(a[1], b[1], 0, NF);
+      __builtin_amdgcn_s_setprio(0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto barrier = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
     wg_barrier();
     __builtin_amdgcn_sched_barrier(0);
+  };
 
-    if (it + 4 < niters) {
-      const int st = it & (kStages - 1);
-      issue_x(it + 4, st);
-      issue_w(c, it + 4, st);
+  // stages 0..2 in flight; every wave's share of stage 0 lands before the
+  // first barrier.  Before phase 2s (group 0 reads stage s) every wave's
+  // share of stage s has landed: group 0 then has stages s+1, s+2 pending
+  // at most, group 1 (which issued up to stage s+1) stage s+1.
+  for (int s = 0; s < 3; ++s) issue_x(s, s);
+  wait_vm(loads(1) + loads(2));
+  barrier();
+  if (c.mg == 0) {
+    for (int it = 0; it < niters; ++it) {
+      load_phase(it);                       // phase 2it
+      barrier();
+      mfma_phase(it);                       // phase 2it+1
+      wait_vm(loads(it + 2) + loads(it + 3));
+      barrier();
     }
-    // operands of stage it+1 (a stale buffer on the last iteration: unused)
-    const unsigned char* xn = c.smem + ((it + 1) & (kStages - 1)) * kStage;
-    uint2 wnext[NF];
-    float snext[NF];
-    read_a(xn, 0, a0);
-    read_w(xn, it + 1, wnext, snext);
-
-    step(a1, wcur, scur, 1);
-#pragma unroll
-    for (int f = 0; f < NF; ++f) { wcur[f] = wnext[f]; scur[f] = snext[f]; }
-    __builtin_amdgcn_sched_barrier(0);
+    // phase 2*niters: group 1's last MFMA phase
+  } else {
+    barrier();                              // phase 0: group 0's first load
+    for (int it = 0; it < niters; ++it) {
+      load_phase(it);                       // phase 2it+1
+      wait_vm(loads(it + 2));
+      barrier();
+      mfma_phase(it);                       // phase 2it+2
+      if (it + 1 < niters) barrier();
+    }
   }
+  vm_wait<0>();  // the loads past the last stage
 
   // epilogue straight from the accumulators: the lane holds D[4*grp + r][li]
   // of each (token fragment, weight fragment)
   const int cbase = c.n0 + (GATEUP ? kColsGateUp : kColsDown) * c.wn;
+  if (GATEUP) {
+    // A lane pair (even: gate, odd: up, of column cbase + 8*f + li/2) swaps
+    // half of its rows, so that the even lane finishes rows 0, 1 of its four
+    // and the odd lane rows 2, 3: each SwiGLU is evaluated once.
+    const bool odd = li & 1;
+    const int col0 = cbase + (li >> 1);
 #pragma unroll
-  for (int i = 0; i < NM; ++i) {
+    for (int i = 0; i < NMW; ++i) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = 16 * i + 4 * grp + r;
-      if (GATEUP) {
-        // even lane: gate, odd lane: up, of column cbase + 8*(3*mg + f) + li/2
-#pragma unroll
-        for (int f = 0; f < NF; ++f) {
-          const float v = acc[i][f][r];
-          const float up = __shfl_xor(v, 1);
-          const int col = cbase + 8 * (NF * c.mg + f) + (li >> 1);
-          if (row < c.rows && (li & 1) == 0 && col < c.N)
-            reinterpret_cast<uint16_t*>(c.out)[(size_t)(c.r0 + row) * c.I + col] =
-                float_to_bf16(silu(v) * up);
+      for (int f = 0; f < NF; ++f) {
+        const floatx4 v = acc[i][f];
+        const float send0 = odd ? v[0] : v[2];
+        const float send1 = odd ? v[1] : v[3];
+        const float got0 = swap_pair(send0);
+        const float got1 = swap_pair(send1);
+        // (gate, up) of rows q = 0, 1 (even lane) or q = 2, 3 (odd lane)
+        const float g0 = odd ? got0 : v[0], u0 = odd ? v[2] : got0;
+        const float g1 = odd ? got1 : v[1], u1 = odd ? v[3] : got1;
+        const int row = mrow0 + 16 * i + 4 * grp + (odd ? 2 : 0);
+        const int col = col0 + 8 * f;
+        uint16_t* o = reinterpret_cast<uint16_t*>(c.out) + (size_t)(c.r0 + row) * c.I + col;
+        if (col < c.N) {
+          if (row < c.rows) o[0] = float_to_bf16(silu_fast(g0) * u0);
+          if (row + 1 < c.rows) o[c.I] = float_to_bf16(silu_fast(g1) * u1);
         }
-      } else {
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NMW; ++i) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = mrow0 + 16 * i + 4 * grp + r;
         if (row >= c.rows) continue;
         const long long p = c.s_slot[row];
         if (p < 0 || p >= c.nslots) continue;
 #pragma unroll
         for (int f = 0; f < NF; ++f) {
-          const int col = cbase + 16 * (NF * c.mg + f) + li;
+          const int col = cbase + 16 * f + li;
           if (col < c.N) reinterpret_cast<float*>(c.out)[(size_t)p * c.H + col] = acc[i][f][r];
         }
       }
@@ -461,20 +525,28 @@ __global__ __launch_bounds__(kThreads, 1) void expert_mma_kernel(
 #pragma unroll
   for (int f = 0; f < kNFW; ++f) {
     int ch, rr;
-    slice_row(c.wn, 16 * (kNFW * c.mg + f) + li, ch, rr);
+    slice_row(c.wn, 16 * f + li, ch, rr);
     c.soff[f] = pbase[ch] * 16 + skip[ch] + rr * KB;
   }
 
-  // token fragments of the tile (all waves take all of them)
-  switch ((rows + 15) >> 4) {
-    case 8: unit_main<GATEUP, 8, 2>(c); break;
-    case 7: unit_main<GATEUP, 7, 2>(c); break;
-    case 6: unit_main<GATEUP, 6, 2>(c); break;
-    case 5: unit_main<GATEUP, 5, 2>(c); break;
-    case 4: unit_main<GATEUP, 4, 1>(c); break;
-    case 3: unit_main<GATEUP, 3, 1>(c); break;
-    case 2: unit_main<GATEUP, 2, 1>(c); break;
-    default: unit_main<GATEUP, 1, 1>(c); break;
+  // token fragments: the first ceil(nm/2) go to the waves with mg = 0, the
+  // rest to those with mg = 1
+  const int nm = (rows + 15) >> 4;
+  const int nm0 = (nm + 1) >> 1;
+  const int mine = c.mg ? nm - nm0 : nm0;  // wave-uniform
+  const int mrow0 = c.mg ? 16 * nm0 : 0;
+  if (nm > 4) {
+    switch (mine) {
+      case 4: unit_main<GATEUP, 4, 2>(c, mrow0); break;
+      case 3: unit_main<GATEUP, 3, 2>(c, mrow0); break;
+      default: unit_main<GATEUP, 2, 2>(c, mrow0); break;
+    }
+  } else {
+    switch (mine) {
+      case 2: unit_main<GATEUP, 2, 1>(c, mrow0); break;
+      case 1: unit_main<GATEUP, 1, 1>(c, mrow0); break;
+      default: unit_main<GATEUP, 0, 1>(c, mrow0); break;
+    }
   }
 }
 

@@ -63,6 +63,19 @@ __device__ __forceinline__ floatx4 mfma16x16x32(bf16x8 a, bf16x8 b, floatx4 c) {
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
+// silu with the hardware exp2 and reciprocal (about 1 ulp each, far below
+// the bf16 rounding of the result): z * 1 / (1 + 2^(-z * log2 e)).  Large
+// negative z gives 1 / inf = 0, large positive z gives z.
+__device__ __forceinline__ float silu_fast(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * 1.4426950408889634f));
+}
+
+// Value of the other lane of an even/odd lane pair (quad permutation 1,0,3,2
+// through DPP, no LDS traffic).
+__device__ __forceinline__ float swap_pair(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
+}
+
 // Workgroup barrier for phases that exchange data through LDS only: waits
 // for this wave's LDS operations, not for its global stores (__syncthreads
 // also waits for every outstanding global access, i.e. for store
