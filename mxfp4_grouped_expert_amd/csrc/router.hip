@@ -15,7 +15,9 @@
 //      router loads, coalesced across lanes), and a butterfly reduction
 //      leaves one partial sum per (K-range, token, expert).  Splitting K
 //      spreads the router matrix over many CUs when T is small (decode), so
-//      it streams at HBM speed instead of one CU's.
+//      it streams at HBM speed instead of one CU's.  With many tokens
+//      (prefill) router_logits_mfma computes whole logits on the fp64 matrix
+//      cores instead.
 //   2. router_topk_softmax: one wave per token sums the K-range partials in
 //      a fixed order (deterministic), adds the bias, and runs k rounds of a
 //      wave-wide argmax on a total order (higher logit first, then lower
@@ -116,6 +118,98 @@ __global__ __launch_bounds__(256) void router_logits_partial(
     int split_len, double* __restrict__ partial) {
   logits_partial_body<false, TPW>(x, w_router, T, H, E, split_len, partial, blockIdx.x,
                                   blockIdx.y, blockIdx.z);
+}
+
+// Logits of many tokens on the fp64 matrix cores (v_mfma_f64_16x16x4_f64).
+// A workgroup of 8 waves (two per SIMD) takes 16 tokens and up to
+// kMfmaExperts experts (8 tiles of 16), and its waves split K: wave w takes
+// the 16-element groups g = w, w+8, ... .  Within a group, lane (r = l % 16, q = l / 16)
+// loads elements 16g + 4q .. +3 of token row r (8 bytes of bf16) and of
+// expert row r of each tile (16 bytes of fp32), and MFMA step s (0..3) takes
+// element s of each: step s sums over q, so the four steps together cover
+// the group.  Operands are converted to fp64 exactly (bf16 and fp32 both
+// embed in fp64) and accumulated in fp64.  The eight waves' sums meet in LDS
+// and are added in wave order, so the result does not depend on timing.
+constexpr int kMfmaExperts = 128;
+constexpr int kMfmaTiles = kMfmaExperts / 16;
+constexpr int kMfmaWaves = 8;
+typedef double doublex4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(64 * kMfmaWaves) void router_logits_mfma(
+    const uint16_t* __restrict__ x, const float* __restrict__ w_router, int T, int H, int E,
+    double* __restrict__ logits) {
+  __shared__ double red[kMfmaWaves][16][kMfmaExperts + 1];
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 15;
+  const int q = lane >> 4;
+  const int t0 = blockIdx.x * 16;
+  const int nt = (E + 15) >> 4;  // expert tiles holding real experts
+
+  const uint16_t* xr = x + (size_t)min(t0 + r, T - 1) * H + 4 * q;
+  const float* wr[kMfmaTiles];
+#pragma unroll
+  for (int n = 0; n < kMfmaTiles; ++n)
+    wr[n] = w_router + (size_t)min(16 * n + r, E - 1) * H + 4 * q;
+
+  doublex4 acc[kMfmaTiles];
+#pragma unroll
+  for (int n = 0; n < kMfmaTiles; ++n) acc[n] = doublex4{0.0, 0.0, 0.0, 0.0};
+
+  // group g+8's loads are in flight while group g is multiplied (the index
+  // is clamped, so the load past the last group reads a valid one)
+  const int ng = H / 16;
+  auto load = [&](int g, uint2& xv, float4 (&w)[kMfmaTiles]) {
+    g = min(g, ng - 1);
+    xv = *reinterpret_cast<const uint2*>(xr + 16 * g);
+    // all tiles, branch-free (tiles past E read clamped rows; their sums
+    // are not stored)
+#pragma unroll
+    for (int n = 0; n < kMfmaTiles; ++n) w[n] = *reinterpret_cast<const float4*>(wr[n] + 16 * g);
+  };
+  uint2 xv;
+  float4 w[kMfmaTiles];
+  load(wave, xv, w);
+  for (int g = wave; g < ng; g += kMfmaWaves) {
+    uint2 xn;
+    float4 wn[kMfmaTiles];
+    load(g + kMfmaWaves, xn, wn);
+    double a[4];
+    a[0] = (double)bf16_to_float(xv.x & 0xffffu);
+    a[1] = (double)bf16_to_float(xv.x >> 16);
+    a[2] = (double)bf16_to_float(xv.y & 0xffffu);
+    a[3] = (double)bf16_to_float(xv.y >> 16);
+    // step-major order: consecutive MFMAs go to different accumulators, so
+    // none waits for the previous one's result
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+#pragma unroll
+      for (int n = 0; n < kMfmaTiles; ++n) {
+        const float wv = st == 0 ? w[n].x : st == 1 ? w[n].y : st == 2 ? w[n].z : w[n].w;
+        acc[n] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[st], (double)wv, acc[n], 0, 0, 0);
+      }
+    xv = xn;
+#pragma unroll
+    for (int n = 0; n < kMfmaTiles; ++n) w[n] = wn[n];
+  }
+
+  // The fp64 MFMA leaves D[q + 4i][r] of tile n in register i of lane
+  // (r, q): token t0 + q + 4i, expert 16n + r.
+#pragma unroll
+  for (int n = 0; n < kMfmaTiles; ++n)
+    if (n < nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[wave][q + 4 * i][16 * n + r] = acc[n][i];
+  __syncthreads();
+  for (int o = threadIdx.x; o < 16 * E; o += 64 * kMfmaWaves) {
+    const int tt = o / E, e = o - tt * E;
+    if (t0 + tt < T) {
+      double v = red[0][tt][e];
+#pragma unroll
+      for (int ww = 1; ww < kMfmaWaves; ++ww) v += red[ww][tt][e];
+      logits[(size_t)(t0 + tt) * E + e] = v;
+    }
+  }
 }
 
 // Total order on doubles as int64 (larger key = larger value); -0 is folded
@@ -349,6 +443,12 @@ __global__ __launch_bounds__(kFusedThreads) void router_decode_fused(
 
 }  // namespace
 
+// Many tokens (enough 16-token workgroups to fill the chip), at most
+// kMfmaExperts experts, K a multiple of 16.
+bool router_mfma_ok(int T, int H, int E) {
+  return T >= 1024 && E <= kMfmaExperts && H % 16 == 0;
+}
+
 RouterPlan router_plan(int T, int H, int E) {
   const long long tb = (T + kTokPerWave - 1) / kTokPerWave;
   const long long eb = (E + kExpPerBlock - 1) / kExpPerBlock;
@@ -373,6 +473,11 @@ size_t router_partial_bytes(int T, int H, int E) {
 
 void launch_router_logits(const uint16_t* x, const float* w_router, int T, int H, int E,
                           const RouterPlan& plan, double* partial, hipStream_t stream) {
+  if (router_mfma_ok(T, H, E) && plan.splits == 1) {
+    hipLaunchKernelGGL(router_logits_mfma, dim3((T + 15) / 16), dim3(64 * kMfmaWaves), 0, stream,
+                       x, w_router, T, H, E, partial);
+    return;
+  }
   dim3 grid((T + kTokPerWave - 1) / kTokPerWave, (E + kExpPerBlock - 1) / kExpPerBlock,
             plan.splits);
   hipLaunchKernelGGL(router_logits_partial<kTokPerWave>, grid, dim3(256), 0, stream, x,

@@ -109,6 +109,27 @@ def test_random_shapes(case):
     check_all(inp, BM)
 
 
+# Many tokens: router logits on the fp64 matrix cores (16-token workgroups,
+# up to 128 experts).  A ragged last token block, an expert count that is not
+# a multiple of 16, and the full 2880-wide hidden size.
+ROUTER_MANY_CASES = [
+    # T, H, E, k
+    (1029, 2880, 128, 4),
+    (1040, 160, 72, 4),
+    (2048, 64, 5, 2),
+]
+
+
+@pytest.mark.parametrize("case", ROUTER_MANY_CASES, ids=lambda c: "T{}_H{}_E{}".format(*c[:3]))
+def test_router_many_tokens_match_oracle(case):
+    T, H, E, k = case
+    inp = make_random(T=T, H=H, E=E, k=k, I=32, seed=T + E, router_std=0.3)
+    inp["name"] = "router_many_T{}_E{}".format(T, E)
+    res = check_all(inp, 128, tokens=np.arange(0, T, 97))
+    ref = oracle.router_logits(inp["x"], inp["w_router"], None)
+    np.testing.assert_allclose(res["gpu"]["logits"], ref, rtol=1e-13, atol=1e-12)
+
+
 def test_wide_scale_range():
     T, H, E, k, I = 9, 192, 4, 2, 96
     inp = make_random(T=T, H=H, E=E, k=k, I=I, seed=5, router_std=0.3)
