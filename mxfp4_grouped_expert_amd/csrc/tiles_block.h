@@ -6,15 +6,15 @@
 // expert write its own tiles instead of the expert GEMM searching a
 // tiles x experts grid.  One workgroup of NT threads does it in LDS, with no
 // order-dependent atomics, so the result is bit-exact and deterministic:
-//   1. count slots per expert (LDS integer adds: totals do not depend on
-//      order); ids outside [0, E) go to a trash bucket E;
-//   2. exclusive scans of the counts (row offsets) and of ceil(count/BM)
-//      (tile offsets), one wave each;
-//   3. stable scatter in chunks of NT slots: within a wave, lanes with the
-//      same expert find each other with nine ballots (one per bit of the
-//      bucket index) and rank themselves with mbcnt; per-wave counts give
-//      each wave's base; a running count per expert carries across chunks,
-//      so slot order inside an expert is ascending;
+//   1. each wave counts the slots of its own contiguous range per expert
+//      (LDS integer adds: totals do not depend on order); ids outside
+//      [0, E) go to a trash bucket E;
+//   2. exclusive scans of the counts (row offsets, and per expert over the
+//      waves in order) and of ceil(count/BM) (tile offsets);
+//   3. stable scatter: each wave walks its range in rounds of 64 slots;
+//      lanes with the same expert find each other with nine ballots (one
+//      per bit of the bucket index) and rank themselves with mbcnt, after
+//      the wave's own running position in that expert;
 //   4. each tile index finds its expert by binary search over the tile
 //      offsets and writes (expert, row_start, rows).
 #pragma once
@@ -64,6 +64,14 @@ __device__ inline void wave_exclusive_scan(const int* in, int* out, int n, int l
 // Builds the table from ids[0..N) (any address space).  Every thread of the
 // NT-thread workgroup must call it; it ends with a barrier.  Phases exchange
 // data through LDS only, so the barriers do not wait for global stores.
+//
+// Wave w owns the contiguous slot range [w*L, (w+1)*L): it counts its slots
+// per bucket (LDS integer adds), an exclusive scan over (bucket, wave) in
+// bucket-major order gives every wave its first position in each bucket, and
+// the wave then scatters its range in rounds of 64 slots, ranking equal
+// buckets within a round by ballots and advancing its own per-bucket cursor.
+// Only the wave touches its cursors, so the scatter needs no workgroup
+// barrier, and slot order inside a bucket stays ascending.
 template <int NT, typename IdPtr>
 __device__ void build_tiles_block(IdPtr ids, int N, int E, int BM, TilesScratch<NT>& S,
                                   int32_t* __restrict__ expert_offsets,
@@ -75,16 +83,31 @@ __device__ void build_tiles_block(IdPtr ids, int N, int E, int BM, TilesScratch<
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int NB = E + 1;  // buckets in use
+  const int L = ((N + kW - 1) / kW + kWave - 1) / kWave * kWave;  // slots per wave
+  const int p0 = wave * L;
+  const int p1 = min(N, p0 + L);
+  auto bucket = [&](int p) {
+    const int e = ids[p];
+    return (e < 0 || e >= E) ? E : e;
+  };
 
-  for (int i = tid; i < NB; i += NT) { S.cnt[i] = 0; S.run[i] = 0; }
+  for (int i = tid; i < kW * NB; i += NT) S.wcnt[i / NB][i % NB] = 0;
   lds_barrier();
-  for (int p = tid; p < N; p += NT) {
-    int e = ids[p];
-    e = (e < 0 || e >= E) ? E : e;
-    atomicAdd(&S.cnt[e], 1);
+#pragma unroll 8
+  for (int p = p0 + lane; p < p1; p += kWave) atomicAdd(&S.wcnt[wave][bucket(p)], 1);
+  lds_barrier();
+  // per bucket: total, and each wave's first position relative to the
+  // bucket (exclusive scan over waves, in wave order)
+  for (int i = tid; i < NB; i += NT) {
+    int run = 0;
+    for (int w = 0; w < kW; ++w) {
+      const int c = S.wcnt[w][i];
+      S.wcnt[w][i] = run;
+      run += c;
+    }
+    S.cnt[i] = run;
+    S.ntile[i] = (i < E) ? (run + BM - 1) / BM : 0;
   }
-  lds_barrier();
-  for (int i = tid; i < NB; i += NT) S.ntile[i] = (i < E) ? (S.cnt[i] + BM - 1) / BM : 0;
   lds_barrier();
   if (wave == 0) wave_exclusive_scan(S.cnt, S.off, NB, lane);
   if (wave == 1) wave_exclusive_scan(S.ntile, S.toff, NB, lane);
@@ -92,39 +115,38 @@ __device__ void build_tiles_block(IdPtr ids, int N, int E, int BM, TilesScratch<
   for (int i = tid; i <= E; i += NT) expert_offsets[i] = S.off[i];
 
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int c0 = 0; c0 < N; c0 += NT) {
-    for (int i = tid; i < kW * NB; i += NT) S.wcnt[i / NB][i % NB] = 0;
-    const int p = c0 + tid;
-    const bool valid = p < N;
-    int e = 0;
-    if (valid) {
-      e = ids[p];
-      e = (e < 0 || e >= E) ? E : e;
-    }
-    uint64_t same = __ballot(valid);
+  constexpr int kBatch = 8;  // rounds whose ids are loaded together
+  for (int c1 = p0; c1 < p1; c1 += kBatch * kWave) {  // wave-uniform
+    int eb[kBatch];
 #pragma unroll
-    for (int bit = 0; bit < 9; ++bit) {
-      const bool b = (e >> bit) & 1;
-      const uint64_t bal = __ballot(b);
-      same &= b ? bal : ~bal;
+    for (int j = 0; j < kBatch; ++j) {
+      const int p = c1 + j * kWave + lane;
+      eb[j] = p < p1 ? bucket(p) : 0;
     }
-    const int rank = lanes_below(same);
-    lds_barrier();  // wcnt zeroed
-    if (valid && (same & ~lt_mask & ~(1ull << lane)) == 0)  // last lane of its group
-      S.wcnt[wave][e] = rank + 1;
-    lds_barrier();
-    if (valid) {
-      int before = S.off[e] + S.run[e] + rank;
-      for (int w = 0; w < wave; ++w) before += S.wcnt[w][e];
-      sorted_ids[before] = p;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int c0 = c1 + j * kWave;
+      if (c0 >= p1) break;  // wave-uniform
+      const int p = c0 + lane;
+      const bool valid = p < p1;
+      const int e = eb[j];
+      uint64_t same = __ballot(valid);
+#pragma unroll
+      for (int bit = 0; bit < 9; ++bit) {
+        const bool b = (e >> bit) & 1;
+        const uint64_t bal = __ballot(b);
+        same &= b ? bal : ~bal;
+      }
+      const int rank = lanes_below(same);
+      int cur = 0;
+      if (valid) {
+        cur = S.wcnt[wave][e];
+        sorted_ids[S.off[e] + cur + rank] = p;
+      }
+      // the group's last lane moves the wave's cursor past the group (read
+      // above, written here, read again next round: one wave, in order)
+      if (valid && (same & ~lt_mask & ~(1ull << lane)) == 0) S.wcnt[wave][e] = cur + rank + 1;
     }
-    lds_barrier();
-    for (int i = tid; i < NB; i += NT) {
-      int add = 0;
-      for (int w = 0; w < kW; ++w) add += S.wcnt[w][i];
-      S.run[i] += add;
-    }
-    lds_barrier();
   }
 
   const int total = S.toff[E];
