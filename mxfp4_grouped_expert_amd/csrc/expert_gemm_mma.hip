@@ -157,22 +157,10 @@ __device__ __forceinline__ void issue_w(const UnitCtx& c, int it, int st) {
 __device__ __forceinline__ void lds_wait_all() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 // K loop and epilogue of one wave: all kNFW weight fragments of slice wn
-// against NMW token fragments of the tile's half mg (rows 64*mg + 16*i ..),
-// with XCW activation loads per wave and stage (1: rows 0..63 of the tile,
-// 2: rows 0..127).  NMW (0..4) and XCW are compile-time constants so the
-// loop body is straight-line code; a wave with NMW = 0 only loads and syncs.
-//
-// Software pipeline, per iteration it (stage it in buffer it % 4):
-//   region 1: read the step-1 activation operands of stage it; MFMAs of
-//             step 0 (operands already in registers);
-//   sync:     stage it is fully read (lgkmcnt 0) and stage it+1 has landed
-//             (vmcnt): barrier;
-//   region 2: refill buffer it % 4 with stage it+4; read the weights, scale
-//             bytes and step-0 activation operands of stage it+1; MFMAs of
-//             step 1; decode both steps' weights of stage it+1 to bf16.
-// The MFMAs of a region never wait for the LDS reads issued in it, and one
-// barrier per iteration both publishes a stage and frees a buffer.
-// Scheduling fences keep instructions from drifting across the sync.
+// against NMW token fragments starting at tile row mrow0, with XCW
+// activation loads per wave and stage (1: rows 0..63 of the tile, 2: rows
+// 0..127).  NMW (0..4) and XCW are compile-time constants so the loop body
+// is straight-line code; a wave with NMW = 0 only loads and syncs.
 template <bool GATEUP, int NMW, int XCW>
 __device__ __forceinline__ void unit_main(const UnitCtx& c, int mrow0) {
   constexpr int NF = kNFW;
