@@ -66,6 +66,13 @@ __device__ __forceinline__ uint32_t word(const uint4& q, int j) {
 // (K <= kChunk * 512, KB <= 96).
 constexpr int kScaleRunMax = kRowsPerBlock * kChunk * kBlocksPerStep;  // 1536 bytes
 
+// Wait until at most N of this wave's vector-memory operations are pending.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 // Row stride of the staged activations in LDS: K bf16 plus a 16-byte pad.
 __host__ __device__ __forceinline__ int act_stride_bytes(int K) { return K * 2 + 16; }
 
@@ -82,13 +89,17 @@ __global__ __launch_bounds__(256 * NBW) void expert_gemm_kernel(
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int NW = GATEUP ? 2 : 1;  // weight rows per lane per step (gate + up)
 
+  // The tile count and the tile's row are read together (one round trip
+  // instead of two dependent ones); the row exists for every workgroup, as
+  // the grid has one workgroup per possible tile.
   const int tile = blockIdx.x;
-  if (tile >= num_tiles[0]) return;  // uniform over the workgroup
+  const int ntiles = num_tiles[0];
   const int e = tiles[3 * tile + 0];
   const int r0 = tiles[3 * tile + 1];
   const int rows = tiles[3 * tile + 2];
+  asm volatile("" ::"s"(ntiles), "s"(e), "s"(r0), "s"(rows));  // all four loads, one wait
   const long long nslots = (long long)T * k;
-  if (!tile_ok(e, r0, rows, E, nslots)) return;  // uniform
+  if (tile >= ntiles || !tile_ok(e, r0, rows, E, nslots)) return;  // uniform
 
   const int K = GATEUP ? H : I;       // reduction length
   const int N = GATEUP ? I : H;       // output rows (row pairs for gate/up)
@@ -193,38 +204,51 @@ __global__ __launch_bounds__(256 * NBW) void expert_gemm_kernel(
     }
   };
 
-  if constexpr (ONECHUNK) {  // depends only on the tile row
-    load_weights(0);
+  // With one K chunk and activation rows that do not depend on the slot ids
+  // (down, or a single token), the activations and the scale piece are
+  // issued ahead of the weights and waited for alone; each step's MFMAs then
+  // start as soon as that step's weights land.  Otherwise the weights go
+  // first and everything is waited for at once.
+  const bool early = ONECHUNK && (!GATEUP || T == 1);  // uniform
+  if (early) {
+    if (tid < rows) s_rowoff[tid] = GATEUP ? 0LL : (long long)(r0 + tid) * I;
+    lds_barrier();
+    stage_acts(0, min(XR, rows));
     load_scale_runs();
-  }
-  // Row offsets: for down they are the tile's own rows of h, and with one
-  // token every gate/up row is token 0, so neither waits for the slot ids
-  // (which queue behind the weight stream); the slot ids go to LDS once the
-  // stream has landed.
-  if (tid < rows) {
-    long long off;
-    if (GATEUP) {
-      const int t = T == 1 ? 0 : min(max(my_slot / k, 0), T - 1);
-      off = (long long)t * H;
-    } else {
-      off = (long long)(r0 + tid) * I;
+    asm volatile("" ::: "memory");  // the weight loads stay behind
+    load_weights(0);
+    wait_vmcnt<kChunk * NW>();      // all but the weight loads
+  } else {
+    if constexpr (ONECHUNK) {  // depends only on the tile row
+      load_weights(0);
+      load_scale_runs();
     }
-    s_rowoff[tid] = off;
+    // Row offsets: for down they are the tile's own rows of h, and with one
+    // token every gate/up row is token 0, so neither waits for the slot ids
+    // (which queue behind the weight stream).
+    if (tid < rows) {
+      long long off;
+      if (GATEUP) {
+        const int t = T == 1 ? 0 : min(max(my_slot / k, 0), T - 1);
+        off = (long long)t * H;
+      } else {
+        off = (long long)(r0 + tid) * I;
+      }
+      s_rowoff[tid] = off;
+    }
+    // LDS-only barrier: __syncthreads would also wait for the whole weight
+    // stream issued above, and the activation staging below would no longer
+    // overlap it (the slot-id load was issued first, so using it waited only
+    // for that load)
+    lds_barrier();
+    // Pass 0's activations are staged while the weight stream is in flight;
+    // one wait covers both.
+    stage_acts(0, min(XR, rows));
+    __builtin_amdgcn_s_waitcnt(0);
   }
-  // LDS-only barrier: __syncthreads would also wait for the whole weight
-  // stream issued above, and the activation staging below would no longer
-  // overlap it (the slot-id load was issued first, so using it waited only
-  // for that load)
-  lds_barrier();
-
-  // Pass 0's activations are staged while the weight stream is in flight;
-  // one wait covers both.  With K <= kChunk*512 (ONECHUNK) a wave's whole
-  // share of the weights is loaded once and reused by every pass.
-  stage_acts(0, min(XR, rows));
-  __builtin_amdgcn_s_waitcnt(0);
   if constexpr (ONECHUNK) store_scale_runs();
   if (tid < rows) s_slot[tid] = my_slot;
-  __syncthreads();
+  lds_barrier();  // this wave's staging loads have landed (waited above)
 
   for (int pass = 0; pass < npass; ++pass) {
     const int p0 = pass * XR;
@@ -244,15 +268,6 @@ __global__ __launch_bounds__(256 * NBW) void expert_gemm_kernel(
 #pragma unroll
         for (int w = 0; w < NW; ++w) sreg[c][w] = s_sc[(nb * NW + w) * kScaleRunMax + li * KB + bc];
       }
-      // The weights are decoded only after the staging barrier (an empty
-      // asm that "modifies" them stops the compiler from hoisting the
-      // decode, which would quadruple their register footprint).
-#pragma unroll
-      for (int c = 0; c < kChunk; ++c)
-#pragma unroll
-        for (int w = 0; w < NW; ++w)
-          asm volatile("" : "+v"(wreg[c][w].x), "+v"(wreg[c][w].y), "+v"(wreg[c][w].z),
-                       "+v"(wreg[c][w].w), "+v"(sreg[c][w]));
     }
     floatx4 acc[NW];
 #pragma unroll
@@ -263,6 +278,14 @@ __global__ __launch_bounds__(256 * NBW) void expert_gemm_kernel(
       if constexpr (!ONECHUNK) load_weights(ch);
 #pragma unroll
       for (int c = 0; c < kChunk; ++c) {
+        // Step c's weights are decoded here and no earlier: an empty asm that
+        // "modifies" them stops the compiler from hoisting the decode (which
+        // would quadruple their register footprint) and makes this step wait
+        // for its own loads only.
+#pragma unroll
+        for (int w = 0; w < NW; ++w)
+          asm volatile("" : "+v"(wreg[c][w].x), "+v"(wreg[c][w].y), "+v"(wreg[c][w].z),
+                       "+v"(wreg[c][w].w), "+v"(sreg[c][w]));
         const int b = (ch * kChunk + c) * kBlocksPerStep + kq * 4 + grp;
         const bool valid = b < KB;
         const int bc = min(b, KB - 1);

@@ -332,6 +332,71 @@ constexpr int kFusedMaxTE = kFusedMaxT * kMaxExperts;  // logits staged in LDS a
 constexpr int kFusedMaxSlots = kFusedMaxT * kMaxTopk;
 constexpr int kFusedMaxSplits = 32;
 
+// The logits of a single token, lane l holding experts l, l+64, ...: the
+// K-range partials (agent-scope atomic loads, all in flight at once) summed
+// in order plus the bias, as router_topk_softmax sums them.
+__device__ void one_token_logits(const double* __restrict__ partial,
+                                 const float* __restrict__ bias, int E, int splits,
+                                 double (&val)[4]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = lane + kWave * i;
+    double v = 0.0;
+    if (e < E) {
+      double p[kFusedMaxSplits];
+#pragma unroll
+      for (int c = 0; c < kFusedMaxSplits; ++c) {
+        p[c] = __hip_atomic_load(&partial[(size_t)min(c, splits - 1) * E + e], __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+      }
+#pragma unroll
+      for (int c = 0; c < kFusedMaxSplits; ++c)
+        if (c < splits) v += p[c];
+      if (bias) v += (double)bias[e];
+    }
+    val[i] = v;
+  }
+}
+
+// The tail of the fused launch for a single token, run by one wave with the
+// token's logits in val (lane l: experts l, l+64, ...): top-k and softmax by
+// topk_softmax_wave (the unfused path's code, so ids and weights are
+// identical), and the tile table of the k slots.  Their experts are
+// distinct, so slot j's position in expert order is the number of selected
+// experts below its own, every selected expert gets one tile of one row, and
+// build_tiles_small would produce exactly this table.
+__device__ void tail_one_token(const double (&val)[4], int E, int k,
+                               int32_t* __restrict__ topk_ids,
+                               float* __restrict__ topk_weights, double* __restrict__ logits,
+                               int* s_ids, int32_t* __restrict__ expert_offsets,
+                               int32_t* __restrict__ sorted_ids, int32_t* __restrict__ tiles,
+                               int32_t* __restrict__ num_tiles) {
+  const int lane = threadIdx.x & 63;
+  if (logits)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (lane + kWave * i < E) logits[lane + kWave * i] = val[i];
+  topk_softmax_wave(val, E, k, 0, topk_ids, topk_weights, s_ids);  // lane 0 fills s_ids
+  // (lane 0's LDS writes precede these reads in the wave's instruction order)
+  int ej = 0;
+  if (lane < k) ej = s_ids[lane];
+  int pos = 0;  // selected experts below ej
+  for (int q = 0; q < k; ++q) pos += s_ids[q] < ej;
+  if (lane < k) {
+    sorted_ids[pos] = lane;
+    tiles[3 * pos + 0] = ej;
+    tiles[3 * pos + 1] = pos;
+    tiles[3 * pos + 2] = 1;
+  }
+  for (int e = lane; e <= E; e += kWave) {
+    int below = 0;
+    for (int q = 0; q < k; ++q) below += s_ids[q] < e;
+    expert_offsets[e] = below;
+  }
+  if (lane == 0) num_tiles[0] = k;
+}
+
 __global__ __launch_bounds__(kFusedThreads) void router_decode_fused(
     const uint16_t* __restrict__ x, const float* __restrict__ w_router,
     const float* __restrict__ bias, int T, int H, int E, int k, int BM, int split_len,
@@ -367,6 +432,17 @@ __global__ __launch_bounds__(kFusedThreads) void router_decode_fused(
   if (threadIdx.x == 0) s_last = (atomicAdd(counter, 1) == nwg - 1);
   __syncthreads();
   if (!s_last) return;  // uniform over the workgroup
+  if (T == 1) {  // uniform: one wave finishes a single token, no barriers
+    if (threadIdx.x < kWave) {
+      double val[4];
+      one_token_logits(partial, bias, E, splits, val);
+      tail_one_token(val, E, k, topk_ids, topk_weights, logits, s_ids, expert_offsets,
+                     sorted_ids, tiles, num_tiles);
+      if (threadIdx.x == 0)
+        __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    return;
+  }
 
   // fixed-order sum of the K-range partials (+ bias); all loads independent
   const int TE = T * E;
