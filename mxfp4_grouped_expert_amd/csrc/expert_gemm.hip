@@ -339,6 +339,133 @@ __global__ __launch_bounds__(256 * NBW) void expert_gemm_kernel(
   }
 }
 
+// Down GEMM and combine of a single token in one launch (T = 1, k <= 4).
+// Workgroup n owns output rows 16n .. 16n+15 of w2 for all k tiles at once:
+// waves 4g .. 4g+3 are tile g's split-K group and run exactly the arithmetic
+// of expert_gemm_kernel<false, 1, 1, true> for that tile (same blocks per
+// lane, same MFMA order, same fixed-order split-K sum), so each slot's y
+// value is bit-identical to the unfused down GEMM's; the k values then meet
+// in LDS and are combined as combine_kernel does (fp32 fma in ascending slot
+// order, one bf16 rounding).  No y buffer and no extra launch.
+constexpr int kFuseMaxK = 4;
+__host__ __device__ __forceinline__ int fuse_row_region(int K) {
+  return (act_stride_bytes(K) + 1023) / 1024 * 1024;
+}
+
+__global__ __launch_bounds__(256 * kFuseMaxK) void down_combine_one_token_kernel(
+    const uint16_t* __restrict__ h, const uint8_t* __restrict__ wq,
+    const uint8_t* __restrict__ ws, const int32_t* sorted_ids,
+    const int32_t* __restrict__ tiles, const int32_t* __restrict__ num_tiles,
+    const float* __restrict__ topk_weights, int H, int I, int E, int k,
+    uint16_t* __restrict__ out) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int li = lane & 15;
+  const int grp = lane >> 4;
+  const int g = wave >> 2;   // tile (slot group) of this wave
+  const int kq = wave & 3;   // K quarter
+  const int K = I, KB = K / 32;
+  const int n_row = blockIdx.x * kRowsPerBlock + li;  // grid covers H / 16 blocks exactly
+
+  // every tile row in one round trip; a tile outside the table (g >= count)
+  // or malformed computes nothing and contributes nothing
+  const int ntiles = num_tiles[0];
+  const int gt = min(g, k - 1);
+  const int e = tiles[3 * gt + 0];
+  const int r0 = tiles[3 * gt + 1];
+  const int rows = tiles[3 * gt + 2];
+  asm volatile("" ::"s"(ntiles), "s"(e), "s"(r0), "s"(rows));
+  const bool live = g < k && g < ntiles && tile_ok(e, r0, rows, E, k) && rows == 1;  // uniform per wave
+  const int slot = live ? sorted_ids[r0] : -1;
+
+  // LDS: tile g's staged h row (I bf16 + 16-byte pad, in a region rounded
+  // up to whole kilobytes: the last load instruction's surplus slots land
+  // there) | its scale run (16 rows x KB bytes) | the split-K table
+  const int region = fuse_row_region(K);
+  unsigned char* arow = smem + g * region;
+  unsigned char* s_sc = smem + kFuseMaxK * region + g * kScaleRunMax;
+  float* red = reinterpret_cast<float*>(smem + kFuseMaxK * (region + kScaleRunMax));
+  __shared__ int s_slot[kFuseMaxK];
+
+  uint4 wreg[kChunk];
+  uint32_t sreg[kChunk];
+  if (live) {
+    // activations first (row r0 of h, one 16-byte slot per lane of the group,
+    // the pad slot repeating the last chunk), then the scale run, then the
+    // weights, so that each step waits for its own weights only
+    const int cpr = K / 8, spr = cpr + 1;
+    const int gl = tid & 255;
+    for (int ins = kq; ins < (spr + 63) / 64; ins += 4) {  // wave-uniform
+      const int sl = ins * 64 + lane;
+      const int c = min(sl, cpr - 1);
+      __builtin_amdgcn_global_load_lds(
+          h + (size_t)r0 * I + (size_t)c * 8,
+          (__attribute__((address_space(3))) void*)(arow + (size_t)ins * 1024), 16, 0, 0);
+    }
+    const size_t grow0 = (size_t)e * H + (size_t)blockIdx.x * kRowsPerBlock;
+    const int piece = min(gl, KB - 1);
+    const uint4 sp = *reinterpret_cast<const uint4*>(ws + grow0 * KB + (size_t)piece * 16);
+    asm volatile("" ::: "memory");
+    const size_t wrow = (size_t)e * H + n_row;
+#pragma unroll
+    for (int c = 0; c < kChunk; ++c) {
+      const int bc = min(c * kBlocksPerStep + kq * 4 + grp, KB - 1);
+      wreg[c] = *reinterpret_cast<const uint4*>(wq + wrow * (K / 2) + (size_t)bc * 16);
+    }
+    wait_vmcnt<kChunk>();  // activations and the scale piece
+    if (gl < KB) *reinterpret_cast<uint4*>(s_sc + gl * 16) = sp;
+  }
+  if (tid < kFuseMaxK) s_slot[tid] = -1;
+  lds_barrier();
+  if (live && kq == 0 && lane == 0) s_slot[g] = slot;
+
+  floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+  if (live) {
+#pragma unroll
+    for (int c = 0; c < kChunk; ++c) {
+      const int bc = min(c * kBlocksPerStep + kq * 4 + grp, KB - 1);
+      sreg[c] = s_sc[li * KB + bc];
+    }
+#pragma unroll
+    for (int c = 0; c < kChunk; ++c) {
+      asm volatile("" : "+v"(wreg[c].x), "+v"(wreg[c].y), "+v"(wreg[c].z), "+v"(wreg[c].w),
+                   "+v"(sreg[c]));
+      const int b = c * kBlocksPerStep + kq * 4 + grp;
+      const int bc = min(b, KB - 1);
+      const float scale = b < KB ? e8m0_to_float(sreg[c]) : 0.f;
+      const uint4* ap = reinterpret_cast<const uint4*>(arow + bc * 64);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc = mfma16x16x32(as_bf16x8(ap[j]), dequant8_bf16(word(wreg[c], j), scale), acc);
+    }
+  }
+  // split-K table: row 0 (the token) of each group's 16x16 result
+  if (live && grp == 0) red[(g * 4 + kq) * 16 + li] = acc[0];
+  __syncthreads();
+  if (tid < kRowsPerBlock) {
+    // y of slot j = fixed-order sum over the K quarters of its tile's table
+    float y[kFuseMaxK];
+#pragma unroll
+    for (int gg = 0; gg < kFuseMaxK; ++gg) {
+      float v = red[(gg * 4 + 0) * 16 + tid];
+#pragma unroll
+      for (int q = 1; q < 4; ++q) v += red[(gg * 4 + q) * 16 + tid];
+      y[gg] = v;
+    }
+    float a = 0.f;
+    for (int j = 0; j < k; ++j) {
+      float yj = 0.f;
+#pragma unroll
+      for (int gg = 0; gg < kFuseMaxK; ++gg)
+        if (s_slot[gg] == j) yj = y[gg];
+      a = fmaf(topk_weights[j], yj, a);
+    }
+    out[blockIdx.x * kRowsPerBlock + tid] = float_to_bf16(a);
+  }
+}
+
 // Rows of activations staged per pass: twice the expected rows per expert
 // (T*k/E), bounded by the tile's row bound (an expert gets at most one slot
 // per token, so rows <= min(BM, T)), rounded up to a power of two, at most
@@ -404,6 +531,21 @@ void launch_gateup_swiglu(const uint16_t* x, const uint8_t* w13_q, const uint8_t
   }
   launch_expert_gemm<true>(x, w13_q, w13_s, sorted_ids, tiles, num_tiles, tiles_max, T, H, I, E,
                            k, BM, h, stream);
+}
+
+bool down_combine_one_token_ok(int T, int H, int I, int k) {
+  return T == 1 && k <= kFuseMaxK && I <= kChunk * kBlocksPerStep * 32 && H % kRowsPerBlock == 0;
+}
+
+void launch_down_combine_one_token(const uint16_t* h, const uint8_t* w2_q, const uint8_t* w2_s,
+                                   const int32_t* sorted_ids, const int32_t* tiles,
+                                   const int32_t* num_tiles, const float* topk_weights, int H,
+                                   int I, int E, int k, uint16_t* out, hipStream_t stream) {
+  const size_t red_bytes = (size_t)kFuseMaxK * 4 * 16 * sizeof(float);
+  const size_t lds = (size_t)kFuseMaxK * (fuse_row_region(I) + kScaleRunMax) + red_bytes;
+  hipLaunchKernelGGL(down_combine_one_token_kernel, dim3(H / kRowsPerBlock),
+                     dim3(256 * kFuseMaxK), lds, stream, h, w2_q, w2_s, sorted_ids, tiles,
+                     num_tiles, topk_weights, H, I, E, k, out);
 }
 
 void launch_down(const uint16_t* h, const uint8_t* w2_q, const uint8_t* w2_s,

@@ -241,6 +241,12 @@ moe_status moe_forward(const uint16_t* x, const uint8_t* w13_q, const uint8_t* w
   hipStream_t s = as_stream(stream);
   moe::launch_gateup_swiglu(x, w13_q, w13_s, sorted_ids, tiles, num_tiles, (int)tmax, T, H, I, E,
                             k, BM, h, s);
+  if (moe::down_combine_one_token_ok(T, H, I, k)) {
+    // one token: down GEMM and combine in one launch, bit-identical to the two
+    moe::launch_down_combine_one_token(h, w2_q, w2_s, sorted_ids, tiles, num_tiles, topk_weights,
+                                       H, I, E, k, out, s);
+    return finish_launches();
+  }
   moe::launch_down(h, w2_q, w2_s, sorted_ids, tiles, num_tiles, (int)tmax, T, H, I, E, k, BM, y,
                    s);
   moe::launch_combine(y, topk_weights, T, H, k, out, s);

@@ -47,6 +47,13 @@ void launch_down(const uint16_t* h, const uint8_t* w2_q, const uint8_t* w2_s,
                  int tiles_max, int T, int H, int I, int E, int k, int BM, float* y,
                  hipStream_t stream);
 
+// Down GEMM and combine of a single token in one launch (no y buffer).
+bool down_combine_one_token_ok(int T, int H, int I, int k);
+void launch_down_combine_one_token(const uint16_t* h, const uint8_t* w2_q, const uint8_t* w2_s,
+                                   const int32_t* sorted_ids, const int32_t* tiles,
+                                   const int32_t* num_tiles, const float* topk_weights, int H,
+                                   int I, int E, int k, uint16_t* out, hipStream_t stream);
+
 // Large-tile (prefill) form of the grouped GEMMs: 128-row tiles, LDS-staged
 // operands.  expert_mma_ok says when the launchers above use it.
 bool expert_mma_ok(int T, int H, int I, int E, int k, int BM);

@@ -61,8 +61,15 @@ def test_graph_replays_match_eager(wid):
         torch.cuda.synchronize()
 
 
-def test_step_entry_points_equal_forward():
-    inp = make_random(T=37, H=320, E=6, k=3, I=224, seed=21, router_std=0.3)
+# One token takes the fused down + combine launch inside moe_forward; it must
+# match the separate entry points bit for bit.
+STEP_CASES = [(37, 320, 6, 3, 224), (1, 320, 6, 3, 224), (1, 2880, 8, 4, 2880), (1, 64, 1, 1, 32)]
+
+
+@pytest.mark.parametrize("case", STEP_CASES, ids=lambda c: "T{}_H{}_E{}_k{}_I{}".format(*c))
+def test_step_entry_points_equal_forward(case):
+    T, H, E, k, I = case
+    inp = make_random(T=T, H=H, E=E, k=k, I=I, seed=21 + T, router_std=0.3)
     d = to_device(inp)
     k, E, BM = inp["k"], inp["E"], 16
     log("step entry points vs moe_forward")
