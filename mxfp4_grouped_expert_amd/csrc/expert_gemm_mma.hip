@@ -23,10 +23,10 @@
 //   down: a fragment is 16 rows of w2; 384 output columns per unit.
 //
 // K loop: 64 K per stage (two MX blocks), four stage buffers in LDS: the
-// stage being read and the next three in flight.  MFMA 16x16x32: lane group g supplies K elements
-// 32*(g>>1) + 16*(g&1) + 8j .. +8 of the stage for step j = 0, 1 (any K order
-// works as long as both operands use it), so a lane's weight operand is one
-// 8-byte half of one MX block and its scale is one byte.  All loads in the
+// stage being read and two in flight.  MFMA 16x16x32: lane group g supplies
+// K elements 32*(g>>1) + 16*(g&1) + 8j .. +8 of the stage for step j = 0, 1
+// (any K order works as long as both operands use it), so a lane's weight
+// operand is one 8-byte half of one MX block and its scale is one byte.  All loads in the
 // loop are direct global->LDS 16-byte loads (global_load_lds_dwordx4), a
 // fixed number per wave and stage, so a stage wait is an exact vmcnt:
 //   * activations: 64 or 128 rows x 128 B (as many as the tile needs),
@@ -171,12 +171,14 @@ __device__ __forceinline__ void unit_main(const UnitCtx& c, int mrow0) {
   const int sub = grp & 1;    // which 8-byte half of it
   const int ww = 2 - c.mg;    // weight loads of this wave per stage
   const int niters = c.niters;
-  // loads per stage of this wave: stages 0..2 are issued before the loop
-  // (their weights, and stage 3's, came with the prologue); stage s >= 3 is
-  // issued in iteration s - 3 with its weights.  Stages past the last one are
-  // loaded too (clamped, in-bounds addresses, into a buffer that is not read
-  // again), so the loop issues a fixed number of loads per iteration.
-  auto loads = [&](int s) { return s <= 2 ? XCW : XCW + ww; };
+  // loads per stage of this wave: stages 0 and 1 are issued before the loop
+  // (their weights, and those of stages 2 and 3, came with the prologue);
+  // stage s >= 2 is issued in iteration s - 2 with its weights.  Stages past
+  // the last one are loaded too (clamped, in-bounds addresses, into a buffer
+  // that is not read again), so the loop issues a fixed number of loads per
+  // iteration.  Two stages ahead measured faster than three (fewer loads in
+  // flight compete less with the MFMA phases).
+  auto loads = [&](int s) { return s <= 1 ? XCW : XCW + ww; };
 
   // this lane's source rows of the activation loads (load t covers rows
   // 8L .. 8L+7, L = 8t + wave, the lane's row being 8L + (lane >> 3)); its
@@ -272,13 +274,13 @@ __device__ __forceinline__ void unit_main(const UnitCtx& c, int mrow0) {
     }
     __builtin_amdgcn_sched_barrier(0);
   };
-  // MFMA phase: stage `it`; this wave also issues its share of stage it+3,
-  // into the buffer of stage it-1 (read by both groups before the previous
+  // MFMA phase: stage `it`; this wave also issues its share of stage it+2,
+  // into the buffer of stage it-2 (read by both groups before the previous
   // barrier)
   auto mfma_phase = [&](int it) {
-    const int st = (it + 3) & (kStages - 1);
-    issue_x(it + 3, st);
-    issue_w(c, it + 3, st);
+    const int st = (it + 2) & (kStages - 1);
+    issue_x(it + 2, st);
+    issue_w(c, it + 2, st);
     if (NMW > 0) {
       __builtin_amdgcn_s_setprio(1);
       mfmas(a[0], b[0], 0, NF);
@@ -293,19 +295,19 @@ __device__ __forceinline__ void unit_main(const UnitCtx& c, int mrow0) {
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // stages 0..2 in flight; every wave's share of stage 0 lands before the
+  // stages 0 and 1 in flight; every wave's share of stage 0 lands before the
   // first barrier.  Before phase 2s (group 0 reads stage s) every wave's
-  // share of stage s has landed: group 0 then has stages s+1, s+2 pending
-  // at most, group 1 (which issued up to stage s+1) stage s+1.
-  for (int s = 0; s < 3; ++s) issue_x(s, s);
-  wait_vm(loads(1) + loads(2));
+  // share of stage s has landed: group 0 then has stage s+1 pending at most,
+  // group 1 (which issued up to stage s) nothing.
+  for (int s = 0; s < 2; ++s) issue_x(s, s);
+  wait_vm(loads(1));
   barrier();
   if (c.mg == 0) {
     for (int it = 0; it < niters; ++it) {
       load_phase(it);                       // phase 2it
       barrier();
       mfma_phase(it);                       // phase 2it+1
-      wait_vm(loads(it + 2) + loads(it + 3));
+      wait_vm(loads(it + 2));
       barrier();
     }
     // phase 2*niters: group 1's last MFMA phase
@@ -313,7 +315,7 @@ __device__ __forceinline__ void unit_main(const UnitCtx& c, int mrow0) {
     barrier();                              // phase 0: group 0's first load
     for (int it = 0; it < niters; ++it) {
       load_phase(it);                       // phase 2it+1
-      wait_vm(loads(it + 2));
+      vm_wait<0>();
       barrier();
       mfma_phase(it);                       // phase 2it+2
       if (it + 1 < niters) barrier();
