@@ -114,15 +114,25 @@ __global__ __launch_bounds__(256 * NBW) void expert_gemm_kernel(
   const int n_base = (blockIdx.y * NBW + nb) * kRowsPerBlock;
   const int n_row = n_base < N ? n_base + li : li;  // blocks past N compute, never store
 
-  // weight rows of this lane
+  // Weight rows this lane loads.  In the gate/up kernel with one K chunk and
+  // one 16-row block per workgroup, a wave instruction reads 4 rows x 256
+  // contiguous bytes (lane l: row 4*kq + l/16 of the block, MX block
+  // 16*step + l%16), which streams from HBM markedly faster than 16 rows x
+  // 64 bytes; each step's pieces are then exchanged through LDS so that
+  // every lane holds row li, block 16*step + 4*kq + grp, as the MFMAs need.
+  // The other variants load that mapping directly: for down the exchange's
+  // per-step barriers and LDS cost more than the faster stream gains, and
+  // with 4 blocks per workgroup its LDS would lower occupancy.
   const size_t q_stride = (size_t)K / 2;
   const size_t s_stride = (size_t)K / 32;
+  constexpr bool XCHG = GATEUP && ONECHUNK && NBW == 1;
+  const int l_row = XCHG ? (n_base < N ? n_base : 0) + 4 * kq + (lane >> 4) : n_row;
   size_t wrow[NW];
   if (GATEUP) {
-    wrow[0] = (size_t)e * 2 * I + n_row;
-    if (NW > 1) wrow[NW - 1] = (size_t)e * 2 * I + I + n_row;
+    wrow[0] = (size_t)e * 2 * I + l_row;
+    if (NW > 1) wrow[NW - 1] = (size_t)e * 2 * I + I + l_row;
   } else {
-    wrow[0] = (size_t)e * H + n_row;
+    wrow[0] = (size_t)e * H + l_row;
   }
 
   const int nsteps = (KB + kBlocksPerStep - 1) / kBlocksPerStep;
@@ -136,7 +146,8 @@ __global__ __launch_bounds__(256 * NBW) void expert_gemm_kernel(
   auto load_weights = [&](int ch) {
 #pragma unroll
     for (int c = 0; c < kChunk; ++c) {
-      const int b = (ch * kChunk + c) * kBlocksPerStep + kq * 4 + grp;
+      const int b = XCHG ? c * kBlocksPerStep + (lane & 15)
+                             : (ch * kChunk + c) * kBlocksPerStep + kq * 4 + grp;
       const int bc = min(b, KB - 1);  // clamped: always a valid address
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
@@ -154,6 +165,18 @@ __global__ __launch_bounds__(256 * NBW) void expert_gemm_kernel(
   static_assert(!ONECHUNK || kRuns * kChunk * kBlocksPerStep <= 256 * NBW,
                 "one scale piece per thread");
   __shared__ __align__(16) unsigned char s_sc[ONECHUNK ? NBW * NW * kScaleRunMax : 16];
+
+  // XCHG: LDS slots through which one step of the workgroup's weights is
+  // exchanged between its 4 waves: [slot][half][row][16 pieces of 16
+  // bytes], piece p of row r stored at position p ^ r so that both the
+  // row-wise writes and the column-wise reads spread over all banks.  With
+  // one staged token, two slots let step c+1 be written while step c is
+  // read; with more, one slot (and a second barrier per step) keeps the
+  // LDS footprint low enough for as many workgroups per CU as the
+  // registers allow, which measured faster.
+  constexpr int kRing = XR == 1 ? 2 : 1;
+  constexpr int kSlotBytes = NW * NBW * kRowsPerBlock * 256;
+  __shared__ __align__(16) unsigned char s_ring[XCHG ? kRing * kSlotBytes : 16];
   uint4 spiece = uint4{0u, 0u, 0u, 0u};
   const int pr = min(tid / KB, kRuns - 1);  // this thread's run and piece
   const int pp = tid - pr * KB;
@@ -278,6 +301,20 @@ __global__ __launch_bounds__(256 * NBW) void expert_gemm_kernel(
       if constexpr (!ONECHUNK) load_weights(ch);
 #pragma unroll
       for (int c = 0; c < kChunk; ++c) {
+        if (XCHG && pass == 0) {  // uniform: exchange step c's pieces
+          unsigned char* slot = s_ring + (c % kRing) * kSlotBytes;
+          if (kRing == 1 && c > 0) lds_barrier();  // every wave done reading step c-1
+          const int wr16 = 4 * kq + (lane >> 4);
+#pragma unroll
+          for (int w = 0; w < NW; ++w)
+            *reinterpret_cast<uint4*>(slot + ((w * NBW + nb) * kRowsPerBlock + wr16) * 256 +
+                                      (((lane & 15) ^ wr16) << 4)) = wreg[c][w];
+          lds_barrier();
+#pragma unroll
+          for (int w = 0; w < NW; ++w)
+            wreg[c][w] = *reinterpret_cast<const uint4*>(
+                slot + ((w * NBW + nb) * kRowsPerBlock + li) * 256 + (((4 * kq + grp) ^ li) << 4));
+        }
         // Step c's weights are decoded here and no earlier: an empty asm that
         // "modifies" them stops the compiler from hoisting the decode (which
         // would quadruple their register footprint) and makes this step wait
