@@ -18,10 +18,17 @@
 // b = 16*step + 4*kq + group goes to lane group `group` (lanes 16*group ..
 // +15) of the block's wave kq.  A lane thus loads exactly one MX block (16
 // bytes, 32 codes) plus its scale byte per weight row and step, and a wave
-// reads 64 contiguous bytes of each of its 16 rows.  An MFMA sums over its
+// needs 64 contiguous bytes of each of its 16 rows (the one-chunk gate/up
+// kernel loads them in a faster pattern and regroups them through LDS, as
+// described at its loads).  An MFMA sums over its
 // whole K range, so the K order is free as long as the activation operand
 // uses the same assignment: for MFMA j (0..3) of a step, group g supplies
 // elements 32*b + 8*j .. +8 of both operands.
+//
+// Workgroup (x, y) is column block x of tile y, so the workgroups of one
+// tile are dispatched together and stream neighbouring rows of one
+// expert's weights; at 64 tokens this measured 6-13% faster than
+// dispatching column block by column block across all tiles.
 //
 // Memory behaviour.  All weight loads of a wave (up to kChunk steps) are
 // issued branch-free before the first MFMA (out-of-range blocks read a
@@ -92,7 +99,7 @@ __global__ __launch_bounds__(256 * NBW) void expert_gemm_kernel(
   // The tile count and the tile's row are read together (one round trip
   // instead of two dependent ones); the row exists for every workgroup, as
   // the grid has one workgroup per possible tile.
-  const int tile = blockIdx.x;
+  const int tile = blockIdx.y;
   const int ntiles = num_tiles[0];
   const int e = tiles[3 * tile + 0];
   const int r0 = tiles[3 * tile + 1];
@@ -111,7 +118,7 @@ __global__ __launch_bounds__(256 * NBW) void expert_gemm_kernel(
   const int grp = lane >> 4;
   const int nb = wave >> 2;           // 16-row block within the workgroup
   const int kq = wave & 3;            // K quarter of this wave
-  const int n_base = (blockIdx.y * NBW + nb) * kRowsPerBlock;
+  const int n_base = (blockIdx.x * NBW + nb) * kRowsPerBlock;
   const int n_row = n_base < N ? n_base + li : li;  // blocks past N compute, never store
 
   // Weight rows this lane loads.  In the gate/up kernel with one K chunk and
@@ -183,7 +190,7 @@ __global__ __launch_bounds__(256 * NBW) void expert_gemm_kernel(
   const bool has_piece = tid < kRuns * KB;
   auto load_scale_runs = [&]() {
     const int rb = pr / NW, rw = pr % NW;
-    const int nb0 = (blockIdx.y * NBW + rb) * kRowsPerBlock;
+    const int nb0 = (blockIdx.x * NBW + rb) * kRowsPerBlock;
     const int row0 = nb0 < N ? nb0 : 0;  // blocks past N read block 0's rows
     const size_t grow0 = GATEUP ? (size_t)e * 2 * I + (size_t)rw * I + row0
                                 : (size_t)e * H + row0;
@@ -354,7 +361,7 @@ __global__ __launch_bounds__(256 * NBW) void expert_gemm_kernel(
       const int idx = tid & 255;      // 16 tokens x 16 rows
       const int tm = idx / kRowsPerBlock;
       const int tn = idx % kRowsPerBlock;
-      const int on = (blockIdx.y * NBW + obl) * kRowsPerBlock + tn;
+      const int on = (blockIdx.x * NBW + obl) * kRowsPerBlock + tn;
       float v[NW];
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
@@ -535,7 +542,7 @@ void launch_expert_gemm(const uint16_t* act, const uint8_t* wq, const uint8_t* w
   do {                                                                                          \
     size_t lds = ((size_t)(XR_) * act_stride_bytes(K) + 1023) / 1024 * 1024;                    \
     if (lds < red_bytes_1 * (NBW_)) lds = red_bytes_1 * (NBW_);                                 \
-    dim3 grid(tiles_max, (nblk16 + (NBW_) - 1) / (NBW_));                                       \
+    dim3 grid((nblk16 + (NBW_) - 1) / (NBW_), tiles_max);                                       \
     if (one_chunk)                                                                              \
       hipLaunchKernelGGL((expert_gemm_kernel<GATEUP, NBW_, XR_, true>), grid, dim3(256 * (NBW_)), \
                          lds, stream, act, wq, ws, sorted_ids, tiles, num_tiles, T, H, I, E, k,  \
