@@ -221,41 +221,69 @@ __device__ __forceinline__ long long order_key(double v) {
   return b >= 0 ? b : (b ^ 0x7fffffffffffffffLL);
 }
 
-// Softmax over the k selected logits of token t (in selection order), in
-// fp64; writes ids and weights (and the ids to ids_lds when given).  Both
-// routing paths use it, so their weights are bit-identical.
-__device__ __forceinline__ void softmax_selected(const int* sel_e, const double* sel_v, int k,
-                                                 int t, int32_t* __restrict__ topk_ids,
-                                                 float* __restrict__ topk_weights,
-                                                 int* ids_lds) {
-  double m = sel_v[0];
+__device__ __forceinline__ double readlane_f64(double v, int l) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane((int)(b & 0xffffffffLL), l);
+  const int hi = __builtin_amdgcn_readlane((int)(b >> 32), l);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+
+__device__ __forceinline__ long long readlane_i64(long long v, int l) {
+  const int lo = __builtin_amdgcn_readlane((int)(v & 0xffffffffLL), l);
+  const int hi = __builtin_amdgcn_readlane((int)(v >> 32), l);
+  return ((long long)hi << 32) | (unsigned int)lo;
+}
+
+// Waits until this wave's LDS writes have completed, so its later reads (of
+// other lanes' entries) see them; the memory clobber keeps the compiler from
+// moving LDS accesses across.
+__device__ __forceinline__ void wave_lds_sync() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
+// max(v, v of the lane DPP control CTRL selects); lanes without a source
+// keep v
+template <int CTRL>
+__device__ __forceinline__ long long dpp_max_i64(long long v) {
+  const int lo = __builtin_amdgcn_update_dpp((int)(v & 0xffffffffLL), (int)(v & 0xffffffffLL),
+                                             CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp((int)(v >> 32), (int)(v >> 32), CTRL, 0xF, 0xF,
+                                             false);
+  const long long o = ((long long)hi << 32) | (unsigned int)lo;
+  return o > v ? o : v;
+}
+
+// Largest 64-bit key of the wave, the same value in every lane: the maximum
+// within each quad, then within each row of 16 (DPP), then over the 4 rows.
+__device__ __forceinline__ long long wave_max_i64(long long v) {
+  v = dpp_max_i64<0xB1>(v);   // quad_perm [1,0,3,2]
+  v = dpp_max_i64<0x4E>(v);   // quad_perm [2,3,0,1]
+  v = dpp_max_i64<0x124>(v);  // row_ror:4
+  v = dpp_max_i64<0x128>(v);  // row_ror:8
+  long long m = readlane_i64(v, 0);
 #pragma unroll
-  for (int j = 1; j < kMaxTopk; ++j)
-    if (j < k) m = fmax(m, sel_v[j]);
-  double z[kMaxTopk];
-  double sum = 0.0;
-#pragma unroll
-  for (int j = 0; j < kMaxTopk; ++j)
-    if (j < k) { z[j] = exp(sel_v[j] - m); sum += z[j]; }
-#pragma unroll
-  for (int j = 0; j < kMaxTopk; ++j) {
-    if (j < k) {
-      topk_ids[(size_t)t * k + j] = sel_e[j];
-      topk_weights[(size_t)t * k + j] = (float)(z[j] / sum);
-      if (ids_lds) ids_lds[t * k + j] = sel_e[j];
-    }
+  for (int r = 1; r < 4; ++r) {
+    const long long o = readlane_i64(v, 16 * r);
+    m = o > m ? o : m;
   }
+  return m;
 }
 
 // Top-k and softmax of one token by one wave.  Lane l holds the logits of
 // experts l, l+64, l+128, l+192 in val[] (entries >= E are ignored).  k
-// rounds of a wave-wide argmax on (higher logit, then lower expert index);
-// lane 0 takes the softmax of the winners in fp64 and writes them (and, if
-// ids_lds is given, the ids there too).
+// rounds of a wave-wide argmax on (higher logit, then lower expert index):
+// each round takes the largest order key, then the lowest expert holding it
+// (one ballot per slot), and retires that expert.  The softmax over the
+// winners is computed in fp64 as one formula: m = their maximum,
+// z_j = exp(v_j - m) with lane j taking z_j, the sum of z_0..z_{k-1} in
+// ascending j, w_j = z_j / sum, so the weights do not depend on which lane
+// computed which term.  Writes ids and weights (and, if ids_lds is given,
+// the ids there too).
 __device__ void topk_softmax_wave(const double (&val)[4], int E, int k, int t,
                                   int32_t* __restrict__ topk_ids,
                                   float* __restrict__ topk_weights, int* ids_lds) {
   const int lane = threadIdx.x & 63;
+  const int nI = (E + kWave - 1) / kWave;  // slots that hold experts (uniform)
   long long key[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) key[i] = (lane + kWave * i < E) ? order_key(val[i]) : LLONG_MIN;
@@ -264,29 +292,52 @@ __device__ void topk_softmax_wave(const double (&val)[4], int E, int k, int t,
   double sel_v[kMaxTopk];
 #pragma unroll
   for (int j = 0; j < kMaxTopk; ++j) {
-    if (j >= k) break;
-    long long bk = LLONG_MIN;
-    int be = 0x7fffffff;
-    double bv = 0.0;
+    sel_e[j] = 0;
+    sel_v[j] = 0.0;
+    if (j >= k) continue;
+    long long mine = key[0];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (key[i] > bk) { bk = key[i]; be = lane + kWave * i; bv = val[i]; }
-    }
+    for (int i = 1; i < 4; ++i)
+      if (i < nI) mine = key[i] > mine ? key[i] : mine;
+    const long long best = wave_max_i64(mine);
+    // the lowest expert with the best key: slots in order, lanes in order
+    int slot = 0, src = 0;
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const long long ok = __shfl_xor(bk, off);
-      const int oe = __shfl_xor(be, off);
-      const double ov = __shfl_xor(bv, off);
-      if (ok > bk || (ok == bk && oe < be)) { bk = ok; be = oe; bv = ov; }
+    for (int i = 3; i >= 0; --i) {
+      if (i >= nI) continue;
+      const uint64_t hit = __ballot(key[i] == best);
+      if (hit) { slot = i; src = __builtin_ctzll(hit); }
     }
-    sel_e[j] = be;
-    sel_v[j] = bv;
+    double v = val[0];
+#pragma unroll
+    for (int i = 1; i < 4; ++i)
+      if (slot == i) v = val[i];
+    sel_e[j] = src + kWave * slot;
+    sel_v[j] = readlane_f64(v, src);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      if (lane + kWave * i == be) key[i] = LLONG_MIN;
+      if (i == slot && lane == src) key[i] = LLONG_MIN;
   }
 
-  if (lane == 0) softmax_selected(sel_e, sel_v, k, t, topk_ids, topk_weights, ids_lds);
+  double m = sel_v[0];
+#pragma unroll
+  for (int j = 1; j < kMaxTopk; ++j)
+    if (j < k) m = fmax(m, sel_v[j]);
+  double vl = sel_v[0];
+  int el = sel_e[0];
+#pragma unroll
+  for (int j = 1; j < kMaxTopk; ++j)
+    if (lane == j) { vl = sel_v[j]; el = sel_e[j]; }
+  const double z = exp(vl - m);
+  double sum = 0.0;
+#pragma unroll
+  for (int j = 0; j < kMaxTopk; ++j)
+    if (j < k) sum += readlane_f64(z, j);
+  if (lane < k) {
+    topk_ids[(size_t)t * k + lane] = el;
+    topk_weights[(size_t)t * k + lane] = (float)(z / sum);
+    if (ids_lds) ids_lds[t * k + lane] = el;
+  }
 }
 
 __global__ __launch_bounds__(256) void router_topk_softmax(
@@ -377,8 +428,8 @@ __device__ void tail_one_token(const double (&val)[4], int E, int k,
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       if (lane + kWave * i < E) logits[lane + kWave * i] = val[i];
-  topk_softmax_wave(val, E, k, 0, topk_ids, topk_weights, s_ids);  // lane 0 fills s_ids
-  // (lane 0's LDS writes precede these reads in the wave's instruction order)
+  topk_softmax_wave(val, E, k, 0, topk_ids, topk_weights, s_ids);  // lanes < k fill s_ids
+  wave_lds_sync();
   int ej = 0;
   if (lane < k) ej = s_ids[lane];
   int pos = 0;  // selected experts below ej
@@ -489,7 +540,7 @@ __global__ __launch_bounds__(kFusedThreads) void router_decode_fused(
   }
   lds_barrier();
   // softmax: the k exponentials of a token in parallel, then each of its
-  // threads sums them in ascending j, the order of softmax_selected, so the
+  // threads sums them in ascending j, the order of topk_softmax_wave, so the
   // weights are bit-identical to the unfused path
   for (int i = threadIdx.x; i < T * k; i += kFusedThreads) {
     const int t = i / k;
