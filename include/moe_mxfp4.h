@@ -219,6 +219,46 @@ moe_status moe_route_tiles(const uint16_t* x, const float* w_router, const float
                            void* workspace, size_t workspace_bytes,
                            struct ihipStream_t* stream);
 
+/* --------------------------------------------------- moe_layer_one_token
+ * The whole layer for a single token (T = 1) in one launch: moe_route_tiles
+ * followed by moe_forward.  The write-up books launch and host gaps as their
+ * own cost of a decode step ("Where the time went": "Launch and host gaps");
+ * with one token, five dependent launches leave the GPU waiting between
+ * steps.  Here the routing, gate/up and down workgroups share one grid: each
+ * waits (by polling counters in the workspace) only for workgroups with a
+ * lower index, the down weights stream while gate/up still runs, and the
+ * last down workgroup of each 16-row block combines its k slots.  Every
+ * output is bit-identical to moe_route_tiles + moe_forward with the same
+ * arguments (BM any valid value: one token gives k one-row tiles).
+ *
+ *   arguments as for moe_route_tiles and moe_forward with T = 1; logits may
+ *   be NULL; bias may be NULL.  Also requires H <= 3072 and I <= 3072 (one
+ *   register chunk of weights per lane), else MOE_ERR_SHAPE.
+ *   workspace   >= moe_layer_one_token_workspace_bytes(H, I, E, k) (0 means
+ *               the shape is not accepted), 16-byte aligned.  Its first
+ *               moe_layer_one_token_sync_bytes(H) bytes are counters and
+ *               flags: zero before the first call; each call leaves them
+ *               consistent for the next (zeroing the whole region between
+ *               calls is also allowed, zeroing part of it is not).  The int
+ *               at byte 4 counts completed calls.  Calls that share a
+ *               workspace must not overlap in time.  If a wait ever gave up
+ *               (a GPU too busy to run the grid for about a second), the
+ *               int at byte 8 is set and the outputs are unspecified until
+ *               the region is zeroed.
+ */
+size_t moe_layer_one_token_workspace_bytes(int H, int I, int E, int k);
+size_t moe_layer_one_token_sync_bytes(int H);
+
+moe_status moe_layer_one_token(const uint16_t* x, const float* w_router, const float* bias,
+                               const uint8_t* w13_q, const uint8_t* w13_s,
+                               const uint8_t* w2_q, const uint8_t* w2_s,
+                               int H, int I, int E, int k,
+                               int32_t* topk_ids, float* topk_weights, double* logits,
+                               int32_t* expert_offsets, int32_t* sorted_ids,
+                               int32_t* tiles, int32_t* num_tiles,
+                               void* workspace, size_t workspace_bytes,
+                               uint16_t* out, struct ihipStream_t* stream);
+
 /* --------------------------------------------- the three steps of moe_forward
  * moe_forward is exactly these three calls in order; they are exported so a
  * caller can time or overlap them separately.  Arguments and constraints are

@@ -9,11 +9,14 @@ from .binding import (MoeError, LIB_PATH, load, version, status_string, pick_bm,
                       route_workspace_bytes, forward_workspace_bytes, moe_route,
                       moe_build_tiles, moe_forward, moe_gateup_swiglu, moe_down, moe_combine,
                       moe_route_tiles, route_tiles_ok, route_tiles_workspace_bytes,
-                      zeroed_route_tiles_workspace)
+                      zeroed_route_tiles_workspace, moe_layer_one_token,
+                      layer_one_token_workspace_bytes, layer_one_token_sync_bytes,
+                      zeroed_layer_one_token_workspace)
 from .layer import MoeLayer
 
 __all__ = ["MoeError", "LIB_PATH", "load", "version", "status_string", "pick_bm", "tiles_max",
            "route_workspace_bytes", "forward_workspace_bytes", "moe_route", "moe_build_tiles",
            "moe_forward", "moe_gateup_swiglu", "moe_down", "moe_combine", "moe_route_tiles",
            "route_tiles_ok", "route_tiles_workspace_bytes", "zeroed_route_tiles_workspace",
-           "MoeLayer"]
+           "moe_layer_one_token", "layer_one_token_workspace_bytes", "layer_one_token_sync_bytes",
+           "zeroed_layer_one_token_workspace", "MoeLayer"]

@@ -71,6 +71,13 @@ def load() -> ctypes.CDLL:
     lib.moe_down.restype = _i
     lib.moe_combine.argtypes = [_p, _p, _i, _i, _i, _p, _p]
     lib.moe_combine.restype = _i
+    lib.moe_layer_one_token_workspace_bytes.argtypes = [_i, _i, _i, _i]
+    lib.moe_layer_one_token_workspace_bytes.restype = _sz
+    lib.moe_layer_one_token_sync_bytes.argtypes = [_i]
+    lib.moe_layer_one_token_sync_bytes.restype = _sz
+    lib.moe_layer_one_token.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i,
+                                        _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p, _p]
+    lib.moe_layer_one_token.restype = _i
     _lib = lib
     return lib
 
@@ -202,6 +209,63 @@ def moe_route_tiles(x: torch.Tensor, w_router: torch.Tensor, bias: Optional[torc
                                   _ptr(tiles), _ptr(num_tiles), _ptr(workspace),
                                   workspace.numel(), _stream(dev)), "moe_route_tiles")
     return ids, wts, logits, offsets, sorted_ids, tiles, num_tiles
+
+
+def layer_one_token_workspace_bytes(H: int, I: int, E: int, k: int) -> int:
+    """Workspace bytes of moe_layer_one_token; 0 if the shape is not accepted."""
+    return int(load().moe_layer_one_token_workspace_bytes(H, I, E, k))
+
+
+def layer_one_token_sync_bytes(H: int) -> int:
+    """Bytes at the start of that workspace that must be zero before first use."""
+    return int(load().moe_layer_one_token_sync_bytes(H))
+
+
+def zeroed_layer_one_token_workspace(H: int, I: int, E: int, k: int, device) -> torch.Tensor:
+    """A workspace for moe_layer_one_token whose sync block starts at zero."""
+    return torch.zeros(max(layer_one_token_workspace_bytes(H, I, E, k), 256), dtype=torch.uint8,
+                       device=device)
+
+
+def moe_layer_one_token(x: torch.Tensor, w_router: torch.Tensor, bias: Optional[torch.Tensor],
+                        w13_q: torch.Tensor, w13_s: torch.Tensor, w2_q: torch.Tensor,
+                        w2_s: torch.Tensor, k: int, BM: int, want_logits: bool = False,
+                        workspace: Optional[torch.Tensor] = None,
+                        out: Optional[torch.Tensor] = None):
+    """The whole layer for one token in one launch.  Returns (out bf16 [1, H],
+    topk_ids, topk_weights, logits or None, expert_offsets, sorted_ids, tiles,
+    num_tiles), each equal to what moe_route_tiles + moe_forward produce."""
+    _need(x, "x", _BF16)
+    dev = x.device
+    _need(w_router, "w_router", (torch.float32,), dev)
+    if bias is not None:
+        _need(bias, "bias", (torch.float32,), dev)
+    for name, t in (("w13_q", w13_q), ("w13_s", w13_s), ("w2_q", w2_q), ("w2_s", w2_s)):
+        _need(t, name, _U8, dev)
+    T, H = x.shape
+    if T != 1:
+        raise ValueError("moe_layer_one_token takes exactly one token")
+    E, I2, _ = w13_q.shape
+    I = I2 // 2
+    ids = torch.empty((1, k), dtype=torch.int32, device=dev)
+    wts = torch.empty((1, k), dtype=torch.float32, device=dev)
+    logits = torch.empty((1, E), dtype=torch.float64, device=dev) if want_logits else None
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    sorted_ids = torch.empty(k, dtype=torch.int32, device=dev)
+    tiles = torch.empty((max(tiles_max(1, k, E, BM), 1), 3), dtype=torch.int32, device=dev)
+    num_tiles = torch.zeros(1, dtype=torch.int32, device=dev)
+    if out is None:
+        out = torch.empty((1, H), dtype=torch.bfloat16, device=dev)
+    _need(out, "out", _BF16, dev)
+    if workspace is None:
+        workspace = zeroed_layer_one_token_workspace(H, I, E, k, dev)
+    _check(load().moe_layer_one_token(_ptr(x), _ptr(w_router), _ptr(bias), _ptr(w13_q),
+                                      _ptr(w13_s), _ptr(w2_q), _ptr(w2_s), H, I, E, k, _ptr(ids),
+                                      _ptr(wts), _ptr(logits), _ptr(offsets), _ptr(sorted_ids),
+                                      _ptr(tiles), _ptr(num_tiles), _ptr(workspace),
+                                      workspace.numel(), _ptr(out), _stream(dev)),
+           "moe_layer_one_token")
+    return out, ids, wts, logits, offsets, sorted_ids, tiles, num_tiles
 
 
 def moe_build_tiles(topk_ids: torch.Tensor, E: int, BM: int):

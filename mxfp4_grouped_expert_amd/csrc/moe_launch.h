@@ -62,6 +62,20 @@ void launch_expert_mma(bool gateup, const uint16_t* act, const uint8_t* wq, cons
                        int tiles_max, int T, int H, int I, int E, int k, void* out,
                        hipStream_t stream);
 
+// The whole layer for one token in one launch (routing, gate/up, down and
+// combine; bit-identical to the separate launches).  The workspace starts
+// with a sync block of layer_one_token_sync_bytes(H) bytes that must be zero
+// before first use and is left zero by every call.
+bool layer_one_token_ok(int H, int I, int E, int k);
+size_t layer_one_token_sync_bytes(int H);
+size_t layer_one_token_bytes(int H, int I, int E, int k);
+void launch_layer_one_token(const uint16_t* x, const float* w_router, const float* bias,
+                            const uint8_t* w13_q, const uint8_t* w13_s, const uint8_t* w2_q,
+                            const uint8_t* w2_s, int H, int I, int E, int k, int32_t* topk_ids,
+                            float* topk_weights, double* logits, int32_t* expert_offsets,
+                            int32_t* sorted_ids, int32_t* tiles, int32_t* num_tiles,
+                            void* workspace, uint16_t* out, hipStream_t stream);
+
 // Weighted combine back to token order.
 void launch_combine(const float* y, const float* topk_weights, int T, int H, int k,
                     uint16_t* out, hipStream_t stream);

@@ -1,0 +1,574 @@
+// The whole MoE layer for one token in a single launch: router logits,
+// top-k, softmax and tile table, the grouped gate/up GEMM with SwiGLU, the
+// grouped down GEMM and the weighted combine.
+//
+// The SimpleLLM write-up ("A 297-line kernel file that decodes faster than
+// vLLM", section "Where the time went") books launch and host gaps as their
+// own row of a decode step.  With one token each step is short, so the gaps
+// between dependent launches and the time each launch takes to fill the GPU
+// with workgroups are a large share of the layer.  Here one grid holds all
+// of it, every workgroup resident from the start:
+//   routing   splits x ceil(E/16) workgroups compute fp64 partial logits (as
+//             router_decode_fused does); the last to finish sums them, runs
+//             the wave top-k and softmax, publishes the plan (expert and
+//             slot of each sorted position, weight of each slot), then
+//             writes the routing outputs and the tile table for the caller.
+//   GEMM      workgroup j runs gate/up job j (tile g = j / (I/16), 16-row
+//             block j % (I/16)) with exactly the arithmetic of the one-token
+//             gate/up kernel (expert_gemm_kernel<gate/up, 1, 1>), then the
+//             down job(s) of the tile t with (t+1) * I/16 <= j <
+//             (t+1) * I/16 + H/16 with exactly the arithmetic of the
+//             one-token down kernel.  The last tile's down job of each
+//             16-row block also combines the block's k slots in ascending
+//             slot order, as combine_kernel does.
+// Every value is therefore bit-identical to moe_route_tiles + moe_forward.
+//
+// Handshakes.  A workgroup only ever waits for data produced by workgroups
+// with a lower index (a tile's gate/up jobs sit below its down jobs, the
+// other tiles' down jobs below the combining one), and workgroups are
+// dispatched in index order, so no wait can deadlock however few
+// workgroups fit on the GPU at once.  Each value that crosses workgroups
+// (plan entries, routing weights, h pairs, y values) travels in one 64-bit
+// word together with a stamp, the call's epoch + 1, written and read with
+// agent-scope atomics (coherent across the XCDs' L2 caches); a consumer
+// polls the words it needs until their stamps match, so no producer waits
+// for its stores to complete and no counter sits on the critical path.
+// The routing partials use the ticket pattern of router_decode_fused.  The
+// epoch is read by every workgroup at its start and advanced by the last
+// of them to check in (a two-level arrival tree), so each call sees its own
+// value.  Polls are bounded: one that gives up sets the error word and its
+// workgroup carries on with whatever it read (the launch still ends).
+//
+// Contention.  Atomics and polls on one address are serialised by the
+// memory system, so hot words have their own 128-byte lines: the plan is
+// written to 16 replica lines (workgroup i reads replica i % 16) and the
+// arrival tree spreads its counters over 16 leaf lines and a top line.
+#include "expert_common.h"
+#include "moe_device.h"
+#include "moe_launch.h"
+#include "router_body.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kThreads = 256;           // every role: 4 waves
+constexpr int kSpinLimit = 1 << 20;     // polls (about 1 us each) before a wait gives up
+constexpr int kMaxK = 3072;             // K of either GEMM: one chunk of weights
+constexpr int kActRegion = (kMaxK * 2 + 16 + 1023) / 1024 * 1024;  // staged row + pad
+constexpr int kRedBytes = 4 * 2 * 256 * 4;  // split-K table of the gate/up job
+constexpr int kRegion0 = kActRegion > kRedBytes ? kActRegion : kRedBytes;
+
+typedef unsigned long long u64;
+
+// The sync region at the start of the workspace, in 128-byte lines (zero
+// before the first call; afterwards each call leaves it consistent).
+constexpr int kLine = 32;      // ints per line
+constexpr int kReplicas = 16;  // plan replicas
+constexpr int kLeaves = 16;    // leaves of the arrival tree
+struct Tree {
+  int leaf[kLeaves][kLine];
+  int top[kLine];
+};
+struct ReplicaLine {
+  u64 plan[kMaxTopk];    // sorted position g: stamp | slot << 16 | expert
+  u64 weight[kMaxTopk];  // slot j: stamp | routing weight bits
+};
+struct Sync {
+  int router_ticket;     // routing workgroups finished (the last resets it)
+  int epoch;             // calls begun by every workgroup
+  int error;             // set (sticky) when a poll gives up
+  int pad0[kLine - 3];
+  Tree arrivals;         // every workgroup, once it has read the epoch
+  ReplicaLine rep[kReplicas];
+};
+static_assert(sizeof(ReplicaLine) == 128, "one line per replica");
+static_assert(sizeof(Sync) % 128 == 0, "whole lines");
+
+__device__ __forceinline__ int ld_agent(const int* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(int* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int add_agent(int* p, int v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ u64 ld64(const u64* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st64(u64* p, unsigned stamp, unsigned payload) {
+  __hip_atomic_store(p, ((u64)stamp << 32) | payload, __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Reads the N stamped words p[i] (those with use[i]) until every stamp is
+// this call's, in rounds: each round requests all words still stale at
+// once, so once the producers are done one round trip suffices.  Returns
+// the payloads in v's low halves.
+template <int N>
+__device__ __forceinline__ void settle(const u64* const (&p)[N], const bool (&use)[N], u64 (&v)[N],
+                                       unsigned stamp, int* error) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = use[i] ? ld64(p[i]) : ((u64)stamp << 32);
+  for (int round = 0;; ++round) {
+    bool stale = false;
+#pragma unroll
+    for (int i = 0; i < N; ++i) stale |= (unsigned)(v[i] >> 32) != stamp;
+    if (!stale) return;
+    if (round == kSpinLimit) {
+      st_agent(error, 1);
+      return;
+    }
+    __builtin_amdgcn_s_sleep(8);  // about 0.2 us: a poll is itself a memory round trip
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      if ((unsigned)(v[i] >> 32) != stamp) v[i] = ld64(p[i]);
+  }
+}
+
+// Arrival i of n at the tree (one thread).  True for exactly one arrival,
+// the last; every counter touched is reset by its last arrival.
+__device__ bool tree_arrive(Tree* t, int i, int n) {
+  const int leaf = i % kLeaves;
+  const int per_leaf = n / kLeaves + (leaf < n % kLeaves ? 1 : 0);
+  if (add_agent(&t->leaf[leaf][0], 1) != per_leaf - 1) return false;
+  st_agent(&t->leaf[leaf][0], 0);
+  const int leaves = n < kLeaves ? n : kLeaves;
+  if (add_agent(&t->top[0], 1) != leaves - 1) return false;
+  st_agent(&t->top[0], 0);
+  return true;
+}
+
+// This workgroup has read `epoch`; the last of the call to check in
+// advances it for the next call.
+__device__ void check_in(Sync* S, int epoch) {
+  if (tree_arrive(&S->arrivals, blockIdx.x, gridDim.x)) st_agent(&S->epoch, epoch + 1);
+}
+
+struct Args {
+  const uint16_t* x;
+  const float* w_router;
+  const float* bias;
+  const uint8_t* w13_q;
+  const uint8_t* w13_s;
+  const uint8_t* w2_q;
+  const uint8_t* w2_s;
+  int H, I, E, k;
+  int split_len, splits, n_route;
+  int32_t* topk_ids;
+  float* topk_weights;
+  double* logits;
+  int32_t* expert_offsets;
+  int32_t* sorted_ids;
+  int32_t* tiles;
+  int32_t* num_tiles;
+  Sync* sync;
+  double* partial;  // [splits][E]
+  u64* h;           // [k][I/2] stamped bf16 pairs
+  u64* y;           // [k][H] stamped fp32
+  uint16_t* out;
+};
+
+// ---------------------------------------------------------------- routing
+__device__ void routing_role(const Args& a, int rid, unsigned char* lds) {
+  const int epoch = ld_agent(&a.sync->epoch);
+  const unsigned stamp = (unsigned)epoch + 1u;
+  const int eb = (a.E + kExpPerBlock - 1) / kExpPerBlock;
+  logits_partial_body<true, 1>(a.x, a.w_router, 1, a.H, a.E, a.split_len, a.partial, 0, rid % eb,
+                               rid / eb);
+  __builtin_amdgcn_s_waitcnt(0);  // this workgroup's partials are stored
+  __syncthreads();
+  int* s_last = reinterpret_cast<int*>(lds);
+  int* s_ids = s_last + 4;
+  float* s_w = reinterpret_cast<float*>(s_ids + kMaxTopk);
+  if (threadIdx.x == 0) {
+    *s_last = add_agent(&a.sync->router_ticket, 1) == a.n_route - 1;
+    check_in(a.sync, epoch);
+  }
+  __syncthreads();
+  if (!*s_last || threadIdx.x >= kWave) return;  // one wave finishes the token
+  const int lane = threadIdx.x;
+  double val[4];
+  one_token_logits(a.partial, a.bias, a.E, a.splits, val);
+  // top-k and softmax into LDS only: the plan goes out first, the routing
+  // outputs for the caller (identical values) after it
+  topk_softmax_wave(val, a.E, a.k, 0, nullptr, nullptr, s_ids, s_w);
+  wave_lds_sync();
+  // lane (r, j) writes slot j's entries of replica r, 8 replicas per pass
+  for (int r0 = 0; r0 < kReplicas; r0 += kWave / kMaxTopk) {
+    const int r = r0 + lane / kMaxTopk, j = lane % kMaxTopk;
+    if (j < a.k) {
+      const int e = s_ids[j];
+      int pos = 0;  // sorted position of slot j: selected experts below e
+      for (int q = 0; q < a.k; ++q) pos += s_ids[q] < e;
+      ReplicaLine* L = &a.sync->rep[r];
+      st64(&L->plan[pos], stamp, ((unsigned)j << 16) | (unsigned)e);
+      st64(&L->weight[j], stamp, __float_as_uint(s_w[j]));
+    }
+  }
+  if (lane == 0) st_agent(&a.sync->router_ticket, 0);
+  if (a.logits)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (lane + kWave * i < a.E) a.logits[lane + kWave * i] = val[i];
+  if (lane < a.k) {
+    a.topk_ids[lane] = s_ids[lane];
+    a.topk_weights[lane] = s_w[lane];
+  }
+  one_token_tables(a.E, a.k, s_ids, a.expert_offsets, a.sorted_ids, a.tiles, a.num_tiles);
+}
+
+// ----------------------------------------------------------------- gate/up
+// Tile g (sorted position g, one row), 16-row block cb of the gate and up
+// halves.  Same lane roles, loads, exchange, MFMA order, split-K order and
+// epilogue as expert_gemm_kernel<true, 1, 1, true> for one token.
+struct GateupLoads {
+  uint4 w[kChunk][2];  // this lane's weight pieces, per step and half
+  uint4 spiece;        // this thread's piece of the two scale runs
+};
+
+__device__ __forceinline__ void gateup_issue(const Args& a, int cb, int e, unsigned char* act,
+                                             GateupLoads& L) {
+  const int I = a.I, K = a.H, KB = K / 32;
+  const int tid = threadIdx.x, lane = tid & 63, kq = tid >> 6;
+  const int n_base = cb * kRowsPerBlock;
+  // activations (token 0) first, then the scale piece, then the weights
+  const int cpr = K / 8, spr = cpr + 1;
+  for (int ins = kq; ins < (spr + 63) / 64; ins += 4) {
+    const int c = min(ins * 64 + lane, cpr - 1);
+    __builtin_amdgcn_global_load_lds(a.x + (size_t)c * 8,
+                                     (__attribute__((address_space(3))) void*)(act + ins * 1024),
+                                     16, 0, 0);
+  }
+  const int pr = min(tid / KB, 1), pp = tid - pr * KB;
+  L.spiece = *reinterpret_cast<const uint4*>(
+      a.w13_s + ((size_t)e * 2 * I + (size_t)pr * I + n_base) * KB + (size_t)min(pp, KB - 1) * 16);
+  asm volatile("" ::: "memory");
+  const int l_row = n_base + 4 * kq + (lane >> 4);
+  const size_t wrow[2] = {(size_t)e * 2 * I + l_row, (size_t)e * 2 * I + I + l_row};
+#pragma unroll
+  for (int c = 0; c < kChunk; ++c) {
+    const int bc = min(c * kBlocksPerStep + (lane & 15), KB - 1);
+#pragma unroll
+    for (int w = 0; w < 2; ++w)
+      L.w[c][w] = *reinterpret_cast<const uint4*>(a.w13_q + wrow[w] * (K / 2) + (size_t)bc * 16);
+  }
+}
+
+__device__ __forceinline__ void gateup_finish(const Args& a, int g, int cb, unsigned stamp,
+                                              unsigned char* lds, GateupLoads& L) {
+  constexpr int NW = 2;
+  const int I = a.I, K = a.H, KB = K / 32;
+  const int n_base = cb * kRowsPerBlock;
+  const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, grp = lane >> 4;
+  const int kq = tid >> 6;
+  unsigned char* act = lds;                          // x row, then the split-K table
+  unsigned char* s_sc = lds + kRegion0;              // 2 scale runs
+  unsigned char* s_ring = s_sc + NW * kScaleRunMax;  // 2 exchange slots
+
+  wait_vmcnt<kChunk * NW>();  // activations and the scale piece
+  const int pr = min(tid / KB, NW - 1), pp = tid - pr * KB;
+  if (tid < NW * KB) *reinterpret_cast<uint4*>(s_sc + pr * kScaleRunMax + pp * 16) = L.spiece;
+  lds_barrier();
+
+  uint32_t sreg[kChunk][NW];
+#pragma unroll
+  for (int c = 0; c < kChunk; ++c) {
+    const int bc = min(c * kBlocksPerStep + kq * 4 + grp, KB - 1);
+#pragma unroll
+    for (int w = 0; w < NW; ++w) sreg[c][w] = s_sc[w * kScaleRunMax + li * KB + bc];
+  }
+  floatx4 acc[NW] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int c = 0; c < kChunk; ++c) {
+    unsigned char* slot = s_ring + (c & 1) * NW * kRowsPerBlock * 256;
+    const int wr16 = 4 * kq + (lane >> 4);
+#pragma unroll
+    for (int w = 0; w < NW; ++w)
+      *reinterpret_cast<uint4*>(slot + (w * kRowsPerBlock + wr16) * 256 +
+                                (((lane & 15) ^ wr16) << 4)) = L.w[c][w];
+    lds_barrier();
+#pragma unroll
+    for (int w = 0; w < NW; ++w)
+      L.w[c][w] = *reinterpret_cast<const uint4*>(
+          slot + (w * kRowsPerBlock + li) * 256 + (((4 * kq + grp) ^ li) << 4));
+#pragma unroll
+    for (int w = 0; w < NW; ++w)
+      asm volatile("" : "+v"(L.w[c][w].x), "+v"(L.w[c][w].y), "+v"(L.w[c][w].z),
+                   "+v"(L.w[c][w].w), "+v"(sreg[c][w]));
+    const int b = c * kBlocksPerStep + kq * 4 + grp;
+    const int bc = min(b, KB - 1);
+    float scale[NW];
+#pragma unroll
+    for (int w = 0; w < NW; ++w) scale[w] = b < KB ? e8m0_to_float(sreg[c][w]) : 0.f;
+    const uint4* ap = reinterpret_cast<const uint4*>(act + bc * 64);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bf16x8 av = as_bf16x8(ap[j]);
+#pragma unroll
+      for (int w = 0; w < NW; ++w)
+        acc[w] = mfma16x16x32(av, dequant8_bf16(word(L.w[c][w], j), scale[w]), acc[w]);
+    }
+  }
+
+  // split-K sum in wave order, then SwiGLU of row 0 (the token)
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(act);
+#pragma unroll
+  for (int w = 0; w < NW; ++w)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      red[(kq * NW + w) * 256 + (4 * grp + r) * kRowsPerBlock + li] = acc[w][r];
+  __syncthreads();
+  float v[NW];
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    v[w] = red[(0 * NW + w) * 256 + tid];
+#pragma unroll
+    for (int q = 1; q < 4; ++q) v[w] += red[(q * NW + w) * 256 + tid];
+  }
+  const uint32_t hv = float_to_bf16(silu(v[0]) * v[NW - 1]);
+  const uint32_t hn = (uint32_t)__float_as_int(swap_pair(__int_as_float((int)hv)));
+  if (tid < kRowsPerBlock && (tid & 1) == 0)  // one stamped word per bf16 pair
+    st64(a.h + ((size_t)g * I + n_base + tid) / 2, stamp, hv | (hn << 16));
+}
+
+// -------------------------------------------------------------------- down
+// Tile g, 16-row block cb of w2: the arithmetic of expert_gemm_kernel<false,
+// 1, 1, true> for one token.  The last tile's job also combines the block.
+struct DownLoads {
+  uint4 w[kChunk];
+  uint4 spiece;
+};
+
+__device__ __forceinline__ void down_issue(const Args& a, int cb, int e, DownLoads& L) {
+  const int K = a.I, KB = K / 32;
+  const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, grp = lane >> 4;
+  const int kq = tid >> 6;
+  const int n_base = cb * kRowsPerBlock;
+  const size_t wrow = (size_t)e * a.H + n_base + li;
+#pragma unroll
+  for (int c = 0; c < kChunk; ++c) {
+    const int bc = min(c * kBlocksPerStep + kq * 4 + grp, KB - 1);
+    L.w[c] = *reinterpret_cast<const uint4*>(a.w2_q + wrow * (K / 2) + (size_t)bc * 16);
+  }
+  L.spiece = *reinterpret_cast<const uint4*>(
+      a.w2_s + ((size_t)e * a.H + n_base) * KB + (size_t)min(tid, KB - 1) * 16);
+}
+
+__device__ __forceinline__ void down_finish(const Args& a, int g, int cb, int slot,
+                                            unsigned stamp, const ReplicaLine* R,
+                                            unsigned char* lds, DownLoads& L) {
+  const int H = a.H, I = a.I, K = I, KB = K / 32;
+  const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, grp = lane >> 4;
+  const int kq = tid >> 6;
+  const int n_base = cb * kRowsPerBlock;
+  unsigned char* act = lds;                          // h row
+  unsigned char* s_sc = lds + kRegion0;              // scale run
+  float* red = reinterpret_cast<float*>(s_sc + kScaleRunMax);
+
+  __syncthreads();  // the LDS of any earlier job is free
+  // h row g into LDS as its stamped pairs arrive (16-byte slots, the pad
+  // slot repeating the last chunk): every word of this thread requested at
+  // once, then re-polled only where the stamp is not yet this call's
+  {
+    constexpr int kPer = ((kMaxK / 8 + 1) * 4 + kThreads - 1) / kThreads;
+    const int cpr = K / 8, spr = cpr + 1;
+    const u64* hrow = a.h + (size_t)g * I / 2;
+    unsigned* dst = reinterpret_cast<unsigned*>(act);
+    const u64* src[kPer];
+    bool use[kPer];
+    u64 v[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int d = tid + i * kThreads;
+      use[i] = d < spr * 4;
+      src[i] = hrow + min(min(d, spr * 4 - 1) >> 2, cpr - 1) * 4 + (d & 3);
+    }
+    settle(src, use, v, stamp, &a.sync->error);
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+      if (use[i]) dst[tid + i * kThreads] = (unsigned)v[i];
+  }
+  if (tid < KB) *reinterpret_cast<uint4*>(s_sc + tid * 16) = L.spiece;
+  __syncthreads();
+
+  uint32_t sreg[kChunk];
+#pragma unroll
+  for (int c = 0; c < kChunk; ++c)
+    sreg[c] = s_sc[li * KB + min(c * kBlocksPerStep + kq * 4 + grp, KB - 1)];
+  floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < kChunk; ++c) {
+    asm volatile("" : "+v"(L.w[c].x), "+v"(L.w[c].y), "+v"(L.w[c].z), "+v"(L.w[c].w),
+                 "+v"(sreg[c]));
+    const int b = c * kBlocksPerStep + kq * 4 + grp;
+    const float scale = b < KB ? e8m0_to_float(sreg[c]) : 0.f;
+    const uint4* ap = reinterpret_cast<const uint4*>(act + min(b, KB - 1) * 64);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc = mfma16x16x32(as_bf16x8(ap[j]), dequant8_bf16(word(L.w[c], j), scale), acc);
+  }
+  if (grp == 0) red[kq * kRowsPerBlock + li] = acc[0];  // row 0: the token
+  __syncthreads();
+  if (tid >= kRowsPerBlock) return;  // no barrier below
+  float yv = red[tid];
+#pragma unroll
+  for (int q = 1; q < 4; ++q) yv += red[q * kRowsPerBlock + tid];
+  if (g != a.k - 1) {
+    st64(a.y + (size_t)slot * H + n_base + tid, stamp, __float_as_uint(yv));
+    return;
+  }
+  // the last tile's job combines the block: the other slots' y as their
+  // stamped words arrive, then fma in ascending slot order
+  const u64* src[2 * kMaxTopk];
+  bool use[2 * kMaxTopk];
+  u64 v[2 * kMaxTopk];
+#pragma unroll
+  for (int j = 0; j < kMaxTopk; ++j) {
+    const int jc = min(j, a.k - 1);
+    src[j] = &R->weight[jc];
+    use[j] = j < a.k;
+    src[kMaxTopk + j] = a.y + (size_t)jc * H + n_base + tid;
+    use[kMaxTopk + j] = j < a.k && j != slot;
+  }
+  settle(src, use, v, stamp, &a.sync->error);
+  float wj[kMaxTopk], yj[kMaxTopk];
+#pragma unroll
+  for (int j = 0; j < kMaxTopk; ++j) {
+    wj[j] = __uint_as_float((unsigned)v[j]);
+    yj[j] = j == slot ? yv : __uint_as_float((unsigned)v[kMaxTopk + j]);
+  }
+  float acc_o = 0.f;
+#pragma unroll
+  for (int j = 0; j < kMaxTopk; ++j)
+    if (j < a.k) acc_o = fmaf(wj[j], yj[j], acc_o);
+  a.out[n_base + tid] = float_to_bf16(acc_o);
+}
+
+// ------------------------------------------------------- GEMM workgroups
+// Workgroup j (after the routing ones) runs gate/up job j when j < k * I/16,
+// then the down jobs of every tile t with (t+1) * I/16 <= j <
+// (t+1) * I/16 + H/16 (block j - (t+1) * I/16): a tile's down jobs sit above
+// all of its gate/up jobs, and the last tile's down job of a block above the
+// other tiles' jobs of that block.  A down job's weights are requested once
+// the workgroup's gate/up job is done (requested together, the two streams
+// measured slower).
+__device__ void gemm_role(const Args& a, int j, unsigned char* lds) {
+  const int ncbI = a.I / kRowsPerBlock, ncbH = a.H / kRowsPerBlock;
+  unsigned* s_plan = reinterpret_cast<unsigned*>(lds + kRegion0 + 2 * kScaleRunMax +
+                                                 2 * 2 * kRowsPerBlock * 256);
+  const bool has_gu = j < a.k * ncbI;
+  const int g_gu = min(j / ncbI, a.k - 1);
+  int t0 = a.k;  // first tile with a down job here
+  for (int t = a.k - 1; t >= 0; --t)
+    if (j >= (t + 1) * ncbI && j < (t + 1) * ncbI + ncbH) t0 = t;
+
+  const int epoch = ld_agent(&a.sync->epoch);
+  const unsigned stamp = (unsigned)epoch + 1u;
+  const ReplicaLine* R = &a.sync->rep[blockIdx.x % kReplicas];
+  if (threadIdx.x == 0) {
+    check_in(a.sync, epoch);
+    const u64* src[2] = {&R->plan[g_gu], &R->plan[min(t0, a.k - 1)]};
+    const bool use[2] = {true, true};
+    u64 v[2];
+    settle(src, use, v, stamp, &a.sync->error);
+    s_plan[0] = (unsigned)v[0];
+    s_plan[1] = (unsigned)v[1];
+  }
+  __syncthreads();
+  // clamped: the indices stay in bounds whatever the words hold
+  auto expert = [&](unsigned p) { return min((int)(p & 0xffffu), a.E - 1); };
+  auto slot_of = [&](unsigned p) { return min((int)(p >> 16), a.k - 1); };
+  const unsigned p_gu = s_plan[0], p_d0 = s_plan[1];
+
+  if (has_gu) {
+    GateupLoads gl;
+    gateup_issue(a, j - g_gu * ncbI, expert(p_gu), lds, gl);
+    gateup_finish(a, g_gu, j - g_gu * ncbI, stamp, lds, gl);
+  }
+  for (int t = t0; t < a.k; ++t) {
+    const int cb = j - (t + 1) * ncbI;
+    if (cb < 0 || cb >= ncbH) continue;
+    unsigned p = p_d0;
+    if (t != t0) {  // only when H/16 > I/16
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        const u64* src[1] = {&R->plan[t]};
+        const bool use[1] = {true};
+        u64 v[1];
+        settle(src, use, v, stamp, &a.sync->error);
+        s_plan[2] = (unsigned)v[0];
+      }
+      __syncthreads();
+      p = s_plan[2];
+    }
+    DownLoads dl;
+    down_issue(a, cb, expert(p), dl);
+    down_finish(a, t, cb, slot_of(p), stamp, R, lds, dl);
+  }
+}
+
+constexpr int kLdsBytes = kRegion0 + 2 * kScaleRunMax + 2 * 2 * kRowsPerBlock * 256 + 16;
+
+__global__ __launch_bounds__(kThreads, 4) void moe_layer_one_token_kernel(Args a) {
+  __shared__ __align__(16) unsigned char lds[kLdsBytes];
+  if ((int)blockIdx.x < a.n_route)
+    routing_role(a, blockIdx.x, lds);
+  else
+    gemm_role(a, blockIdx.x - a.n_route, lds);
+}
+
+size_t round_up(size_t n) { return (n + 255) / 256 * 256; }
+
+}  // namespace
+
+bool layer_one_token_ok(int H, int I, int E, int k) {
+  return H % 32 == 0 && I % 32 == 0 && H <= kMaxK && I <= kMaxK && E >= 1 &&
+         E <= kMaxExperts && k >= 1 && k <= kMaxTopk && k <= E;
+}
+
+size_t layer_one_token_sync_bytes(int H) {
+  (void)H;
+  return round_up(sizeof(Sync));
+}
+
+size_t layer_one_token_bytes(int H, int I, int E, int k) {
+  const RouterPlan p = router_plan(1, H, E);
+  return layer_one_token_sync_bytes(H) + round_up((size_t)p.splits * E * sizeof(double)) +
+         round_up((size_t)k * (I / 2) * sizeof(u64)) + round_up((size_t)k * H * sizeof(u64));
+}
+
+void launch_layer_one_token(const uint16_t* x, const float* w_router, const float* bias,
+                            const uint8_t* w13_q, const uint8_t* w13_s, const uint8_t* w2_q,
+                            const uint8_t* w2_s, int H, int I, int E, int k, int32_t* topk_ids,
+                            float* topk_weights, double* logits, int32_t* expert_offsets,
+                            int32_t* sorted_ids, int32_t* tiles, int32_t* num_tiles,
+                            void* workspace, uint16_t* out, hipStream_t stream) {
+  const RouterPlan p = router_plan(1, H, E);
+  char* ws = static_cast<char*>(workspace);
+  Args a;
+  a.x = x; a.w_router = w_router; a.bias = bias;
+  a.w13_q = w13_q; a.w13_s = w13_s; a.w2_q = w2_q; a.w2_s = w2_s;
+  a.H = H; a.I = I; a.E = E; a.k = k;
+  a.split_len = p.split_len;
+  a.splits = p.splits;
+  a.n_route = p.splits * ((E + kExpPerBlock - 1) / kExpPerBlock);
+  a.topk_ids = topk_ids; a.topk_weights = topk_weights; a.logits = logits;
+  a.expert_offsets = expert_offsets; a.sorted_ids = sorted_ids; a.tiles = tiles;
+  a.num_tiles = num_tiles;
+  a.sync = reinterpret_cast<Sync*>(ws);
+  size_t off = layer_one_token_sync_bytes(H);
+  a.partial = reinterpret_cast<double*>(ws + off);
+  off += round_up((size_t)p.splits * E * sizeof(double));
+  a.h = reinterpret_cast<u64*>(ws + off);
+  off += round_up((size_t)k * (I / 2) * sizeof(u64));
+  a.y = reinterpret_cast<u64*>(ws + off);
+  a.out = out;
+  const int ncbI = I / kRowsPerBlock, ncbH = H / kRowsPerBlock;
+  const int grid = a.n_route + k * ncbI + ncbH;
+  hipLaunchKernelGGL(moe_layer_one_token_kernel, dim3(grid), dim3(kThreads), 0, stream, a);
+}
+
+}  // namespace moe

@@ -21,96 +21,16 @@
 //   2. router_topk_softmax: one wave per token sums the K-range partials in
 //      a fixed order (deterministic), adds the bias, and runs k rounds of a
 //      wave-wide argmax on a total order (higher logit first, then lower
-//      expert index); lane 0 takes the softmax of the k winners in fp64.
+//      expert index); the softmax of the k winners is taken in fp64.
+// The device code of both steps lives in router_body.h.
 #include "moe_device.h"
 #include "moe_launch.h"
+#include "router_body.h"
 #include "tiles_block.h"
 
 namespace moe {
 
 namespace {
-
-constexpr int kTokPerWave = 4;
-constexpr int kExpPerWave = 4;
-constexpr int kWavesPerBlock = 4;
-constexpr int kExpPerBlock = kExpPerWave * kWavesPerBlock;
-
-// One workgroup's share of the partial logits: tokens [TPW*bx, +TPW), experts
-// [16*by, +16) (4 per wave), K-range bz.  ATOMIC_OUT stores with agent-scope
-// atomics so another workgroup of the same launch may read them.
-template <bool ATOMIC_OUT, int TPW = kTokPerWave>
-__device__ void logits_partial_body(const uint16_t* __restrict__ x,
-                                    const float* __restrict__ w_router, int T, int H, int E,
-                                    int split_len, double* __restrict__ partial, int bx, int by,
-                                    int bz) {
-  const int wave = (threadIdx.x >> 6) & 3;  // wave within this 256-thread expert block
-  const int lane = threadIdx.x & 63;
-  const int t0 = bx * TPW;
-  const int e0 = by * kExpPerBlock + wave * kExpPerWave;
-  const int s = bz;
-  if (e0 >= E) return;  // wave-uniform; no barrier in this body
-  const int kbeg = s * split_len;
-  const int kend = min(H, kbeg + split_len);
-
-  const uint16_t* xr[TPW];
-#pragma unroll
-  for (int t = 0; t < TPW; ++t) xr[t] = x + (size_t)min(t0 + t, T - 1) * H;
-  const float* wr[kExpPerWave];
-#pragma unroll
-  for (int e = 0; e < kExpPerWave; ++e) wr[e] = w_router + (size_t)min(e0 + e, E - 1) * H;
-
-  double acc[TPW][kExpPerWave];
-#pragma unroll
-  for (int t = 0; t < TPW; ++t)
-#pragma unroll
-    for (int e = 0; e < kExpPerWave; ++e) acc[t][e] = 0.0;
-
-  // The wave's 4x4 router weights of a K step stay in registers while each
-  // token's 4 activations stream past (each accumulator sees the same FMA
-  // sequence whatever TPW is).
-  for (int kk = kbeg + 4 * lane; kk < kend; kk += 4 * kWave) {
-    double wv[kExpPerWave][4];
-#pragma unroll
-    for (int e = 0; e < kExpPerWave; ++e) {
-      const float4 w = *reinterpret_cast<const float4*>(wr[e] + kk);
-      wv[e][0] = w.x; wv[e][1] = w.y; wv[e][2] = w.z; wv[e][3] = w.w;
-    }
-#pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-      const uint2 v = *reinterpret_cast<const uint2*>(xr[t] + kk);
-      const double x0 = (double)bf16_to_float(v.x & 0xffffu);
-      const double x1 = (double)bf16_to_float(v.x >> 16);
-      const double x2 = (double)bf16_to_float(v.y & 0xffffu);
-      const double x3 = (double)bf16_to_float(v.y >> 16);
-#pragma unroll
-      for (int e = 0; e < kExpPerWave; ++e) {
-        double a = acc[t][e];
-        a = fma(x0, wv[e][0], a);
-        a = fma(x1, wv[e][1], a);
-        a = fma(x2, wv[e][2], a);
-        a = fma(x3, wv[e][3], a);
-        acc[t][e] = a;
-      }
-    }
-  }
-
-#pragma unroll
-  for (int t = 0; t < TPW; ++t) {
-#pragma unroll
-    for (int e = 0; e < kExpPerWave; ++e) {
-      double v = acc[t][e];
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-      if (lane == 0 && t0 + t < T && e0 + e < E) {
-        double* dst = &partial[((size_t)s * T + (t0 + t)) * E + (e0 + e)];
-        if (ATOMIC_OUT)
-          __hip_atomic_store(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        else
-          *dst = v;
-      }
-    }
-  }
-}
 
 template <int TPW>
 __global__ __launch_bounds__(256) void router_logits_partial(
@@ -212,134 +132,6 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void router_logits_mfma(
   }
 }
 
-// Total order on doubles as int64 (larger key = larger value); -0 is folded
-// into +0 so the two compare equal, and NaN sorts below everything.
-__device__ __forceinline__ long long order_key(double v) {
-  v = v + 0.0;
-  if (v != v) return LLONG_MIN + 1;
-  long long b = __double_as_longlong(v);
-  return b >= 0 ? b : (b ^ 0x7fffffffffffffffLL);
-}
-
-__device__ __forceinline__ double readlane_f64(double v, int l) {
-  const long long b = __double_as_longlong(v);
-  const int lo = __builtin_amdgcn_readlane((int)(b & 0xffffffffLL), l);
-  const int hi = __builtin_amdgcn_readlane((int)(b >> 32), l);
-  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
-}
-
-__device__ __forceinline__ long long readlane_i64(long long v, int l) {
-  const int lo = __builtin_amdgcn_readlane((int)(v & 0xffffffffLL), l);
-  const int hi = __builtin_amdgcn_readlane((int)(v >> 32), l);
-  return ((long long)hi << 32) | (unsigned int)lo;
-}
-
-// Waits until this wave's LDS writes have completed, so its later reads (of
-// other lanes' entries) see them; the memory clobber keeps the compiler from
-// moving LDS accesses across.
-__device__ __forceinline__ void wave_lds_sync() {
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-}
-
-// max(v, v of the lane DPP control CTRL selects); lanes without a source
-// keep v
-template <int CTRL>
-__device__ __forceinline__ long long dpp_max_i64(long long v) {
-  const int lo = __builtin_amdgcn_update_dpp((int)(v & 0xffffffffLL), (int)(v & 0xffffffffLL),
-                                             CTRL, 0xF, 0xF, false);
-  const int hi = __builtin_amdgcn_update_dpp((int)(v >> 32), (int)(v >> 32), CTRL, 0xF, 0xF,
-                                             false);
-  const long long o = ((long long)hi << 32) | (unsigned int)lo;
-  return o > v ? o : v;
-}
-
-// Largest 64-bit key of the wave, the same value in every lane: the maximum
-// within each quad, then within each row of 16 (DPP), then over the 4 rows.
-__device__ __forceinline__ long long wave_max_i64(long long v) {
-  v = dpp_max_i64<0xB1>(v);   // quad_perm [1,0,3,2]
-  v = dpp_max_i64<0x4E>(v);   // quad_perm [2,3,0,1]
-  v = dpp_max_i64<0x124>(v);  // row_ror:4
-  v = dpp_max_i64<0x128>(v);  // row_ror:8
-  long long m = readlane_i64(v, 0);
-#pragma unroll
-  for (int r = 1; r < 4; ++r) {
-    const long long o = readlane_i64(v, 16 * r);
-    m = o > m ? o : m;
-  }
-  return m;
-}
-
-// Top-k and softmax of one token by one wave.  Lane l holds the logits of
-// experts l, l+64, l+128, l+192 in val[] (entries >= E are ignored).  k
-// rounds of a wave-wide argmax on (higher logit, then lower expert index):
-// each round takes the largest order key, then the lowest expert holding it
-// (one ballot per slot), and retires that expert.  The softmax over the
-// winners is computed in fp64 as one formula: m = their maximum,
-// z_j = exp(v_j - m) with lane j taking z_j, the sum of z_0..z_{k-1} in
-// ascending j, w_j = z_j / sum, so the weights do not depend on which lane
-// computed which term.  Writes ids and weights (and, if ids_lds is given,
-// the ids there too).
-__device__ void topk_softmax_wave(const double (&val)[4], int E, int k, int t,
-                                  int32_t* __restrict__ topk_ids,
-                                  float* __restrict__ topk_weights, int* ids_lds) {
-  const int lane = threadIdx.x & 63;
-  const int nI = (E + kWave - 1) / kWave;  // slots that hold experts (uniform)
-  long long key[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) key[i] = (lane + kWave * i < E) ? order_key(val[i]) : LLONG_MIN;
-
-  int sel_e[kMaxTopk];
-  double sel_v[kMaxTopk];
-#pragma unroll
-  for (int j = 0; j < kMaxTopk; ++j) {
-    sel_e[j] = 0;
-    sel_v[j] = 0.0;
-    if (j >= k) continue;
-    long long mine = key[0];
-#pragma unroll
-    for (int i = 1; i < 4; ++i)
-      if (i < nI) mine = key[i] > mine ? key[i] : mine;
-    const long long best = wave_max_i64(mine);
-    // the lowest expert with the best key: slots in order, lanes in order
-    int slot = 0, src = 0;
-#pragma unroll
-    for (int i = 3; i >= 0; --i) {
-      if (i >= nI) continue;
-      const uint64_t hit = __ballot(key[i] == best);
-      if (hit) { slot = i; src = __builtin_ctzll(hit); }
-    }
-    double v = val[0];
-#pragma unroll
-    for (int i = 1; i < 4; ++i)
-      if (slot == i) v = val[i];
-    sel_e[j] = src + kWave * slot;
-    sel_v[j] = readlane_f64(v, src);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (i == slot && lane == src) key[i] = LLONG_MIN;
-  }
-
-  double m = sel_v[0];
-#pragma unroll
-  for (int j = 1; j < kMaxTopk; ++j)
-    if (j < k) m = fmax(m, sel_v[j]);
-  double vl = sel_v[0];
-  int el = sel_e[0];
-#pragma unroll
-  for (int j = 1; j < kMaxTopk; ++j)
-    if (lane == j) { vl = sel_v[j]; el = sel_e[j]; }
-  const double z = exp(vl - m);
-  double sum = 0.0;
-#pragma unroll
-  for (int j = 0; j < kMaxTopk; ++j)
-    if (j < k) sum += readlane_f64(z, j);
-  if (lane < k) {
-    topk_ids[(size_t)t * k + lane] = el;
-    topk_weights[(size_t)t * k + lane] = (float)(z / sum);
-    if (ids_lds) ids_lds[t * k + lane] = el;
-  }
-}
-
 __global__ __launch_bounds__(256) void router_topk_softmax(
     const double* __restrict__ partial, const float* __restrict__ bias, int T, int E, int k,
     int splits, int32_t* __restrict__ topk_ids, float* __restrict__ topk_weights,
@@ -381,72 +173,6 @@ constexpr int kFusedThreads = 1024;  // 16 waves: one token per wave in the tail
 constexpr int kFusedMaxT = 16;
 constexpr int kFusedMaxTE = kFusedMaxT * kMaxExperts;  // logits staged in LDS as fp64
 constexpr int kFusedMaxSlots = kFusedMaxT * kMaxTopk;
-constexpr int kFusedMaxSplits = 32;
-
-// The logits of a single token, lane l holding experts l, l+64, ...: the
-// K-range partials (agent-scope atomic loads, all in flight at once) summed
-// in order plus the bias, as router_topk_softmax sums them.
-__device__ void one_token_logits(const double* __restrict__ partial,
-                                 const float* __restrict__ bias, int E, int splits,
-                                 double (&val)[4]) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = lane + kWave * i;
-    double v = 0.0;
-    if (e < E) {
-      double p[kFusedMaxSplits];
-#pragma unroll
-      for (int c = 0; c < kFusedMaxSplits; ++c) {
-        p[c] = __hip_atomic_load(&partial[(size_t)min(c, splits - 1) * E + e], __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_AGENT);
-      }
-#pragma unroll
-      for (int c = 0; c < kFusedMaxSplits; ++c)
-        if (c < splits) v += p[c];
-      if (bias) v += (double)bias[e];
-    }
-    val[i] = v;
-  }
-}
-
-// The tail of the fused launch for a single token, run by one wave with the
-// token's logits in val (lane l: experts l, l+64, ...): top-k and softmax by
-// topk_softmax_wave (the unfused path's code, so ids and weights are
-// identical), and the tile table of the k slots.  Their experts are
-// distinct, so slot j's position in expert order is the number of selected
-// experts below its own, every selected expert gets one tile of one row, and
-// build_tiles_small would produce exactly this table.
-__device__ void tail_one_token(const double (&val)[4], int E, int k,
-                               int32_t* __restrict__ topk_ids,
-                               float* __restrict__ topk_weights, double* __restrict__ logits,
-                               int* s_ids, int32_t* __restrict__ expert_offsets,
-                               int32_t* __restrict__ sorted_ids, int32_t* __restrict__ tiles,
-                               int32_t* __restrict__ num_tiles) {
-  const int lane = threadIdx.x & 63;
-  if (logits)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (lane + kWave * i < E) logits[lane + kWave * i] = val[i];
-  topk_softmax_wave(val, E, k, 0, topk_ids, topk_weights, s_ids);  // lanes < k fill s_ids
-  wave_lds_sync();
-  int ej = 0;
-  if (lane < k) ej = s_ids[lane];
-  int pos = 0;  // selected experts below ej
-  for (int q = 0; q < k; ++q) pos += s_ids[q] < ej;
-  if (lane < k) {
-    sorted_ids[pos] = lane;
-    tiles[3 * pos + 0] = ej;
-    tiles[3 * pos + 1] = pos;
-    tiles[3 * pos + 2] = 1;
-  }
-  for (int e = lane; e <= E; e += kWave) {
-    int below = 0;
-    for (int q = 0; q < k; ++q) below += s_ids[q] < e;
-    expert_offsets[e] = below;
-  }
-  if (lane == 0) num_tiles[0] = k;
-}
 
 __global__ __launch_bounds__(kFusedThreads) void router_decode_fused(
     const uint16_t* __restrict__ x, const float* __restrict__ w_router,

@@ -1,9 +1,10 @@
 """MoeLayer: one MXFP4 MoE layer with every buffer allocated up front.
 
-A call enqueues the library's three entry points (moe_route,
-moe_build_tiles, moe_forward) on the current stream with preallocated
-outputs and workspaces, so it allocates nothing per call and can be
-captured in a HIP graph.  Weights are device tensors in the library's
+A call enqueues the library's entry points (moe_route, moe_build_tiles,
+moe_forward; for small batches moe_route_tiles + moe_forward; for one token
+the single-launch moe_layer_one_token) on the current stream with
+preallocated outputs and workspaces, so it allocates nothing per call and
+can be captured in a HIP graph.  Weights are device tensors in the library's
 canonical layout (see include/moe_mxfp4.h).
 """
 from __future__ import annotations
@@ -31,8 +32,10 @@ class MoeLayer:
         """Point the layer at another copy of the expert weights (same shapes)."""
         self.w13_q, self.w13_s, self.w2_q, self.w2_s = w13_q, w13_s, w2_q, w2_s
 
-    def plan(self, T: int, BM: Optional[int] = None):
-        """Allocate every buffer for batches of T tokens."""
+    def plan(self, T: int, BM: Optional[int] = None, one_launch: bool = True):
+        """Allocate every buffer for batches of T tokens.  With one token the
+        layer runs as one launch (moe_layer_one_token) unless one_launch is
+        False or the shape is outside that entry point's range."""
         dev, E, H, I, k = self.device, self.E, self.H, self.I, self.k
         self.T = T
         self.BM = B.pick_bm(T, k, E) if BM is None else BM
@@ -51,6 +54,11 @@ class MoeLayer:
         self.fwd_ws = torch.empty(max(B.forward_workspace_bytes(T, H, I, k), 16),
                                   dtype=torch.uint8, device=dev)
         self.out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        one_ws = B.layer_one_token_workspace_bytes(H, I, E, k) if T == 1 else 0
+        self.one_launch = bool(one_launch and one_ws > 0)
+        # its counters must start zeroed; every call leaves them that way
+        self.one_ws = (torch.zeros(one_ws, dtype=torch.uint8, device=dev)
+                       if self.one_launch else None)
         return self
 
     def _args(self):
@@ -120,13 +128,23 @@ class MoeLayer:
                                  s), "moe_combine")
 
     def __call__(self, x: torch.Tensor) -> torch.Tensor:
-        """One layer call: moe_route, moe_build_tiles, moe_forward."""
+        """One layer call: routing and tiles, then moe_forward (one launch for
+        one token)."""
         T = x.shape[0]
         if self.T != T:
             self.plan(T)
         lib, s = self._args()
         p = self._p
         E, H, I, k, BM = self.E, self.H, self.I, self.k, self.BM
+        if self.one_launch:
+            B._check(lib.moe_layer_one_token(p(x), p(self.w_router), p(self.bias), p(self.w13_q),
+                                             p(self.w13_s), p(self.w2_q), p(self.w2_s), H, I, E,
+                                             k, p(self.topk_ids), p(self.topk_weights), None,
+                                             p(self.offsets), p(self.sorted_ids), p(self.tiles),
+                                             p(self.num_tiles), p(self.one_ws),
+                                             self.one_ws.numel(), p(self.out), s),
+                     "moe_layer_one_token")
+            return self.out
         self.route_only(x)
         self.tiles_only()
         B._check(lib.moe_forward(p(x), p(self.w13_q), p(self.w13_s), p(self.w2_q), p(self.w2_s),
