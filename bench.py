@@ -1,9 +1,11 @@
 #!/usr/bin/env python3
 """Benchmark of the MXFP4 grouped-expert MoE layer on one MI355X (gfx950).
 
-One step is one full layer call (moe_route -> moe_build_tiles -> moe_forward:
-router logits, top-k, softmax, tile table, gate/up + SwiGLU, down, combine)
-over one batch of synthetic gpt-oss-shaped input already resident in HBM.
+One step is one full layer call (router logits, top-k, softmax, tile table,
+gate/up + SwiGLU, down, combine) over one batch of synthetic gpt-oss-shaped
+input already resident in HBM: moe_route (or, up to 16 tokens,
+moe_route_tiles) + moe_build_tiles + moe_forward, and for one token the
+single-launch moe_layer_one_token.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1]
 
@@ -16,7 +18,9 @@ k=4, I=2880).  Timing:
     Cache, which keeps repeated calls from being served by it;
   * per-kernel durations: for each entry point a HIP graph of back-to-back
     launches of it alone, timed with HIP events on the launch stream; the
-    dominant kernel's average launch duration gives the roofline fraction;
+    dominant kernel's average launch duration gives the roofline fraction
+    (for one token the whole step is one kernel, timed by the headline loop
+    itself; the separate entry points are then reported as components);
   * cpu_baseline: the float64 oracle on this host's cores, on a bounded
     sample of the same workload.
 Prints one JSON line.
@@ -261,7 +265,15 @@ def main():
         del src, dst
 
     gu_us = kernel_us["gateup"]
-    if T <= 64:
+    if layer.one_launch:
+        # the step is one launch: every byte the layer touches, per launch of it
+        achieved = touched / (us * 1e-6) / 1e9
+        kname = "moe_layer_one_token_kernel"
+        roof = {"kernel": kname, "bound": "hbm", "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(inp["name"], kname),
+                "algorithmic_bytes_per_launch": touched, "avg_launch_us": round(us, 2)}
+    elif T <= 64:
         gu_bytes = n_touched * gateup_bytes(H, I) + T * H * 2 + T * k * I * 2
         achieved = gu_bytes / (gu_us * 1e-6) / 1e9
         kname = "expert_gemm_kernel<gate/up>"
@@ -296,7 +308,9 @@ def main():
         "data": "synthetic (seeded gpt-oss-shaped MXFP4 layer, no checkpoint)",
         "config": {"workload": inp["name"], "T": T, "H": H, "E": E, "k": k, "I": I, "BM": BM,
                    "experts_touched": n_touched, "weight_rotations": R, "timing": mode,
-                   "routing": "moe_route_tiles" if layer.fused else "moe_route+moe_build_tiles"},
+                   "routing": ("moe_layer_one_token" if layer.one_launch else
+                               "moe_route_tiles" if layer.fused else
+                               "moe_route+moe_build_tiles")},
         "tokens_per_s": round(T / (us * 1e-6), 1),
         "hbm_gbps": round(gbps, 1),
         "hbm_frac": round(gbps / HBM_PEAK_GBS, 4),

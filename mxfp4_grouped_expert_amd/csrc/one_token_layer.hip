@@ -9,7 +9,7 @@
 // with workgroups are a large share of the layer.  Here one grid holds all
 // of it, every workgroup resident from the start:
 //   routing   splits x ceil(E/16) workgroups compute fp64 partial logits (as
-//             router_decode_fused does); the last to finish sums them, runs
+//             router_decode_fused does); the last of them sums them, runs
 //             the wave top-k and softmax, publishes the plan (expert and
 //             slot of each sorted position, weight of each slot), then
 //             writes the routing outputs and the tile table for the caller.
@@ -33,7 +33,8 @@
 // agent-scope atomics (coherent across the XCDs' L2 caches); a consumer
 // polls the words it needs until their stamps match, so no producer waits
 // for its stores to complete and no counter sits on the critical path.
-// The routing partials use the ticket pattern of router_decode_fused.  The
+// Each routing workgroup stamps a word once its partials are stored; the
+// last routing workgroup waits for the others' stamps.  The
 // epoch is read by every workgroup at its start and advanced by the last
 // of them to check in (a two-level arrival tree), so each call sees its own
 // value.  Polls are bounded: one that gives up sets the error word and its
@@ -74,13 +75,15 @@ struct ReplicaLine {
   u64 plan[kMaxTopk];    // sorted position g: stamp | slot << 16 | expert
   u64 weight[kMaxTopk];  // slot j: stamp | routing weight bits
 };
+constexpr int kMaxRoute = 32 * (kMaxExperts / 16);  // routing workgroups at most
 struct Sync {
-  int router_ticket;     // routing workgroups finished (the last resets it)
+  int reserved;
   int epoch;             // calls begun by every workgroup
   int error;             // set (sticky) when a poll gives up
   int pad0[kLine - 3];
   Tree arrivals;         // every workgroup, once it has read the epoch
   ReplicaLine rep[kReplicas];
+  u64 routed[kMaxRoute]; // routing workgroup i: stamp once its partials are stored
 };
 static_assert(sizeof(ReplicaLine) == 128, "one line per replica");
 static_assert(sizeof(Sync) % 128 == 0, "whole lines");
@@ -179,16 +182,29 @@ __device__ void routing_role(const Args& a, int rid, unsigned char* lds) {
                                rid / eb);
   __builtin_amdgcn_s_waitcnt(0);  // this workgroup's partials are stored
   __syncthreads();
-  int* s_last = reinterpret_cast<int*>(lds);
-  int* s_ids = s_last + 4;
+  int* s_ids = reinterpret_cast<int*>(lds);
   float* s_w = reinterpret_cast<float*>(s_ids + kMaxTopk);
   if (threadIdx.x == 0) {
-    *s_last = add_agent(&a.sync->router_ticket, 1) == a.n_route - 1;
+    if (rid != a.n_route - 1) st64(&a.sync->routed[rid], stamp, 1u);
     check_in(a.sync, epoch);
   }
-  __syncthreads();
-  if (!*s_last || threadIdx.x >= kWave) return;  // one wave finishes the token
+  // the last routing workgroup finishes the token with one wave, once every
+  // other routing workgroup has stamped its word
+  if (rid != a.n_route - 1 || threadIdx.x >= kWave) return;
   const int lane = threadIdx.x;
+  {
+    constexpr int kPer = kMaxRoute / kWave;
+    const u64* src[kPer];
+    bool use[kPer];
+    u64 v[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int w = lane + i * kWave;
+      use[i] = w < a.n_route - 1;
+      src[i] = &a.sync->routed[min(w, kMaxRoute - 1)];
+    }
+    settle(src, use, v, stamp, &a.sync->error);
+  }
   double val[4];
   one_token_logits(a.partial, a.bias, a.E, a.splits, val);
   // top-k and softmax into LDS only: the plan goes out first, the routing
@@ -207,7 +223,6 @@ __device__ void routing_role(const Args& a, int rid, unsigned char* lds) {
       st64(&L->weight[j], stamp, __float_as_uint(s_w[j]));
     }
   }
-  if (lane == 0) st_agent(&a.sync->router_ticket, 0);
   if (a.logits)
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -525,8 +540,11 @@ size_t round_up(size_t n) { return (n + 255) / 256 * 256; }
 }  // namespace
 
 bool layer_one_token_ok(int H, int I, int E, int k) {
-  return H % 32 == 0 && I % 32 == 0 && H <= kMaxK && I <= kMaxK && E >= 1 &&
-         E <= kMaxExperts && k >= 1 && k <= kMaxTopk && k <= E;
+  if (!(H % 32 == 0 && I % 32 == 0 && H > 0 && I > 0 && H <= kMaxK && I <= kMaxK && E >= 1 &&
+        E <= kMaxExperts && k >= 1 && k <= kMaxTopk && k <= E))
+    return false;
+  const RouterPlan p = router_plan(1, H, E);
+  return p.splits * ((E + kExpPerBlock - 1) / kExpPerBlock) <= kMaxRoute;
 }
 
 size_t layer_one_token_sync_bytes(int H) {
