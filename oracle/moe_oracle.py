@@ -16,7 +16,11 @@ gating and top-k.  Steps, each a function below:
   1. router logits  L[t, e] = sum_h x[t, h] * Wr[e, h] (+ b[e])
   2. top-k          the k largest logits per token, in descending order,
                     exact ties going to the lower expert index
-  3. softmax        over the k selected logits only
+  3. gating         softmax over the k selected logits only; or, with
+                    sigmoid gating (the triton-kernels README's router,
+                    section "Project Structure", moe/router.py: "softmax/
+                    sigmoid gating + top-k"), s = sigmoid of each selected
+                    logit, normalised to sum 1 over the k
   4. tile table     per-expert counts, exclusive offsets, a stable
                     counting sort of flat slot ids p = t*k + j, and tiles of
                     at most BM rows per expert
@@ -40,6 +44,13 @@ section "Correctness"):
   * Two codes per byte, the even element in the low nibble.
   * w13 rows [0, I) are the gate projection, rows [I, 2I) the up projection.
   * The router bias, when present, is added before both top-k and softmax.
+  * Sigmoid gating: the pages name it (the README's router; the DeepSeek-V3
+    report cited there) but give no formula.  Read here as: experts chosen
+    by the same top-k of the logits (sigmoid is increasing, so this is the
+    top-k of the sigmoid scores, except where two large logits round to the
+    same float64 sigmoid), weights sigmoid(L_j) / sum over the k selected of
+    sigmoid(L_q), so the weights sum to 1 as softmax's do; the bias, when
+    present, is part of the logit.
 """
 from __future__ import annotations
 
@@ -123,11 +134,25 @@ def softmax_selected(L: np.ndarray, ids: np.ndarray) -> np.ndarray:
     return z / z.sum(axis=1, keepdims=True)
 
 
-def route(x_bits, w_router, bias, k):
+def sigmoid_selected(L: np.ndarray, ids: np.ndarray) -> np.ndarray:
+    """Step 3, sigmoid gating: s = 1 / (1 + exp(-L)) of the k selected logits
+    of each token, divided by their sum, float64 [T, k]."""
+    sel = np.take_along_axis(L, ids.astype(np.int64), axis=1)
+    s = 1.0 / (1.0 + np.exp(-sel))
+    return s / s.sum(axis=1, keepdims=True)
+
+
+GATINGS = ("softmax", "sigmoid")
+
+
+def route(x_bits, w_router, bias, k, gating="softmax"):
     """Steps 1-3. Returns (topk_ids int32 [T,k], topk_weights float64 [T,k], L)."""
+    if gating not in GATINGS:
+        raise ValueError(f"gating must be one of {GATINGS}")
     L = router_logits(x_bits, w_router, bias)
     ids = top_k(L, k)
-    return ids, softmax_selected(L, ids), L
+    w = softmax_selected(L, ids) if gating == "softmax" else sigmoid_selected(L, ids)
+    return ids, w, L
 
 
 # -------------------------------------------------------------- tile table --
@@ -186,14 +211,16 @@ def combine(y: np.ndarray, w: np.ndarray) -> np.ndarray:
 def moe_layer(inp: dict, BM: int = 16, tokens=None) -> dict:
     """The whole layer in float64.
 
-    inp holds x, w_router, bias, w13_q, w13_s, w2_q, w2_s and k.  With
+    inp holds x, w_router, bias, w13_q, w13_s, w2_q, w2_s and k (and
+    optionally gating, "softmax" when absent).  With
     ``tokens`` (an index array) only those tokens' outputs are evaluated
     (routing and the tile table still cover every token); experts are
     decoded one at a time so the largest layer stays within memory.
     """
     k = int(inp["k"])
     E = inp["w13_q"].shape[0]
-    ids, w, L = route(inp["x"], inp["w_router"], inp.get("bias"), k)
+    ids, w, L = route(inp["x"], inp["w_router"], inp.get("bias"), k,
+                      inp.get("gating", "softmax"))
     offsets, sorted_ids, tiles, num_tiles = build_tiles(ids, E, BM)
     T = ids.shape[0]
     want = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)

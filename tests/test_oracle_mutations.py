@@ -40,6 +40,17 @@ def _softmax_all_experts(L, ids):
     return np.take_along_axis(z, ids.astype(np.int64), axis=1)
 
 
+def _sigmoid_unnormalised(L, ids):
+    sel = np.take_along_axis(L, ids.astype(np.int64), axis=1)
+    return 1.0 / (1.0 + np.exp(-sel))
+
+
+def _sigmoid_sign_flipped(L, ids):
+    sel = np.take_along_axis(L, ids.astype(np.int64), axis=1)
+    s = 1.0 / (1.0 + np.exp(sel))
+    return s / s.sum(axis=1, keepdims=True)
+
+
 def _ffn(swap=False, transpose_down=False, no_silu=False):
     def f(X, q13, s13, q2, s2):
         W13 = mo.dequant_mxfp4(q13, s13)
@@ -73,6 +84,8 @@ PINS = [
     tdec.test_dequant_exhaustive_codes_times_scales,
     trout.test_topk_tie_rule_and_order,
     trout.test_softmax_equals_renormalised_full_softmax,
+    trout.test_sigmoid_gating_worked_example,
+    trout.test_sigmoid_gating_closed_forms,
     lambda: trout.test_tiles_against_python_sort_and_invariants(17, 3, 5, 4),
     tffn.test_permutation_weights_closed_form,
     tffn.test_single_expert_equals_textbook_swiglu_mlp,
@@ -84,6 +97,8 @@ MUTATIONS = {
     "e8m0_bias_126": ("decode_e8m0", _e8m0_bias_126),
     "ties_to_higher_index": ("top_k", _topk_ties_high),
     "softmax_over_all_experts": ("softmax_selected", _softmax_all_experts),
+    "sigmoid_unnormalised": ("sigmoid_selected", _sigmoid_unnormalised),
+    "sigmoid_sign_flipped": ("sigmoid_selected", _sigmoid_sign_flipped),
     "gate_up_swapped": ("expert_ffn", _ffn(swap=True)),
     "down_transposed": ("expert_ffn", _ffn(transpose_down=True)),
     "no_silu": ("expert_ffn", _ffn(no_silu=True)),

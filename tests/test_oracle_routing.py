@@ -90,6 +90,50 @@ def test_softmax_special_cases():
     assert np.all(ids == np.arange(3)) and np.allclose(w, 1 / 3, rtol=0, atol=1e-15)
 
 
+def test_sigmoid_gating_worked_example():
+    # logits 0, ln 3, -ln 3: sigmoids 1/2, 3/4, 1/4; top-2 are experts 1 and 0,
+    # weights (3/4, 1/2) / (5/4) = (0.6, 0.4)
+    L = np.array([[0.0, np.log(3.0), -np.log(3.0)]])
+    ids = oracle.top_k(L, 2)
+    assert list(ids[0]) == [1, 0]
+    np.testing.assert_allclose(oracle.sigmoid_selected(L, ids), [[0.6, 0.4]], rtol=0, atol=1e-15)
+
+
+def test_sigmoid_gating_closed_forms():
+    rng = np.random.default_rng(6)
+    L = rng.standard_normal((12, 7)) * 4
+    # one expert: weight 1
+    assert np.all(oracle.sigmoid_selected(L, oracle.top_k(L, 1)) == 1.0)
+    # a pair of logits a, -a: sigmoid(a) + sigmoid(-a) = 1, so the weights are
+    # the sigmoids themselves (scipy's expit as the independent reference)
+    from scipy.special import expit
+    a = rng.standard_normal(9) * 3
+    P = np.stack([a, -a], axis=1)
+    ids = oracle.top_k(P, 2)
+    w = oracle.sigmoid_selected(P, ids)
+    np.testing.assert_allclose(w, expit(np.take_along_axis(P, ids.astype(np.int64), axis=1)),
+                               rtol=1e-14, atol=0)
+    # in general: positive, summing to 1, descending with the logits, and
+    # different from softmax whenever the selected logits differ
+    ids = oracle.top_k(L, 3)
+    w = oracle.sigmoid_selected(L, ids)
+    assert np.all(w > 0)
+    np.testing.assert_allclose(w.sum(axis=1), 1.0, rtol=0, atol=1e-12)
+    assert np.all(np.diff(w, axis=1) <= 0)
+    assert not np.allclose(w, oracle.softmax_selected(L, ids))
+
+
+def test_route_gating_switch():
+    inp = make_random(T=6, H=64, E=8, k=2, I=32, seed=7, router_std=0.3)
+    ids_s, w_s, L = oracle.route(inp["x"], inp["w_router"], None, 2, gating="sigmoid")
+    ids_m, w_m, _ = oracle.route(inp["x"], inp["w_router"], None, 2)
+    assert np.array_equal(ids_s, ids_m)
+    np.testing.assert_array_equal(w_s, oracle.sigmoid_selected(L, ids_s))
+    np.testing.assert_array_equal(w_m, oracle.softmax_selected(L, ids_m))
+    with pytest.raises(ValueError):
+        oracle.route(inp["x"], inp["w_router"], None, 2, gating="relu")
+
+
 def test_route_on_workloads_has_clear_gaps():
     # routing is unique when the float64 gaps between the k-th and (k+1)-th
     # logits (and between consecutive selected logits) are far above the
