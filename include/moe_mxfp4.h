@@ -88,6 +88,17 @@ const char* moe_version(void);
 #define MOE_MAX_TOPK 8
 #define MOE_MAX_DIM 65536 /* largest H or I */
 
+/* Gating of the k selected logits (the `gating` argument of the routing
+ * entry points).  The triton-kernels README ("Project Structure",
+ * moe/router.py) names softmax and sigmoid gating beside top-k; the
+ * selection is the same top-k of the logits for both.
+ *   MOE_GATING_SOFTMAX  w_j = exp(L_j - max) / sum over the k of the same
+ *   MOE_GATING_SIGMOID  w_j = s_j / sum over the k of s, s = 1/(1+exp(-L_j))
+ * Both are evaluated in fp64, the sum taken in ascending slot order, and the
+ * weights rounded to fp32 once.  Any other value gives MOE_ERR_SHAPE. */
+#define MOE_GATING_SOFTMAX 0
+#define MOE_GATING_SIGMOID 1
+
 /* Token tile for the tile table (host, pure function).  The SimpleLLM
  * write-up pins the tile rather than autotuning it ("Fixed decode tiles")
  * and grows the token tile with tokens per expert ("MoE token tile follows
@@ -114,15 +125,17 @@ size_t moe_forward_workspace_bytes(int T, int H, int I, int k);
 /* ------------------------------------------------------------- moe_route
  * Router logits L[t][e] = sum_h x[t][h]*w_router[e][h] (+ bias[e]) in fp64,
  * then per token the k largest logits in descending order (exact ties go to
- * the lower expert index) and the softmax over those k logits.
- * ("Where the time went": "Router + top-k"; triton-kernels README "Project
- * Structure": moe/router.py "Softmax/sigmoid gating + top-k".)
+ * the lower expert index) and the gating (softmax, or normalised sigmoid:
+ * MOE_GATING_*) over those k logits.
+ * ("Where the time went": "Router + top-k"; the triton-kernels README,
+ * section "Project Structure", lists a router module that pairs top-k with
+ * softmax or sigmoid gating.)
  *
  *   x           [T][H] bf16 bits, 16-byte aligned
  *   w_router    [E][H] fp32, 16-byte aligned
- *   bias        [E] fp32 or NULL; added before top-k and softmax
+ *   bias        [E] fp32 or NULL; added before top-k and gating
  *   T >= 0, 0 < H <= 65536, H % 32 == 0, 1 <= E <= 256, 1 <= k <= min(E, 8),
- *   T*E < 2^31
+ *   T*E < 2^31, gating MOE_GATING_SOFTMAX or MOE_GATING_SIGMOID
  *   topk_ids    out [T][k] int32
  *   topk_weights out [T][k] fp32 (each row sums to 1 within 1e-6)
  *   logits      out [T][E] fp64, or NULL if not wanted
@@ -130,7 +143,7 @@ size_t moe_forward_workspace_bytes(int T, int H, int I, int k);
  * NaN logits make the choice unspecified (but in range).
  */
 moe_status moe_route(const uint16_t* x, const float* w_router, const float* bias,
-                     int T, int H, int E, int k,
+                     int T, int H, int E, int k, int gating,
                      int32_t* topk_ids, float* topk_weights, double* logits,
                      void* workspace, size_t workspace_bytes,
                      struct ihipStream_t* stream);
@@ -212,7 +225,7 @@ moe_status moe_forward(const uint16_t* x,
 size_t moe_route_tiles_workspace_bytes(int T, int H, int E);
 
 moe_status moe_route_tiles(const uint16_t* x, const float* w_router, const float* bias,
-                           int T, int H, int E, int k, int BM,
+                           int T, int H, int E, int k, int gating, int BM,
                            int32_t* topk_ids, float* topk_weights, double* logits,
                            int32_t* expert_offsets, int32_t* sorted_ids,
                            int32_t* tiles, int32_t* num_tiles,
@@ -252,7 +265,7 @@ size_t moe_layer_one_token_sync_bytes(int H);
 moe_status moe_layer_one_token(const uint16_t* x, const float* w_router, const float* bias,
                                const uint8_t* w13_q, const uint8_t* w13_s,
                                const uint8_t* w2_q, const uint8_t* w2_s,
-                               int H, int I, int E, int k,
+                               int H, int I, int E, int k, int gating,
                                int32_t* topk_ids, float* topk_weights, double* logits,
                                int32_t* expert_offsets, int32_t* sorted_ids,
                                int32_t* tiles, int32_t* num_tiles,

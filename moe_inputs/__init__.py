@@ -23,10 +23,18 @@ available:
 A uniformly random byte carries two independent uniform nibbles, so the
 packed weight arrays are drawn as raw bytes.
 
+Two more workloads take the shapes of the triton-kernels README's MoE
+dispatch benchmark (section "Benchmarks": a Mixtral-8x7B-shaped layer, 8
+experts, top-2, hidden 4096, FFN 14336; and a DeepSeek-V3-shaped layer, 256
+experts with sigmoid gating as the report it cites describes; the top-8 and
+the hidden 7168 / expert FFN 2048 widths are that model's published shape,
+not stated on the pages) at 128 tokens, with the same distributions.
+
 Seeds: weights come from ``default_rng([model_id, 1])`` (tiny = 0, 20b = 20,
-120b = 120), so workloads that share a model share its bytes; activations,
-router and bias come from ``default_rng([workload_id, 2])``.  Draw order:
-x, w_router, bias; then w13 codes, w13 scales, w2 codes, w2 scales.
+120b = 120, Mixtral-shaped = 8, DeepSeek-V3-shaped = 671), so workloads that
+share a model share its bytes; activations, router and bias come from
+``default_rng([workload_id, 2])``.  Draw order: x, w_router, bias; then w13
+codes, w13 scales, w2 codes, w2 scales.
 """
 from __future__ import annotations
 
@@ -50,6 +58,7 @@ class Workload:
     I: int
     model_id: int
     router_bias: bool
+    gating: str = "softmax"
 
 
 WORKLOADS = {
@@ -58,6 +67,9 @@ WORKLOADS = {
     2: Workload(2, "gptoss20b_decode_T64_biased_router", 64, 2880, 32, 4, 2880, 20, True),
     3: Workload(3, "gptoss120b_decode_T64", 64, 2880, 128, 4, 2880, 120, False),
     4: Workload(4, "gptoss120b_prefill_T4096", 4096, 2880, 128, 4, 2880, 120, False),
+    5: Workload(5, "mixtral8x7b_shaped_T128", 128, 4096, 8, 2, 14336, 8, False),
+    6: Workload(6, "deepseekv3_shaped_T128_sigmoid", 128, 7168, 256, 8, 2048, 671, False,
+                "sigmoid"),
 }
 
 
@@ -98,9 +110,9 @@ def make_activations(T: int, H: int, E: int, seed, router_bias: bool,
 
 
 def make_workload(wid: int, weights: bool = True) -> dict:
-    """All inputs of one of the five gpt-oss-shaped workloads, with its shape."""
+    """All inputs of one of the workloads above, with its shape and gating."""
     w = WORKLOADS[wid]
-    out = dict(T=w.T, H=w.H, E=w.E, k=w.k, I=w.I, name=w.name, wid=wid)
+    out = dict(T=w.T, H=w.H, E=w.E, k=w.k, I=w.I, name=w.name, wid=wid, gating=w.gating)
     out.update(make_activations(w.T, w.H, w.E, [wid, 2], w.router_bias))
     if weights:
         out.update(make_weights(w.E, w.H, w.I, w.model_id))
@@ -108,9 +120,11 @@ def make_workload(wid: int, weights: bool = True) -> dict:
 
 
 def make_random(T: int, H: int, E: int, k: int, I: int, seed: int,
-                router_bias: bool = False, router_std: float = 0.02) -> dict:
+                router_bias: bool = False, router_std: float = 0.02,
+                gating: str = "softmax") -> dict:
     """A small random layer of arbitrary shape, same distributions."""
-    out = dict(T=T, H=H, E=E, k=k, I=I, name=f"rand_T{T}_H{H}_E{E}_k{k}_I{I}_s{seed}")
+    out = dict(T=T, H=H, E=E, k=k, I=I, name=f"rand_T{T}_H{H}_E{E}_k{k}_I{I}_s{seed}",
+               gating=gating)
     out.update(make_activations(T, H, E, [1000 + seed, 2], router_bias, router_std))
     out.update(make_weights(E, H, I, 1000 + seed))
     return out

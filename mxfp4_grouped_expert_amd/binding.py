@@ -53,7 +53,7 @@ def load() -> ctypes.CDLL:
     lib.moe_route_workspace_bytes.restype = _sz
     lib.moe_forward_workspace_bytes.argtypes = [_i, _i, _i, _i]
     lib.moe_forward_workspace_bytes.restype = _sz
-    lib.moe_route.argtypes = [_p, _p, _p, _i, _i, _i, _i, _p, _p, _p, _p, _sz, _p]
+    lib.moe_route.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p, _p, _sz, _p]
     lib.moe_route.restype = _i
     lib.moe_build_tiles.argtypes = [_p, _i, _i, _i, _i, _p, _p, _p, _p, _p]
     lib.moe_build_tiles.restype = _i
@@ -62,7 +62,7 @@ def load() -> ctypes.CDLL:
     lib.moe_forward.restype = _i
     lib.moe_route_tiles_workspace_bytes.argtypes = [_i, _i, _i]
     lib.moe_route_tiles_workspace_bytes.restype = _sz
-    lib.moe_route_tiles.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p,
+    lib.moe_route_tiles.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p,
                                     _p, _sz, _p]
     lib.moe_route_tiles.restype = _i
     lib.moe_gateup_swiglu.argtypes = [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p, _p]
@@ -75,7 +75,7 @@ def load() -> ctypes.CDLL:
     lib.moe_layer_one_token_workspace_bytes.restype = _sz
     lib.moe_layer_one_token_sync_bytes.argtypes = [_i]
     lib.moe_layer_one_token_sync_bytes.restype = _sz
-    lib.moe_layer_one_token.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i,
+    lib.moe_layer_one_token.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i,
                                         _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p, _p]
     lib.moe_layer_one_token.restype = _i
     _lib = lib
@@ -139,9 +139,20 @@ def _workspace(nbytes: int, device) -> torch.Tensor:
     return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
 
 
+GATINGS = {"softmax": 0, "sigmoid": 1}  # MOE_GATING_SOFTMAX, MOE_GATING_SIGMOID
+
+
+def gating_code(gating: str) -> int:
+    if gating not in GATINGS:
+        raise ValueError(f"gating must be one of {sorted(GATINGS)}")
+    return GATINGS[gating]
+
+
 def moe_route(x: torch.Tensor, w_router: torch.Tensor, bias: Optional[torch.Tensor], k: int,
-              want_logits: bool = False, workspace: Optional[torch.Tensor] = None):
-    """Router logits (fp64) -> top-k -> softmax over the k selected logits.
+              want_logits: bool = False, workspace: Optional[torch.Tensor] = None,
+              gating: str = "softmax"):
+    """Router logits (fp64) -> top-k -> gating (softmax, or sigmoid normalised
+    over the k) of the k selected logits.
 
     x: bf16 [T, H] (or its bits as int16/uint16); w_router: fp32 [E, H];
     bias: fp32 [E] or None.  Returns (topk_ids int32 [T, k],
@@ -162,7 +173,8 @@ def moe_route(x: torch.Tensor, w_router: torch.Tensor, bias: Optional[torch.Tens
     nbytes = route_workspace_bytes(T, H, E)
     if workspace is None:
         workspace = _workspace(nbytes, dev)
-    _check(load().moe_route(_ptr(x), _ptr(w_router), _ptr(bias), T, H, E, k, _ptr(ids),
+    _check(load().moe_route(_ptr(x), _ptr(w_router), _ptr(bias), T, H, E, k, gating_code(gating),
+                            _ptr(ids),
                             _ptr(wts), _ptr(logits), _ptr(workspace), workspace.numel(),
                             _stream(dev)), "moe_route")
     return ids, wts, logits
@@ -185,7 +197,7 @@ def zeroed_route_tiles_workspace(T: int, H: int, E: int, device) -> torch.Tensor
 
 def moe_route_tiles(x: torch.Tensor, w_router: torch.Tensor, bias: Optional[torch.Tensor],
                     k: int, BM: int, want_logits: bool = False,
-                    workspace: Optional[torch.Tensor] = None):
+                    workspace: Optional[torch.Tensor] = None, gating: str = "softmax"):
     """Fused decode routing + tile table.  Returns (topk_ids, topk_weights,
     logits or None, expert_offsets, sorted_ids, tiles, num_tiles)."""
     _need(x, "x", _BF16)
@@ -204,7 +216,8 @@ def moe_route_tiles(x: torch.Tensor, w_router: torch.Tensor, bias: Optional[torc
     num_tiles = torch.zeros(1, dtype=torch.int32, device=dev)
     if workspace is None:
         workspace = zeroed_route_tiles_workspace(T, H, E, dev)
-    _check(load().moe_route_tiles(_ptr(x), _ptr(w_router), _ptr(bias), T, H, E, k, BM, _ptr(ids),
+    _check(load().moe_route_tiles(_ptr(x), _ptr(w_router), _ptr(bias), T, H, E, k,
+                                  gating_code(gating), BM, _ptr(ids),
                                   _ptr(wts), _ptr(logits), _ptr(offsets), _ptr(sorted_ids),
                                   _ptr(tiles), _ptr(num_tiles), _ptr(workspace),
                                   workspace.numel(), _stream(dev)), "moe_route_tiles")
@@ -231,7 +244,7 @@ def moe_layer_one_token(x: torch.Tensor, w_router: torch.Tensor, bias: Optional[
                         w13_q: torch.Tensor, w13_s: torch.Tensor, w2_q: torch.Tensor,
                         w2_s: torch.Tensor, k: int, BM: int, want_logits: bool = False,
                         workspace: Optional[torch.Tensor] = None,
-                        out: Optional[torch.Tensor] = None):
+                        out: Optional[torch.Tensor] = None, gating: str = "softmax"):
     """The whole layer for one token in one launch.  Returns (out bf16 [1, H],
     topk_ids, topk_weights, logits or None, expert_offsets, sorted_ids, tiles,
     num_tiles), each equal to what moe_route_tiles + moe_forward produce."""
@@ -260,7 +273,8 @@ def moe_layer_one_token(x: torch.Tensor, w_router: torch.Tensor, bias: Optional[
     if workspace is None:
         workspace = zeroed_layer_one_token_workspace(H, I, E, k, dev)
     _check(load().moe_layer_one_token(_ptr(x), _ptr(w_router), _ptr(bias), _ptr(w13_q),
-                                      _ptr(w13_s), _ptr(w2_q), _ptr(w2_s), H, I, E, k, _ptr(ids),
+                                      _ptr(w13_s), _ptr(w2_q), _ptr(w2_s), H, I, E, k,
+                                      gating_code(gating), _ptr(ids),
                                       _ptr(wts), _ptr(logits), _ptr(offsets), _ptr(sorted_ids),
                                       _ptr(tiles), _ptr(num_tiles), _ptr(workspace),
                                       workspace.numel(), _ptr(out), _stream(dev)),

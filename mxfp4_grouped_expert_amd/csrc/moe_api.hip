@@ -40,6 +40,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 size_t round256(size_t n) { return (n + 255) & ~size_t(255); }
 
 bool valid_bm(int BM) { return BM == 16 || BM == 32 || BM == 64 || BM == 128; }
+bool gating_ok(int gating) { return gating == MOE_GATING_SOFTMAX || gating == MOE_GATING_SIGMOID; }
 
 moe_status finish_launches() {
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
@@ -93,8 +94,10 @@ size_t moe_forward_workspace_bytes(int T, int H, int I, int k) {
 }
 
 moe_status moe_route(const uint16_t* x, const float* w_router, const float* bias, int T, int H,
-                     int E, int k, int32_t* topk_ids, float* topk_weights, double* logits,
-                     void* workspace, size_t workspace_bytes, struct ihipStream_t* stream) {
+                     int E, int k, int gating, int32_t* topk_ids, float* topk_weights,
+                     double* logits, void* workspace, size_t workspace_bytes,
+                     struct ihipStream_t* stream) {
+  if (!gating_ok(gating)) return MOE_ERR_SHAPE;
   if (T < 0 || H <= 0 || H % 32 != 0 || H > MOE_MAX_DIM || E < 1 || E > MOE_MAX_EXPERTS || k < 1 ||
       k > MOE_MAX_TOPK || k > E || (int64_t)T * E >= (int64_t(1) << 31) ||
       (int64_t)T * H >= (int64_t(1) << 40))
@@ -109,8 +112,8 @@ moe_status moe_route(const uint16_t* x, const float* w_router, const float* bias
   const moe::RouterPlan plan = moe::router_plan(T, H, E);
   double* partial = static_cast<double*>(workspace);
   moe::launch_router_logits(x, w_router, T, H, E, plan, partial, as_stream(stream));
-  moe::launch_router_topk(partial, bias, T, E, k, plan.splits, topk_ids, topk_weights, logits,
-                          as_stream(stream));
+  moe::launch_router_topk(partial, bias, T, E, k, gating, plan.splits, topk_ids, topk_weights,
+                          logits, as_stream(stream));
   return finish_launches();
 }
 
@@ -120,12 +123,14 @@ size_t moe_route_tiles_workspace_bytes(int T, int H, int E) {
 }
 
 moe_status moe_route_tiles(const uint16_t* x, const float* w_router, const float* bias, int T,
-                           int H, int E, int k, int BM, int32_t* topk_ids, float* topk_weights,
+                           int H, int E, int k, int gating, int BM, int32_t* topk_ids,
+                           float* topk_weights,
                            double* logits, int32_t* expert_offsets, int32_t* sorted_ids,
                            int32_t* tiles, int32_t* num_tiles, void* workspace,
                            size_t workspace_bytes, struct ihipStream_t* stream) {
   if (T < 0 || H <= 0 || H % 32 != 0 || H > MOE_MAX_DIM || E < 1 || E > MOE_MAX_EXPERTS ||
-      k < 1 || k > MOE_MAX_TOPK || k > E || !valid_bm(BM) || !moe::router_fused_ok(T, E, k))
+      k < 1 || k > MOE_MAX_TOPK || k > E || !valid_bm(BM) || !moe::router_fused_ok(T, E, k) ||
+      !gating_ok(gating))
     return MOE_ERR_SHAPE;
   if (T == 0) return MOE_OK;
   if (!x || !w_router || !topk_ids || !topk_weights || !expert_offsets || !sorted_ids || !tiles ||
@@ -136,7 +141,8 @@ moe_status moe_route_tiles(const uint16_t* x, const float* w_router, const float
   moe_status st = check_device();
   if (st != MOE_OK) return st;
   (void)hipGetLastError();
-  moe::launch_router_fused(x, w_router, bias, T, H, E, k, BM, workspace, topk_ids, topk_weights,
+  moe::launch_router_fused(x, w_router, bias, T, H, E, k, gating, BM, workspace, topk_ids,
+                           topk_weights,
                            logits, expert_offsets, sorted_ids, tiles, num_tiles,
                            as_stream(stream));
   return finish_launches();
@@ -265,14 +271,15 @@ size_t moe_layer_one_token_sync_bytes(int H) {
 
 moe_status moe_layer_one_token(const uint16_t* x, const float* w_router, const float* bias,
                                const uint8_t* w13_q, const uint8_t* w13_s, const uint8_t* w2_q,
-                               const uint8_t* w2_s, int H, int I, int E, int k,
+                               const uint8_t* w2_s, int H, int I, int E, int k, int gating,
                                int32_t* topk_ids, float* topk_weights, double* logits,
                                int32_t* expert_offsets, int32_t* sorted_ids, int32_t* tiles,
                                int32_t* num_tiles, void* workspace, size_t workspace_bytes,
                                uint16_t* out, struct ihipStream_t* stream) {
   if (H <= 0 || I <= 0 || H > MOE_MAX_DIM || I > MOE_MAX_DIM || E < 1 ||
       E > MOE_MAX_EXPERTS || k < 1 || k > MOE_MAX_TOPK || k > E ||
-      (int64_t)E * 2 * I >= (int64_t(1) << 31) || !moe::layer_one_token_ok(H, I, E, k))
+      (int64_t)E * 2 * I >= (int64_t(1) << 31) || !moe::layer_one_token_ok(H, I, E, k) ||
+      !gating_ok(gating))
     return MOE_ERR_SHAPE;
   if (!x || !w_router || !w13_q || !w13_s || !w2_q || !w2_s || !topk_ids || !topk_weights ||
       !expert_offsets || !sorted_ids || !tiles || !num_tiles || !workspace || !out)
@@ -284,7 +291,8 @@ moe_status moe_layer_one_token(const uint16_t* x, const float* w_router, const f
   moe_status st = check_device();
   if (st != MOE_OK) return st;
   (void)hipGetLastError();
-  moe::launch_layer_one_token(x, w_router, bias, w13_q, w13_s, w2_q, w2_s, H, I, E, k, topk_ids,
+  moe::launch_layer_one_token(x, w_router, bias, w13_q, w13_s, w2_q, w2_s, H, I, E, k, gating,
+                              topk_ids,
                               topk_weights, logits, expert_offsets, sorted_ids, tiles, num_tiles,
                               workspace, out, as_stream(stream));
   return finish_launches();

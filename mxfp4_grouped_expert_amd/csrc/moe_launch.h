@@ -17,9 +17,10 @@ RouterPlan router_plan(int T, int H, int E);
 size_t router_partial_bytes(int T, int H, int E);
 void launch_router_logits(const uint16_t* x, const float* w_router, int T, int H, int E,
                           const RouterPlan& plan, double* partial, hipStream_t stream);
+// gating: 0 softmax, 1 sigmoid (normalised over the k selected)
 void launch_router_topk(const double* partial, const float* bias, int T, int E, int k,
-                        int splits, int32_t* topk_ids, float* topk_weights, double* logits,
-                        hipStream_t stream);
+                        int gating, int splits, int32_t* topk_ids, float* topk_weights,
+                        double* logits, hipStream_t stream);
 
 // Fused decode path: partial logits, then in the last workgroup the sum,
 // top-k, softmax and tile table (T*E <= 8192, T*k <= 1024).  The workspace
@@ -27,7 +28,8 @@ void launch_router_topk(const double* partial, const float* bias, int T, int E, 
 bool router_fused_ok(int T, int E, int k);
 size_t router_fused_bytes(int T, int H, int E);
 void launch_router_fused(const uint16_t* x, const float* w_router, const float* bias, int T,
-                         int H, int E, int k, int BM, void* workspace, int32_t* topk_ids,
+                         int H, int E, int k, int gating, int BM, void* workspace,
+                         int32_t* topk_ids,
                          float* topk_weights, double* logits, int32_t* expert_offsets,
                          int32_t* sorted_ids, int32_t* tiles, int32_t* num_tiles,
                          hipStream_t stream);
@@ -71,7 +73,8 @@ size_t layer_one_token_sync_bytes(int H);
 size_t layer_one_token_bytes(int H, int I, int E, int k);
 void launch_layer_one_token(const uint16_t* x, const float* w_router, const float* bias,
                             const uint8_t* w13_q, const uint8_t* w13_s, const uint8_t* w2_q,
-                            const uint8_t* w2_s, int H, int I, int E, int k, int32_t* topk_ids,
+                            const uint8_t* w2_s, int H, int I, int E, int k, int gating,
+                            int32_t* topk_ids,
                             float* topk_weights, double* logits, int32_t* expert_offsets,
                             int32_t* sorted_ids, int32_t* tiles, int32_t* num_tiles,
                             void* workspace, uint16_t* out, hipStream_t stream);

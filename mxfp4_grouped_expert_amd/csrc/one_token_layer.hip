@@ -157,7 +157,7 @@ struct Args {
   const uint8_t* w13_s;
   const uint8_t* w2_q;
   const uint8_t* w2_s;
-  int H, I, E, k;
+  int H, I, E, k, gating;
   int split_len, splits, n_route;
   int32_t* topk_ids;
   float* topk_weights;
@@ -209,7 +209,7 @@ __device__ void routing_role(const Args& a, int rid, unsigned char* lds) {
   one_token_logits(a.partial, a.bias, a.E, a.splits, val);
   // top-k and softmax into LDS only: the plan goes out first, the routing
   // outputs for the caller (identical values) after it
-  topk_softmax_wave(val, a.E, a.k, 0, nullptr, nullptr, s_ids, s_w);
+  topk_softmax_wave(val, a.E, a.k, a.gating, 0, nullptr, nullptr, s_ids, s_w);
   wave_lds_sync();
   // lane (r, j) writes slot j's entries of replica r, 8 replicas per pass
   for (int r0 = 0; r0 < kReplicas; r0 += kWave / kMaxTopk) {
@@ -560,7 +560,8 @@ size_t layer_one_token_bytes(int H, int I, int E, int k) {
 
 void launch_layer_one_token(const uint16_t* x, const float* w_router, const float* bias,
                             const uint8_t* w13_q, const uint8_t* w13_s, const uint8_t* w2_q,
-                            const uint8_t* w2_s, int H, int I, int E, int k, int32_t* topk_ids,
+                            const uint8_t* w2_s, int H, int I, int E, int k, int gating,
+                            int32_t* topk_ids,
                             float* topk_weights, double* logits, int32_t* expert_offsets,
                             int32_t* sorted_ids, int32_t* tiles, int32_t* num_tiles,
                             void* workspace, uint16_t* out, hipStream_t stream) {
@@ -569,7 +570,7 @@ void launch_layer_one_token(const uint16_t* x, const float* w_router, const floa
   Args a;
   a.x = x; a.w_router = w_router; a.bias = bias;
   a.w13_q = w13_q; a.w13_s = w13_s; a.w2_q = w2_q; a.w2_s = w2_s;
-  a.H = H; a.I = I; a.E = E; a.k = k;
+  a.H = H; a.I = I; a.E = E; a.k = k; a.gating = gating;
   a.split_len = p.split_len;
   a.splits = p.splits;
   a.n_route = p.splits * ((E + kExpPerBlock - 1) / kExpPerBlock);

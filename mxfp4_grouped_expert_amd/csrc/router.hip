@@ -134,7 +134,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void router_logits_mfma(
 
 __global__ __launch_bounds__(256) void router_topk_softmax(
     const double* __restrict__ partial, const float* __restrict__ bias, int T, int E, int k,
-    int splits, int32_t* __restrict__ topk_ids, float* __restrict__ topk_weights,
+    int gating, int splits, int32_t* __restrict__ topk_ids, float* __restrict__ topk_weights,
     double* __restrict__ logits) {
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
@@ -161,7 +161,7 @@ __global__ __launch_bounds__(256) void router_topk_softmax(
     }
     val[i] = v;
   }
-  topk_softmax_wave(val, E, k, t, topk_ids, topk_weights, nullptr);
+  topk_softmax_wave(val, E, k, gating, t, topk_ids, topk_weights, nullptr);
 }
 
 // ------------------------------------------------------------ fused decode
@@ -176,8 +176,8 @@ constexpr int kFusedMaxSlots = kFusedMaxT * kMaxTopk;
 
 __global__ __launch_bounds__(kFusedThreads) void router_decode_fused(
     const uint16_t* __restrict__ x, const float* __restrict__ w_router,
-    const float* __restrict__ bias, int T, int H, int E, int k, int BM, int split_len,
-    int splits, int* __restrict__ counter, double* __restrict__ partial,
+    const float* __restrict__ bias, int T, int H, int E, int k, int gating, int BM,
+    int split_len, int splits, int* __restrict__ counter, double* __restrict__ partial,
     int32_t* __restrict__ topk_ids, float* __restrict__ topk_weights,
     double* __restrict__ logits, int32_t* __restrict__ expert_offsets,
     int32_t* __restrict__ sorted_ids, int32_t* __restrict__ tiles,
@@ -213,7 +213,7 @@ __global__ __launch_bounds__(kFusedThreads) void router_decode_fused(
     if (threadIdx.x < kWave) {
       double val[4];
       one_token_logits(partial, bias, E, splits, val);
-      tail_one_token(val, E, k, topk_ids, topk_weights, logits, s_ids, expert_offsets,
+      tail_one_token(val, E, k, gating, topk_ids, topk_weights, logits, s_ids, expert_offsets,
                      sorted_ids, tiles, num_tiles);
       if (threadIdx.x == 0)
         __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -274,7 +274,7 @@ __global__ __launch_bounds__(kFusedThreads) void router_decode_fused(
     const double* v = s_sel_v + t * kMaxTopk;
     double m = v[0];
     for (int q = 1; q < k; ++q) m = fmax(m, v[q]);
-    s_z[t * kMaxTopk + j] = exp(v[j] - m);
+    s_z[t * kMaxTopk + j] = gate_term(v[j], m, gating);
   }
   lds_barrier();
   for (int i = threadIdx.x; i < T * k; i += kFusedThreads) {
@@ -349,7 +349,8 @@ size_t router_fused_bytes(int T, int H, int E) {
 }
 
 void launch_router_fused(const uint16_t* x, const float* w_router, const float* bias, int T,
-                         int H, int E, int k, int BM, void* workspace, int32_t* topk_ids,
+                         int H, int E, int k, int gating, int BM, void* workspace,
+                         int32_t* topk_ids,
                          float* topk_weights, double* logits, int32_t* expert_offsets,
                          int32_t* sorted_ids, int32_t* tiles, int32_t* num_tiles,
                          hipStream_t stream) {
@@ -359,16 +360,17 @@ void launch_router_fused(const uint16_t* x, const float* w_router, const float* 
   const int eb = (E + kExpPerBlock - 1) / kExpPerBlock;
   dim3 grid((T + kTokPerWave - 1) / kTokPerWave, (eb + 3) / 4, plan.splits);
   hipLaunchKernelGGL(router_decode_fused, grid, dim3(kFusedThreads), 0, stream, x, w_router, bias,
-                     T, H, E, k, BM, plan.split_len, plan.splits, counter, partial, topk_ids,
+                     T, H, E, k, gating, BM, plan.split_len, plan.splits, counter, partial,
+                     topk_ids,
                      topk_weights, logits, expert_offsets, sorted_ids, tiles, num_tiles);
 }
 
 void launch_router_topk(const double* partial, const float* bias, int T, int E, int k,
-                        int splits, int32_t* topk_ids, float* topk_weights, double* logits,
-                        hipStream_t stream) {
+                        int gating, int splits, int32_t* topk_ids, float* topk_weights,
+                        double* logits, hipStream_t stream) {
   dim3 grid((T + kWavesPerBlock - 1) / kWavesPerBlock);
   hipLaunchKernelGGL(router_topk_softmax, grid, dim3(256), 0, stream, partial, bias, T, E, k,
-                     splits, topk_ids, topk_weights, logits);
+                     gating, splits, topk_ids, topk_weights, logits);
 }
 
 }  // namespace moe

@@ -149,6 +149,16 @@ __device__ __forceinline__ long long wave_max_i64(long long v) {
   return m;
 }
 
+// Gating term of a selected logit v (m: the largest selected logit): exp(v - m)
+// for softmax, sigmoid(v) = 1 / (1 + exp(-v)) for sigmoid gating.  Either
+// way the weights are the terms divided by their sum (taken in ascending
+// slot order).
+constexpr int kGatingSoftmax = 0;
+constexpr int kGatingSigmoid = 1;
+__device__ __forceinline__ double gate_term(double v, double m, int gating) {
+  return gating == kGatingSigmoid ? 1.0 / (1.0 + exp(-v)) : exp(v - m);
+}
+
 // Top-k and softmax of one token by one wave.  Lane l holds the logits of
 // experts l, l+64, l+128, l+192 in val[] (entries >= E are ignored).  k
 // rounds of a wave-wide argmax on (higher logit, then lower expert index):
@@ -159,7 +169,7 @@ __device__ __forceinline__ long long wave_max_i64(long long v) {
 // ascending j, w_j = z_j / sum, so the weights do not depend on which lane
 // computed which term.  Writes ids and weights to topk_ids / topk_weights
 // and ids_lds / w_lds, each where given (non-null).
-__device__ void topk_softmax_wave(const double (&val)[4], int E, int k, int t,
+__device__ void topk_softmax_wave(const double (&val)[4], int E, int k, int gating, int t,
                                   int32_t* __restrict__ topk_ids,
                                   float* __restrict__ topk_weights, int* ids_lds,
                                   float* w_lds = nullptr) {
@@ -209,7 +219,7 @@ __device__ void topk_softmax_wave(const double (&val)[4], int E, int k, int t,
 #pragma unroll
   for (int j = 1; j < kMaxTopk; ++j)
     if (lane == j) { vl = sel_v[j]; el = sel_e[j]; }
-  const double z = exp(vl - m);
+  const double z = gate_term(vl, m, gating);
   double sum = 0.0;
 #pragma unroll
   for (int j = 0; j < kMaxTopk; ++j)
@@ -289,7 +299,7 @@ __device__ void one_token_tables(int E, int k, const int* s_ids,
 // experts below its own, every selected expert gets one tile of one row, and
 // build_tiles_small would produce exactly this table.  The selected ids go
 // to s_ids (LDS) and, if s_w is given, their weights to s_w.
-__device__ void tail_one_token(const double (&val)[4], int E, int k,
+__device__ void tail_one_token(const double (&val)[4], int E, int k, int gating,
                                int32_t* __restrict__ topk_ids,
                                float* __restrict__ topk_weights, double* __restrict__ logits,
                                int* s_ids, int32_t* __restrict__ expert_offsets,
@@ -300,7 +310,7 @@ __device__ void tail_one_token(const double (&val)[4], int E, int k,
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       if (lane + kWave * i < E) logits[lane + kWave * i] = val[i];
-  topk_softmax_wave(val, E, k, 0, topk_ids, topk_weights, s_ids, s_w);  // lanes < k fill s_ids
+  topk_softmax_wave(val, E, k, gating, 0, topk_ids, topk_weights, s_ids, s_w);  // lanes < k fill s_ids
   wave_lds_sync();
   one_token_tables(E, k, s_ids, expert_offsets, sorted_ids, tiles, num_tiles);
 }

@@ -20,8 +20,9 @@ from . import binding as B
 class MoeLayer:
     def __init__(self, w_router: torch.Tensor, bias: Optional[torch.Tensor],
                  w13_q: torch.Tensor, w13_s: torch.Tensor, w2_q: torch.Tensor,
-                 w2_s: torch.Tensor, k: int):
+                 w2_s: torch.Tensor, k: int, gating: str = "softmax"):
         self.device = w13_q.device
+        self.gating = B.gating_code(gating)
         self.E, I2, Hh = w13_q.shape
         self.H, self.I, self.k = Hh * 2, I2 // 2, int(k)
         self.w_router, self.bias = w_router, bias
@@ -76,13 +77,14 @@ class MoeLayer:
         p = self._p
         T, E, H, k = x.shape[0], self.E, self.H, self.k
         if self.fused:
-            B._check(lib.moe_route_tiles(p(x), p(self.w_router), p(self.bias), T, H, E, k, self.BM,
+            B._check(lib.moe_route_tiles(p(x), p(self.w_router), p(self.bias), T, H, E, k,
+                                         self.gating, self.BM,
                                          p(self.topk_ids), p(self.topk_weights), None,
                                          p(self.offsets), p(self.sorted_ids), p(self.tiles),
                                          p(self.num_tiles), p(self.route_ws),
                                          self.route_ws.numel(), s), "moe_route_tiles")
             return
-        B._check(lib.moe_route(p(x), p(self.w_router), p(self.bias), T, H, E, k,
+        B._check(lib.moe_route(p(x), p(self.w_router), p(self.bias), T, H, E, k, self.gating,
                                p(self.topk_ids), p(self.topk_weights), None, p(self.route_ws),
                                self.route_ws.numel(), s), "moe_route")
 
@@ -139,7 +141,7 @@ class MoeLayer:
         if self.one_launch:
             B._check(lib.moe_layer_one_token(p(x), p(self.w_router), p(self.bias), p(self.w13_q),
                                              p(self.w13_s), p(self.w2_q), p(self.w2_s), H, I, E,
-                                             k, p(self.topk_ids), p(self.topk_weights), None,
+                                             k, self.gating, p(self.topk_ids), p(self.topk_weights), None,
                                              p(self.offsets), p(self.sorted_ids), p(self.tiles),
                                              p(self.num_tiles), p(self.one_ws),
                                              self.one_ws.numel(), p(self.out), s),

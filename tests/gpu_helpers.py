@@ -31,7 +31,8 @@ def log(msg: str):
 def to_device(inp: dict, dev="cuda") -> dict:
     d = {"x": torch.from_numpy(np.ascontiguousarray(inp["x"]).view(np.int16)).to(dev),
          "w_router": torch.from_numpy(np.ascontiguousarray(inp["w_router"])).to(dev),
-         "bias": None if inp.get("bias") is None else torch.from_numpy(inp["bias"]).to(dev)}
+         "bias": None if inp.get("bias") is None else torch.from_numpy(inp["bias"]).to(dev),
+         "gating": inp.get("gating", "softmax")}
     for key in ("w13_q", "w13_s", "w2_q", "w2_s"):
         d[key] = torch.from_numpy(np.ascontiguousarray(inp[key])).to(dev)
     return d
@@ -39,7 +40,8 @@ def to_device(inp: dict, dev="cuda") -> dict:
 
 def run_gpu(d: dict, k: int, BM: int) -> dict:
     E = d["w13_q"].shape[0]
-    ids, wts, logits = moe.moe_route(d["x"], d["w_router"], d["bias"], k, want_logits=True)
+    ids, wts, logits = moe.moe_route(d["x"], d["w_router"], d["bias"], k, want_logits=True,
+                                     gating=d["gating"])
     off, srt, tiles, nt = moe.moe_build_tiles(ids, E, BM)
     out = moe.moe_forward(d["x"], d["w13_q"], d["w13_s"], d["w2_q"], d["w2_s"], wts, srt, tiles,
                           nt, BM)

@@ -73,12 +73,12 @@ def test_workspace_sizes():
 
 
 def _route(**kw):
-    a = dict(x=P, w=P, bias=None, T=4, H=256, E=8, k=2, ids=P, wts=P, logits=None, ws=P,
-             wsb=1 << 20)
+    a = dict(x=P, w=P, bias=None, T=4, H=256, E=8, k=2, gating=0, ids=P, wts=P, logits=None,
+             ws=P, wsb=1 << 20)
     a.update(kw)
     lib = B.load()
-    return lib.moe_route(a["x"], a["w"], a["bias"], a["T"], a["H"], a["E"], a["k"], a["ids"],
-                         a["wts"], a["logits"], a["ws"], a["wsb"], None)
+    return lib.moe_route(a["x"], a["w"], a["bias"], a["T"], a["H"], a["E"], a["k"], a["gating"],
+                         a["ids"], a["wts"], a["logits"], a["ws"], a["wsb"], None)
 
 
 def _tiles(**kw):
@@ -102,7 +102,8 @@ def _forward(**kw):
     (dict(H=100), SHAPE), (dict(H=0), SHAPE), (dict(E=0), SHAPE), (dict(E=257), SHAPE),
     (dict(k=0), SHAPE), (dict(k=9, E=16), SHAPE), (dict(k=9, E=8), SHAPE), (dict(T=-1), SHAPE),
     (dict(H=65536 + 32), SHAPE), (dict(x=PMIS), ALIGN), (dict(w=PMIS), ALIGN),
-    (dict(wsb=0), WORKSPACE), (dict(T=0, x=None), OK),
+    (dict(wsb=0), WORKSPACE), (dict(T=0, x=None), OK), (dict(gating=2), SHAPE),
+    (dict(gating=-1), SHAPE),
 ])
 def test_route_validation(kw, want):
     assert _route(**kw) == want
@@ -129,18 +130,20 @@ def test_forward_validation(kw, want):
 
 
 def _route_tiles(**kw):
-    a = dict(x=P, w=P, bias=None, T=4, H=256, E=8, k=2, BM=16, ids=P, wts=P, logits=None, off=P,
-             srt=P, tiles=P, nt=P, ws=P, wsb=1 << 20)
+    a = dict(x=P, w=P, bias=None, T=4, H=256, E=8, k=2, gating=0, BM=16, ids=P, wts=P,
+             logits=None, off=P, srt=P, tiles=P, nt=P, ws=P, wsb=1 << 20)
     a.update(kw)
     return B.load().moe_route_tiles(a["x"], a["w"], a["bias"], a["T"], a["H"], a["E"], a["k"],
-                                    a["BM"], a["ids"], a["wts"], a["logits"], a["off"], a["srt"],
-                                    a["tiles"], a["nt"], a["ws"], a["wsb"], None)
+                                    a["gating"], a["BM"], a["ids"], a["wts"], a["logits"],
+                                    a["off"], a["srt"], a["tiles"], a["nt"], a["ws"], a["wsb"],
+                                    None)
 
 
 @pytest.mark.parametrize("kw,want", [
     (dict(x=None), NULL), (dict(tiles=None), NULL), (dict(ws=None), NULL), (dict(nt=None), NULL),
     (dict(T=17, E=128), SHAPE), (dict(T=64, k=4, E=8), SHAPE), (dict(BM=8), SHAPE),
     (dict(H=48), SHAPE), (dict(x=PMIS), ALIGN), (dict(wsb=16), WORKSPACE), (dict(T=0, x=None), OK),
+    (dict(gating=7), SHAPE),
 ])
 def test_route_tiles_validation(kw, want):
     assert _route_tiles(**kw) == want

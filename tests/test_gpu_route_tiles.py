@@ -118,7 +118,7 @@ def test_fused_graph_replays():
     g = torch.cuda.CUDAGraph()
     with torch.cuda.stream(stream):
         with torch.cuda.graph(g, stream=stream):
-            st = lib.moe_route_tiles(p(x), p(wr), p(b), T, inp["H"], E, k, BM, p(ids), p(wts),
+            st = lib.moe_route_tiles(p(x), p(wr), p(b), T, inp["H"], E, k, 0, BM, p(ids), p(wts),
                                      None, p(off), p(srt), p(tiles), p(nt), p(layer_ws),
                                      layer_ws.numel(),
                                      __import__("ctypes").c_void_p(stream.cuda_stream))

@@ -14,7 +14,7 @@ import pytest
 from scipy.special import softmax as sp_softmax
 
 import oracle
-from moe_inputs import make_random, make_workload
+from moe_inputs import WORKLOADS, make_random, make_workload
 
 
 def _exact(v) -> Fraction:
@@ -138,9 +138,10 @@ def test_route_on_workloads_has_clear_gaps():
     # routing is unique when the float64 gaps between the k-th and (k+1)-th
     # logits (and between consecutive selected logits) are far above the
     # GPU's fp64 accumulation error
-    for wid in range(5):
+    for wid in sorted(WORKLOADS):
         inp = make_workload(wid, weights=False)
-        ids, w, L = oracle.route(inp["x"], inp["w_router"], inp["bias"], inp["k"])
+        ids, w, L = oracle.route(inp["x"], inp["w_router"], inp["bias"], inp["k"],
+                                 inp["gating"])
         srt = -np.sort(-L, axis=1)
         gaps = -np.diff(srt[:, :inp["k"] + 1], axis=1)
         assert gaps.min() > 1e-9, (wid, gaps.min())
