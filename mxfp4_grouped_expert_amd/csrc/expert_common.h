@@ -11,6 +11,7 @@ namespace {
 constexpr int kRowsPerBlock = 16;   // weight rows per 16-row block (MFMA N)
 constexpr int kBlocksPerStep = 16;  // MX blocks per step (4 waves x 4 lane groups)
 constexpr int kChunk = 6;           // steps whose weights a wave holds at once (K = 3072)
+constexpr int kChunkK = kChunk * kBlocksPerStep * 32;  // K elements per chunk (3072)
 
 // A tile row that does not describe slots of one valid expert is skipped, so
 // a corrupted table cannot send loads or stores out of bounds.

@@ -107,7 +107,9 @@ __global__ __launch_bounds__(256 * NBW) void expert_gemm_kernel(
 
   const int nsteps = (KB + kBlocksPerStep - 1) / kBlocksPerStep;
   const int nchunks = ONECHUNK ? 1 : (nsteps + kChunk - 1) / kChunk;
-  const int stride = act_stride_bytes(K);
+  // Staged activations: the whole of K with one chunk; with several, one
+  // chunk's K-range at a time (so a pass can hold 16 rows at any K).
+  const int stride = act_stride_bytes(ONECHUNK ? K : min(K, kChunkK));
   const int npass = (rows + XR - 1) / XR;
 
   uint4 wreg[kChunk][NW];
@@ -183,8 +185,10 @@ __global__ __launch_bounds__(256 * NBW) void expert_gemm_kernel(
   // instruction fills 64 consecutive slots = 1 KB.  Slots past the last row
   // repeat it; the LDS allocation is rounded up to whole kilobytes.
   constexpr int kWavesWG = 4 * NBW;
-  auto stage_acts = [&](int p0, int nrows) {
-    const int cpr = K / 8;
+  // (Elements [k0, k0 + klen) of each row; rows then sit klen*2 + 16 bytes
+  // apart.)
+  auto stage_acts = [&](int p0, int nrows, int k0, int klen) {
+    const int cpr = klen / 8;
     const int spr = cpr + 1;
     const int ninst = (nrows * spr + 63) / 64;
     for (int ins = wave; ins < ninst; ins += kWavesWG) {  // wave-uniform
@@ -192,7 +196,7 @@ __global__ __launch_bounds__(256 * NBW) void expert_gemm_kernel(
       const int r = min(slot / spr, nrows - 1);
       const int c = min(slot - (slot / spr) * spr, cpr - 1);
       __builtin_amdgcn_global_load_lds(
-          act + s_rowoff[p0 + r] + (long long)c * 8,
+          act + s_rowoff[p0 + r] + (long long)(k0 + c * 8),
           (__attribute__((address_space(3))) void*)(smem + (size_t)ins * 1024), 16, 0, 0);
     }
   };
@@ -206,7 +210,7 @@ __global__ __launch_bounds__(256 * NBW) void expert_gemm_kernel(
   if (early) {
     if (tid < rows) s_rowoff[tid] = GATEUP ? 0LL : (long long)(r0 + tid) * I;
     lds_barrier();
-    stage_acts(0, min(XR, rows));
+    stage_acts(0, min(XR, rows), 0, K);
     load_scale_runs();
     asm volatile("" ::: "memory");  // the weight loads stay behind
     load_weights(0);
@@ -235,8 +239,8 @@ __global__ __launch_bounds__(256 * NBW) void expert_gemm_kernel(
     // for that load)
     lds_barrier();
     // Pass 0's activations are staged while the weight stream is in flight;
-    // one wait covers both.
-    stage_acts(0, min(XR, rows));
+    // one wait covers both.  (With several chunks each chunk stages its own.)
+    if constexpr (ONECHUNK) stage_acts(0, min(XR, rows), 0, K);
     __builtin_amdgcn_s_waitcnt(0);
   }
   if constexpr (ONECHUNK) store_scale_runs();
@@ -246,9 +250,9 @@ __global__ __launch_bounds__(256 * NBW) void expert_gemm_kernel(
   for (int pass = 0; pass < npass; ++pass) {
     const int p0 = pass * XR;
     const int prow = min(XR, rows - p0);
-    if (pass > 0) {
+    if (ONECHUNK && pass > 0) {
       __syncthreads();  // previous pass done with LDS
-      stage_acts(p0, prow);
+      stage_acts(p0, prow, 0, K);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     }
@@ -266,9 +270,19 @@ __global__ __launch_bounds__(256 * NBW) void expert_gemm_kernel(
 #pragma unroll
     for (int w = 0; w < NW; ++w) acc[w] = floatx4{0.f, 0.f, 0.f, 0.f};
     const unsigned char* arow = smem + min(li, prow - 1) * stride;
+    int chunk_kb = KB;  // MX blocks of the staged K-range
 
     for (int ch = 0; ch < nchunks; ++ch) {
-      if constexpr (!ONECHUNK) load_weights(ch);
+      if constexpr (!ONECHUNK) {
+        const int k0 = ch * kChunkK, klen = min(K - k0, kChunkK);
+        if (pass > 0 || ch > 0) __syncthreads();  // every wave done with the LDS
+        load_weights(ch);
+        stage_acts(p0, prow, k0, klen);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        arow = smem + min(li, prow - 1) * act_stride_bytes(klen);
+        chunk_kb = klen / 32;
+      }
 #pragma unroll
       for (int c = 0; c < kChunk; ++c) {
         if (XCHG && pass == 0) {  // uniform: exchange step c's pieces
@@ -295,11 +309,12 @@ __global__ __launch_bounds__(256 * NBW) void expert_gemm_kernel(
                        "+v"(wreg[c][w].w), "+v"(sreg[c][w]));
         const int b = (ch * kChunk + c) * kBlocksPerStep + kq * 4 + grp;
         const bool valid = b < KB;
-        const int bc = min(b, KB - 1);
+        // block within the staged K-range (the whole of K with one chunk)
+        const int bl = min(c * kBlocksPerStep + kq * 4 + grp, chunk_kb - 1);
         float scale[NW];
 #pragma unroll
         for (int w = 0; w < NW; ++w) scale[w] = valid ? e8m0_to_float(sreg[c][w]) : 0.f;
-        const uint4* ap = reinterpret_cast<const uint4*>(arow + bc * 64);
+        const uint4* ap = reinterpret_cast<const uint4*>(arow + bl * 64);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const bf16x8 a = as_bf16x8(ap[j]);
@@ -476,7 +491,8 @@ __global__ __launch_bounds__(256 * kFuseMaxK) void down_combine_one_token_kernel
 // Rows of activations staged per pass: twice the expected rows per expert
 // (T*k/E), bounded by the tile's row bound (an expert gets at most one slot
 // per token, so rows <= min(BM, T)), rounded up to a power of two, at most
-// 16, and small enough that the staged rows fit in 96 KB.  Small passes keep
+// 16, and small enough that the staged rows fit in 96 KB (whole-K rows) or
+// 100 KB (one chunk's K-range per row when K > 3072, so 16 rows fit).  Small passes keep
 // the LDS footprint low enough for several workgroups per CU (one's loads
 // overlap another's compute); tiles with more rows take extra passes over
 // weights held in registers.
@@ -486,7 +502,10 @@ int pick_xr(int T, int BM, int K, int E, int k) {
   if (want < cap) cap = (int)want;
   int xr = 1;
   while (xr < cap && xr < 16) xr <<= 1;
-  while (xr > 1 && (size_t)xr * act_stride_bytes(K) > 96 * 1024) xr >>= 1;
+  const bool one_chunk = K <= kChunkK;
+  const size_t row_bytes = act_stride_bytes(one_chunk ? K : kChunkK);
+  const size_t budget = (one_chunk ? 96 : 100) * 1024;
+  while (xr > 1 && (size_t)xr * row_bytes > budget) xr >>= 1;
   return xr;
 }
 
@@ -503,7 +522,7 @@ void launch_expert_gemm(const uint16_t* act, const uint8_t* wq, const uint8_t* w
   const size_t red_bytes_1 = (size_t)4 * (GATEUP ? 2 : 1) * 256 * sizeof(float);
 #define MOE_LAUNCH(NBW_, XR_)                                                                  \
   do {                                                                                          \
-    size_t lds = ((size_t)(XR_) * act_stride_bytes(K) + 1023) / 1024 * 1024;                    \
+    size_t lds = ((size_t)(XR_) * act_stride_bytes(one_chunk ? K : kChunkK) + 1023) / 1024 * 1024; \
     if (lds < red_bytes_1 * (NBW_)) lds = red_bytes_1 * (NBW_);                                 \
     dim3 grid((nblk16 + (NBW_) - 1) / (NBW_), tiles_max);                                       \
     if (one_chunk)                                                                              \
