@@ -3,11 +3,12 @@
 Only tests, the smoke check and the benchmark's CPU-baseline leg may use it.
 """
 from .moe_oracle import (E2M1_VALUES, bf16_to_f64, decode_e2m1, decode_e8m0,
-                         unpack_codes, dequant_mxfp4, router_logits, top_k,
+                         unpack_codes, dequant_mxfp4, blocked_from_canonical,
+                         canonical_from_blocked, router_logits, top_k,
                          softmax_selected, sigmoid_selected, GATINGS, route,
                          build_tiles, silu, expert_ffn, combine, moe_layer)
 
 __all__ = ["E2M1_VALUES", "bf16_to_f64", "decode_e2m1", "decode_e8m0", "unpack_codes",
-           "dequant_mxfp4", "router_logits", "top_k", "softmax_selected", "sigmoid_selected",
+           "dequant_mxfp4", "blocked_from_canonical", "canonical_from_blocked", "router_logits", "top_k", "softmax_selected", "sigmoid_selected",
            "GATINGS", "route",
            "build_tiles", "silu", "expert_ffn", "combine", "moe_layer"]

@@ -107,6 +107,35 @@ def dequant_mxfp4(q: np.ndarray, s: np.ndarray) -> np.ndarray:
     return vals * scale
 
 
+# ---------------------------------------------------------- weight layout --
+
+def blocked_from_canonical(q: np.ndarray) -> np.ndarray:
+    """The load-time repack of a packed code matrix uint8 [..., R, K/2]
+    (R a multiple of 16): within each group of 16 consecutive rows the bytes
+    go block-major, so byte i (0..15) of 32-element MX block b of row r
+    moves to offset b*256 + (r % 16)*16 + i of the group's R/16-th share of
+    the array (the group's 16 * K/2 bytes stay where they were as a whole).
+    Returned in the same shape; the E8M0 scales are not repacked."""
+    q = np.asarray(q, dtype=np.uint8)
+    R, KH = q.shape[-2:]
+    if R % 16 or KH % 16:
+        raise ValueError("need rows % 16 == 0 and K % 32 == 0")
+    lead = q.shape[:-2]
+    groups = q.reshape(lead + (R // 16, 16, KH // 16, 16))  # group, row, block, byte
+    return np.ascontiguousarray(np.swapaxes(groups, -3, -2)).reshape(q.shape)
+
+
+def canonical_from_blocked(qb: np.ndarray) -> np.ndarray:
+    """Inverse of blocked_from_canonical."""
+    qb = np.asarray(qb, dtype=np.uint8)
+    R, KH = qb.shape[-2:]
+    if R % 16 or KH % 16:
+        raise ValueError("need rows % 16 == 0 and K % 32 == 0")
+    lead = qb.shape[:-2]
+    groups = qb.reshape(lead + (R // 16, KH // 16, 16, 16))  # group, block, row, byte
+    return np.ascontiguousarray(np.swapaxes(groups, -3, -2)).reshape(qb.shape)
+
+
 # ----------------------------------------------------------------- routing --
 
 def router_logits(x_bits: np.ndarray, w_router: np.ndarray, bias=None) -> np.ndarray:

@@ -96,3 +96,39 @@ def test_dequant_shape_and_mismatch(shape):
     assert oracle.dequant_mxfp4(q, s).shape == shape
     with pytest.raises(ValueError):
         oracle.dequant_mxfp4(q, s[..., :-1])
+
+
+# ----------------------------------------------------------- weight layout --
+
+def _blocked_by_loops(q):
+    # the definition written out byte by byte: byte i of MX block b of row r
+    # goes to offset b*256 + (r % 16)*16 + i of its 16-row group
+    R, KH = q.shape
+    out = np.zeros(R * KH, dtype=np.uint8)
+    for r in range(R):
+        base = (r // 16) * 16 * KH
+        for b in range(KH // 16):
+            for i in range(16):
+                out[base + b * 256 + (r % 16) * 16 + i] = q[r, b * 16 + i]
+    return out.reshape(R, KH)
+
+
+def test_blocked_layout_matches_definition_and_inverts():
+    rng = np.random.default_rng(11)
+    q = rng.integers(0, 256, size=(48, 80), dtype=np.uint8)  # 3 row groups, 5 blocks
+    qb = oracle.blocked_from_canonical(q)
+    np.testing.assert_array_equal(qb, _blocked_by_loops(q))
+    np.testing.assert_array_equal(oracle.canonical_from_blocked(qb), q)
+    # leading dimensions (experts) are independent
+    q3 = rng.integers(0, 256, size=(2, 32, 48), dtype=np.uint8)
+    qb3 = oracle.blocked_from_canonical(q3)
+    for e in range(2):
+        np.testing.assert_array_equal(qb3[e], _blocked_by_loops(q3[e]))
+    # a wave's 64 lanes (16 rows x 4 blocks) read one contiguous kilobyte
+    flat = qb.reshape(-1)
+    lanes = [flat[b * 256 + r * 16: b * 256 + r * 16 + 16] for b in range(4) for r in range(16)]
+    np.testing.assert_array_equal(np.concatenate(lanes), flat[:1024])
+    assert all(np.array_equal(lanes[b * 16 + r], q[r, b * 16:(b + 1) * 16])
+               for b in range(4) for r in range(16))
+    with pytest.raises(ValueError):
+        oracle.blocked_from_canonical(q[:40])

@@ -76,12 +76,25 @@ def _tiles_unstable(topk_ids, E, BM):
     return off, srt, tiles, nt
 
 
+def _blocked_unchanged(q):
+    return np.ascontiguousarray(np.asarray(q, dtype=np.uint8))
+
+
+def _blocked_whole_matrix(q):
+    # block-major over all rows instead of within 16-row groups
+    q = np.asarray(q, dtype=np.uint8)
+    R, KH = q.shape[-2:]
+    t = q.reshape(q.shape[:-2] + (R, KH // 16, 16))
+    return np.ascontiguousarray(np.swapaxes(t, -3, -2)).reshape(q.shape)
+
+
 _orig_build_tiles = mo.build_tiles
 
 PINS = [
     tdec.test_nibble_order_low_first,
     tdec.test_e8m0_matches_torch_exhaustive,
     tdec.test_dequant_exhaustive_codes_times_scales,
+    tdec.test_blocked_layout_matches_definition_and_inverts,
     trout.test_topk_tie_rule_and_order,
     trout.test_softmax_equals_renormalised_full_softmax,
     trout.test_sigmoid_gating_worked_example,
@@ -104,6 +117,8 @@ MUTATIONS = {
     "no_silu": ("expert_ffn", _ffn(no_silu=True)),
     "combine_unweighted": ("combine", _combine_unweighted),
     "unstable_scatter": ("build_tiles", _tiles_unstable),
+    "blocked_layout_unchanged": ("blocked_from_canonical", _blocked_unchanged),
+    "blocked_over_whole_matrix": ("blocked_from_canonical", _blocked_whole_matrix),
 }
 
 
