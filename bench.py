@@ -51,6 +51,8 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", type=int, default=1, choices=range(7))
     ap.add_argument("--rotations", type=int, default=0, help="weight copies (0 = auto)")
+    ap.add_argument("--layout", default="canonical", choices=("canonical", "blocked"),
+                    help="byte layout of the packed expert codes (blocked: repacked at load)")
     ap.add_argument("--no-graph", action="store_true", help="time eager calls instead of graphs")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -154,8 +156,9 @@ def main():
         + 2 * T * H * 2
     layer_flops = 2 * T * k * 3 * I * H + 2 * T * E * H
     R = args.rotations or max(1, min(32, math.ceil(3 * INFINITY_CACHE / touched)))
+    layer = moe.MoeLayer(wr, bias, *w0, k, gating=inp["gating"], layout=args.layout).plan(T)
+    w0 = [layer.w13_q, layer.w13_s, layer.w2_q, layer.w2_s]  # in the layer's layout
     copies = [w0] + [[w.clone() for w in w0] for _ in range(R - 1)]
-    layer = moe.MoeLayer(wr, bias, *w0, k, gating=inp["gating"]).plan(T)
     BM = layer.BM
     del inp["w13_q"], inp["w13_s"], inp["w2_q"], inp["w2_s"]
 
@@ -268,13 +271,14 @@ def main():
     # the 128-row matrix-core kernels run when the library picks them
     # (expert_mma_ok: 128-row tiles, K <= 3072, >= 32 slots per expert)
     uses_mma = BM == 128 and max(H, I) <= 3072 and T * k >= 32 * E
+    traffic_key = inp["name"] + ("" if args.layout == "canonical" else "/" + args.layout)
     if layer.one_launch:
         # the step is one launch: every byte the layer touches, per launch of it
         achieved = touched / (us * 1e-6) / 1e9
         kname = "moe_layer_one_token_kernel"
         roof = {"kernel": kname, "bound": "hbm", "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": measured_traffic(inp["name"], kname),
+                "traffic": measured_traffic(traffic_key, kname),
                 "algorithmic_bytes_per_launch": touched, "avg_launch_us": round(us, 2)}
     elif T <= 64 or not uses_mma:
         gu_bytes = n_touched * gateup_bytes(H, I) + T * H * 2 + T * k * I * 2
@@ -282,7 +286,7 @@ def main():
         kname = "expert_gemm_kernel<gate/up>"
         roof = {"kernel": kname, "bound": "hbm", "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": measured_traffic(inp["name"], kname),
+                "traffic": measured_traffic(traffic_key, kname),
                 "algorithmic_bytes_per_launch": gu_bytes, "avg_launch_us": round(gu_us, 2)}
     else:
         gu_flops = 2 * T * k * 2 * I * H
@@ -291,7 +295,7 @@ def main():
         roof = {"kernel": kname, "bound": "mfma", "achieved": round(achieved, 1),
                 "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
-                "traffic": measured_traffic(inp["name"], kname),
+                "traffic": measured_traffic(traffic_key, kname),
                 "algorithmic_flops_per_launch": gu_flops, "avg_launch_us": round(gu_us, 2)}
 
     gbps = touched / (us * 1e-6) / 1e9
@@ -311,7 +315,7 @@ def main():
         "data": "synthetic (seeded MXFP4 layer of the workload's shape, no checkpoint)",
         "config": {"workload": inp["name"], "T": T, "H": H, "E": E, "k": k, "I": I, "BM": BM,
                    "experts_touched": n_touched, "weight_rotations": R, "timing": mode,
-                   "gating": inp["gating"],
+                   "gating": inp["gating"], "weight_layout": args.layout,
                    "routing": ("moe_layer_one_token" if layer.one_launch else
                                "moe_route_tiles" if layer.fused else
                                "moe_route+moe_build_tiles")},

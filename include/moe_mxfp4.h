@@ -47,6 +47,9 @@
  *   tiles         int32 [tiles_max][3] rows (expert, row_start, rows)
  *   num_tiles     int32 [1]
  *   out           bf16 bits, uint16 [T][H]
+ * The packed codes w13_q and w2_q may instead be in the blocked layout
+ * (MOE_LAYOUT_BLOCKED below, made by moe_repack_weights); the entry points
+ * that read them take a `layout` argument.  Scales are always as above.
  *
  * Numerics: router logits are accumulated in fp64 (bf16 x fp32 products are
  * exact in fp64), so the top-k choice matches an exact evaluation whenever
@@ -98,6 +101,37 @@ const char* moe_version(void);
  * weights rounded to fp32 once.  Any other value gives MOE_ERR_SHAPE. */
 #define MOE_GATING_SOFTMAX 0
 #define MOE_GATING_SIGMOID 1
+
+/* Byte layout of the packed codes w13_q / w2_q (the `layout` argument of the
+ * entry points that read them; any other value gives MOE_ERR_SHAPE).
+ *   MOE_LAYOUT_CANONICAL  row-major [rows][K/2] as described above.
+ *   MOE_LAYOUT_BLOCKED    the same bytes regrouped within each run of 16
+ *                         consecutive rows (rows 16g .. 16g+15 of the
+ *                         flattened [E*rows][K/2] matrix): byte i (0..15) of
+ *                         MX block b of row 16g + r sits at byte
+ *                         16g*(K/2) + 256b + 16r + i.
+ * The blocked layout gives every wave of the expert kernels one contiguous
+ * kilobyte per load instruction.  Results are bit-identical between the two
+ * layouts. */
+#define MOE_LAYOUT_CANONICAL 0
+#define MOE_LAYOUT_BLOCKED 1
+
+/* ------------------------------------------------------ moe_repack_weights
+ * Reorders a packed code matrix from MOE_LAYOUT_CANONICAL to
+ * MOE_LAYOUT_BLOCKED, once, when weights are loaded.  The SimpleLLM write-up
+ * permutes its MXFP4 weights at load into the order its kernel reads
+ * ("Optimizations": "MXFP4 MoE on tensor cores"; "Dead ends": fixing the
+ * layout inside the kernel was slower) and re-quantizes nothing
+ * ("Correctness"); here too only bytes move.
+ *   q          device, uint8 [rows][K/2] canonical (w13_q: rows = E*2I,
+ *              K = H; w2_q: rows = E*H, K = I), 16-byte aligned, read only
+ *   rows       > 0, a multiple of 16;  K: > 0, a multiple of 32, <= 65536
+ *   q_blocked  device, uint8 [rows][K/2], 16-byte aligned, written; must not
+ *              overlap q
+ * Scales are not touched.  Errors: MOE_ERR_SHAPE (sizes), MOE_ERR_NULL,
+ * MOE_ERR_ALIGN, MOE_ERR_DEVICE, MOE_ERR_HIP; on error nothing is written. */
+moe_status moe_repack_weights(const uint8_t* q, int64_t rows, int K, uint8_t* q_blocked,
+                              struct ihipStream_t* stream);
 
 /* Token tile for the tile table (host, pure function).  The SimpleLLM
  * write-up pins the tile rather than autotuning it ("Fixed decode tiles")
@@ -187,6 +221,7 @@ moe_status moe_build_tiles(const int32_t* topk_ids, int T, int k, int E, int BM,
  *
  *   x             [T][H] bf16 bits, 16-byte aligned
  *   w13_q, w13_s, w2_q, w2_s   MXFP4 weights (layouts above), 16-byte aligned
+ *   layout        MOE_LAYOUT_CANONICAL or MOE_LAYOUT_BLOCKED, for w13_q and w2_q
  *   topk_weights  [T][k] fp32 (from moe_route)
  *   sorted_ids, tiles, num_tiles  from moe_build_tiles with the same T, k,
  *                 E and BM; every slot id must appear once in sorted_ids
@@ -202,7 +237,7 @@ moe_status moe_forward(const uint16_t* x,
                        const uint8_t* w2_q, const uint8_t* w2_s,
                        const float* topk_weights, const int32_t* sorted_ids,
                        const int32_t* tiles, const int32_t* num_tiles,
-                       int T, int H, int I, int E, int k, int BM,
+                       int T, int H, int I, int E, int k, int BM, int layout,
                        void* workspace, size_t workspace_bytes,
                        uint16_t* out, struct ihipStream_t* stream);
 
@@ -244,7 +279,8 @@ moe_status moe_route_tiles(const uint16_t* x, const float* w_router, const float
  * output is bit-identical to moe_route_tiles + moe_forward with the same
  * arguments (BM any valid value: one token gives k one-row tiles).
  *
- *   arguments as for moe_route_tiles and moe_forward with T = 1; logits may
+ *   arguments as for moe_route_tiles and moe_forward with T = 1 (layout
+ *   included: it follows gating); logits may
  *   be NULL; bias may be NULL.  Also requires H <= 3072 and I <= 3072 (one
  *   register chunk of weights per lane), else MOE_ERR_SHAPE.
  *   workspace   >= moe_layer_one_token_workspace_bytes(H, I, E, k) (0 means
@@ -265,7 +301,7 @@ size_t moe_layer_one_token_sync_bytes(int H);
 moe_status moe_layer_one_token(const uint16_t* x, const float* w_router, const float* bias,
                                const uint8_t* w13_q, const uint8_t* w13_s,
                                const uint8_t* w2_q, const uint8_t* w2_s,
-                               int H, int I, int E, int k, int gating,
+                               int H, int I, int E, int k, int gating, int layout,
                                int32_t* topk_ids, float* topk_weights, double* logits,
                                int32_t* expert_offsets, int32_t* sorted_ids,
                                int32_t* tiles, int32_t* num_tiles,
@@ -286,12 +322,12 @@ moe_status moe_layer_one_token(const uint16_t* x, const float* w_router, const f
 moe_status moe_gateup_swiglu(const uint16_t* x, const uint8_t* w13_q, const uint8_t* w13_s,
                              const int32_t* sorted_ids, const int32_t* tiles,
                              const int32_t* num_tiles, int T, int H, int I, int E, int k, int BM,
-                             uint16_t* h, struct ihipStream_t* stream);
+                             int layout, uint16_t* h, struct ihipStream_t* stream);
 
 /* Grouped down GEMM ("MoE down + combine"): y[sorted_ids[r]] = h[r] W2_e^T. */
 moe_status moe_down(const uint16_t* h, const uint8_t* w2_q, const uint8_t* w2_s,
                     const int32_t* sorted_ids, const int32_t* tiles, const int32_t* num_tiles,
-                    int T, int H, int I, int E, int k, int BM, float* y,
+                    int T, int H, int I, int E, int k, int BM, int layout, float* y,
                     struct ihipStream_t* stream);
 
 /* Weighted combine ("MoE down + combine"; the README's unpermute):

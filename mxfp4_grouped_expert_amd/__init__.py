@@ -11,7 +11,8 @@ from .binding import (MoeError, LIB_PATH, load, version, status_string, pick_bm,
                       moe_route_tiles, route_tiles_ok, route_tiles_workspace_bytes,
                       zeroed_route_tiles_workspace, moe_layer_one_token,
                       layer_one_token_workspace_bytes, layer_one_token_sync_bytes,
-                      zeroed_layer_one_token_workspace)
+                      zeroed_layer_one_token_workspace, moe_repack_weights, LAYOUTS,
+                      GATINGS)
 from .layer import MoeLayer
 
 __all__ = ["MoeError", "LIB_PATH", "load", "version", "status_string", "pick_bm", "tiles_max",
@@ -19,4 +20,5 @@ __all__ = ["MoeError", "LIB_PATH", "load", "version", "status_string", "pick_bm"
            "moe_forward", "moe_gateup_swiglu", "moe_down", "moe_combine", "moe_route_tiles",
            "route_tiles_ok", "route_tiles_workspace_bytes", "zeroed_route_tiles_workspace",
            "moe_layer_one_token", "layer_one_token_workspace_bytes", "layer_one_token_sync_bytes",
-           "zeroed_layer_one_token_workspace", "MoeLayer"]
+           "zeroed_layer_one_token_workspace", "moe_repack_weights", "LAYOUTS", "GATINGS",
+           "MoeLayer"]

@@ -58,16 +58,16 @@ def load() -> ctypes.CDLL:
     lib.moe_build_tiles.argtypes = [_p, _i, _i, _i, _i, _p, _p, _p, _p, _p]
     lib.moe_build_tiles.restype = _i
     lib.moe_forward.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _p,
-                                _i, _i, _i, _i, _i, _i, _p, _sz, _p, _p]
+                                _i, _i, _i, _i, _i, _i, _i, _p, _sz, _p, _p]
     lib.moe_forward.restype = _i
     lib.moe_route_tiles_workspace_bytes.argtypes = [_i, _i, _i]
     lib.moe_route_tiles_workspace_bytes.restype = _sz
     lib.moe_route_tiles.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p,
                                     _p, _sz, _p]
     lib.moe_route_tiles.restype = _i
-    lib.moe_gateup_swiglu.argtypes = [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p, _p]
+    lib.moe_gateup_swiglu.argtypes = [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p]
     lib.moe_gateup_swiglu.restype = _i
-    lib.moe_down.argtypes = [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p, _p]
+    lib.moe_down.argtypes = [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p]
     lib.moe_down.restype = _i
     lib.moe_combine.argtypes = [_p, _p, _i, _i, _i, _p, _p]
     lib.moe_combine.restype = _i
@@ -75,9 +75,11 @@ def load() -> ctypes.CDLL:
     lib.moe_layer_one_token_workspace_bytes.restype = _sz
     lib.moe_layer_one_token_sync_bytes.argtypes = [_i]
     lib.moe_layer_one_token_sync_bytes.restype = _sz
-    lib.moe_layer_one_token.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i,
+    lib.moe_layer_one_token.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i,
                                         _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p, _p]
     lib.moe_layer_one_token.restype = _i
+    lib.moe_repack_weights.argtypes = [_p, ctypes.c_int64, _i, _p, _p]
+    lib.moe_repack_weights.restype = _i
     _lib = lib
     return lib
 
@@ -146,6 +148,31 @@ def gating_code(gating: str) -> int:
     if gating not in GATINGS:
         raise ValueError(f"gating must be one of {sorted(GATINGS)}")
     return GATINGS[gating]
+
+
+LAYOUTS = {"canonical": 0, "blocked": 1}  # MOE_LAYOUT_CANONICAL, MOE_LAYOUT_BLOCKED
+
+
+def layout_code(layout: str) -> int:
+    if layout not in LAYOUTS:
+        raise ValueError(f"layout must be one of {sorted(LAYOUTS)}")
+    return LAYOUTS[layout]
+
+
+def moe_repack_weights(q: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Packed codes (w13_q [E, 2I, H/2] or w2_q [E, H, I/2], canonical) ->
+    the same bytes in the blocked layout, as a new tensor of the same shape."""
+    _need(q, "q", _U8)
+    K = q.shape[-1] * 2
+    rows = q.numel() // q.shape[-1]
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", _U8, q.device)
+    if out.shape != q.shape:
+        raise ValueError("out must have the shape of q")
+    _check(load().moe_repack_weights(_ptr(q), rows, K, _ptr(out), _stream(q.device)),
+           "moe_repack_weights")
+    return out
 
 
 def moe_route(x: torch.Tensor, w_router: torch.Tensor, bias: Optional[torch.Tensor], k: int,
@@ -244,7 +271,8 @@ def moe_layer_one_token(x: torch.Tensor, w_router: torch.Tensor, bias: Optional[
                         w13_q: torch.Tensor, w13_s: torch.Tensor, w2_q: torch.Tensor,
                         w2_s: torch.Tensor, k: int, BM: int, want_logits: bool = False,
                         workspace: Optional[torch.Tensor] = None,
-                        out: Optional[torch.Tensor] = None, gating: str = "softmax"):
+                        out: Optional[torch.Tensor] = None, gating: str = "softmax",
+                        layout: str = "canonical"):
     """The whole layer for one token in one launch.  Returns (out bf16 [1, H],
     topk_ids, topk_weights, logits or None, expert_offsets, sorted_ids, tiles,
     num_tiles), each equal to what moe_route_tiles + moe_forward produce."""
@@ -274,7 +302,7 @@ def moe_layer_one_token(x: torch.Tensor, w_router: torch.Tensor, bias: Optional[
         workspace = zeroed_layer_one_token_workspace(H, I, E, k, dev)
     _check(load().moe_layer_one_token(_ptr(x), _ptr(w_router), _ptr(bias), _ptr(w13_q),
                                       _ptr(w13_s), _ptr(w2_q), _ptr(w2_s), H, I, E, k,
-                                      gating_code(gating), _ptr(ids),
+                                      gating_code(gating), layout_code(layout), _ptr(ids),
                                       _ptr(wts), _ptr(logits), _ptr(offsets), _ptr(sorted_ids),
                                       _ptr(tiles), _ptr(num_tiles), _ptr(workspace),
                                       workspace.numel(), _ptr(out), _stream(dev)),
@@ -301,7 +329,8 @@ def moe_forward(x: torch.Tensor, w13_q: torch.Tensor, w13_s: torch.Tensor, w2_q:
                 w2_s: torch.Tensor, topk_weights: torch.Tensor, sorted_ids: torch.Tensor,
                 tiles: torch.Tensor, num_tiles: torch.Tensor, BM: int,
                 out: Optional[torch.Tensor] = None,
-                workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+                workspace: Optional[torch.Tensor] = None,
+                layout: str = "canonical") -> torch.Tensor:
     """Grouped gate/up + SwiGLU, grouped down, weighted combine.  Returns
     out bf16 [T, H]."""
     _need(x, "x", _BF16)
@@ -331,13 +360,14 @@ def moe_forward(x: torch.Tensor, w13_q: torch.Tensor, w13_s: torch.Tensor, w2_q:
         workspace = _workspace(nbytes, dev)
     _check(load().moe_forward(_ptr(x), _ptr(w13_q), _ptr(w13_s), _ptr(w2_q), _ptr(w2_s),
                               _ptr(topk_weights), _ptr(sorted_ids), _ptr(tiles), _ptr(num_tiles),
-                              T, H, I, E, k, BM, _ptr(workspace), workspace.numel(), _ptr(out),
+                              T, H, I, E, k, BM, layout_code(layout), _ptr(workspace),
+                              workspace.numel(), _ptr(out),
                               _stream(dev)), "moe_forward")
     return out
 
 
 def moe_gateup_swiglu(x, w13_q, w13_s, sorted_ids, tiles, num_tiles, k: int, BM: int,
-                      h: Optional[torch.Tensor] = None) -> torch.Tensor:
+                      h: Optional[torch.Tensor] = None, layout: str = "canonical") -> torch.Tensor:
     """Grouped gate/up GEMM + SwiGLU.  Returns h bf16 [T*k, I] in tile order."""
     _need(x, "x", _BF16)
     dev = x.device
@@ -348,13 +378,14 @@ def moe_gateup_swiglu(x, w13_q, w13_s, sorted_ids, tiles, num_tiles, k: int, BM:
         h = torch.empty((T * k, I), dtype=torch.bfloat16, device=dev)
     _need(h, "h", _BF16, dev)
     _check(load().moe_gateup_swiglu(_ptr(x), _ptr(w13_q), _ptr(w13_s), _ptr(sorted_ids),
-                                    _ptr(tiles), _ptr(num_tiles), T, H, I, E, k, BM, _ptr(h),
+                                    _ptr(tiles), _ptr(num_tiles), T, H, I, E, k, BM,
+                                    layout_code(layout), _ptr(h),
                                     _stream(dev)), "moe_gateup_swiglu")
     return h
 
 
 def moe_down(h, w2_q, w2_s, sorted_ids, tiles, num_tiles, T: int, k: int, BM: int,
-             y: Optional[torch.Tensor] = None) -> torch.Tensor:
+             y: Optional[torch.Tensor] = None, layout: str = "canonical") -> torch.Tensor:
     """Grouped down GEMM.  Returns y fp32 [T*k, H] indexed by flat slot id."""
     _need(h, "h", _BF16)
     dev = h.device
@@ -364,7 +395,8 @@ def moe_down(h, w2_q, w2_s, sorted_ids, tiles, num_tiles, T: int, k: int, BM: in
         y = torch.empty((T * k, H), dtype=torch.float32, device=dev)
     _need(y, "y", (torch.float32,), dev)
     _check(load().moe_down(_ptr(h), _ptr(w2_q), _ptr(w2_s), _ptr(sorted_ids), _ptr(tiles),
-                           _ptr(num_tiles), T, H, I, E, k, BM, _ptr(y), _stream(dev)),
+                           _ptr(num_tiles), T, H, I, E, k, BM, layout_code(layout), _ptr(y),
+                           _stream(dev)),
            "moe_down")
     return y
 

@@ -50,7 +50,8 @@ namespace {
 //         and up rows of w13, output h[r][n] = bf16(silu(g) * u).
 // !GATEUP: A rows are h[r], K = I, weights are rows of w2, output
 //         y[sorted_ids[r]][n] in fp32.
-template <bool GATEUP, int NBW, int XR, bool ONECHUNK>
+// BLK: the code matrix is in the blocked layout (see wq_row_offset).
+template <bool GATEUP, int NBW, int XR, bool ONECHUNK, bool BLK>
 __global__ __launch_bounds__(256 * NBW) void expert_gemm_kernel(
     const uint16_t* __restrict__ act, const uint8_t* __restrict__ wq,
     const uint8_t* __restrict__ ws, const int32_t* sorted_ids,  // not restrict: see below
@@ -84,18 +85,21 @@ __global__ __launch_bounds__(256 * NBW) void expert_gemm_kernel(
   const int n_base = (blockIdx.x * NBW + nb) * kRowsPerBlock;
   const int n_row = n_base < N ? n_base + li : li;  // blocks past N compute, never store
 
-  // Weight rows this lane loads.  In the gate/up kernel with one K chunk and
-  // one 16-row block per workgroup, a wave instruction reads 4 rows x 256
-  // contiguous bytes (lane l: row 4*kq + l/16 of the block, MX block
-  // 16*step + l%16), which streams from HBM markedly faster than 16 rows x
-  // 64 bytes; each step's pieces are then exchanged through LDS so that
-  // every lane holds row li, block 16*step + 4*kq + grp, as the MFMAs need.
-  // The other variants load that mapping directly: for down the exchange's
-  // per-step barriers and LDS cost more than the faster stream gains, and
-  // with 4 blocks per workgroup its LDS would lower occupancy.
+  // Weight rows this lane loads.  In the blocked layout the MFMA mapping
+  // (row li, block 16*step + 4*kq + grp) is one contiguous kilobyte per wave
+  // instruction, in lane order.  In the canonical layout it is 16 rows x 64
+  // bytes; there the gate/up kernel with one K chunk and one 16-row block
+  // per workgroup instead reads 4 rows x 256 contiguous bytes per wave
+  // instruction (lane l: row 4*kq + l/16 of the block, MX block
+  // 16*step + l%16), which streams from HBM markedly faster, and exchanges
+  // each step's pieces through LDS so that every lane holds the MFMA
+  // mapping.  The other canonical variants load the mapping directly: for
+  // down the exchange's per-step barriers and LDS cost more than the faster
+  // stream gains, and with 4 blocks per workgroup its LDS would lower
+  // occupancy.
   const size_t q_stride = (size_t)K / 2;
   const size_t s_stride = (size_t)K / 32;
-  constexpr bool XCHG = GATEUP && ONECHUNK && NBW == 1;
+  constexpr bool XCHG = GATEUP && ONECHUNK && NBW == 1 && !BLK;
   const int l_row = XCHG ? (n_base < N ? n_base : 0) + 4 * kq + (lane >> 4) : n_row;
   size_t wrow[NW];
   if (GATEUP) {
@@ -123,7 +127,8 @@ __global__ __launch_bounds__(256 * NBW) void expert_gemm_kernel(
       const int bc = min(b, KB - 1);  // clamped: always a valid address
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
-        wreg[c][w] = *reinterpret_cast<const uint4*>(wq + wrow[w] * q_stride + (size_t)bc * 16);
+        wreg[c][w] = *reinterpret_cast<const uint4*>(wq + wq_row_offset(wrow[w], q_stride, BLK) +
+                                                     (size_t)bc * wq_piece_stride(BLK));
         if constexpr (!ONECHUNK) sreg[c][w] = ws[wrow[w] * s_stride + bc];
       }
     }
@@ -378,7 +383,7 @@ __global__ __launch_bounds__(256 * kFuseMaxK) void down_combine_one_token_kernel
     const uint16_t* __restrict__ h, const uint8_t* __restrict__ wq,
     const uint8_t* __restrict__ ws, const int32_t* sorted_ids,
     const int32_t* __restrict__ tiles, const int32_t* __restrict__ num_tiles,
-    const float* __restrict__ topk_weights, int H, int I, int E, int k,
+    const float* __restrict__ topk_weights, int H, int I, int E, int k, bool blocked,
     uint16_t* __restrict__ out) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int tid = threadIdx.x;
@@ -434,7 +439,8 @@ __global__ __launch_bounds__(256 * kFuseMaxK) void down_combine_one_token_kernel
 #pragma unroll
     for (int c = 0; c < kChunk; ++c) {
       const int bc = min(c * kBlocksPerStep + kq * 4 + grp, KB - 1);
-      wreg[c] = *reinterpret_cast<const uint4*>(wq + wrow * (K / 2) + (size_t)bc * 16);
+      wreg[c] = *reinterpret_cast<const uint4*>(wq + wq_row_offset(wrow, K / 2, blocked) +
+                                                (size_t)bc * wq_piece_stride(blocked));
     }
     wait_vmcnt<kChunk>();  // activations and the scale piece
     if (gl < KB) *reinterpret_cast<uint4*>(s_sc + gl * 16) = sp;
@@ -509,7 +515,7 @@ int pick_xr(int T, int BM, int K, int E, int k) {
   return xr;
 }
 
-template <bool GATEUP>
+template <bool GATEUP, bool BLK>
 void launch_expert_gemm(const uint16_t* act, const uint8_t* wq, const uint8_t* ws,
                         const int32_t* sorted_ids, const int32_t* tiles,
                         const int32_t* num_tiles, int tiles_max, int T, int H, int I, int E,
@@ -526,11 +532,11 @@ void launch_expert_gemm(const uint16_t* act, const uint8_t* wq, const uint8_t* w
     if (lds < red_bytes_1 * (NBW_)) lds = red_bytes_1 * (NBW_);                                 \
     dim3 grid((nblk16 + (NBW_) - 1) / (NBW_), tiles_max);                                       \
     if (one_chunk)                                                                              \
-      hipLaunchKernelGGL((expert_gemm_kernel<GATEUP, NBW_, XR_, true>), grid, dim3(256 * (NBW_)), \
+      hipLaunchKernelGGL((expert_gemm_kernel<GATEUP, NBW_, XR_, true, BLK>), grid, dim3(256 * (NBW_)), \
                          lds, stream, act, wq, ws, sorted_ids, tiles, num_tiles, T, H, I, E, k,  \
                          out);                                                                  \
     else                                                                                        \
-      hipLaunchKernelGGL((expert_gemm_kernel<GATEUP, NBW_, XR_, false>), grid,                  \
+      hipLaunchKernelGGL((expert_gemm_kernel<GATEUP, NBW_, XR_, false, BLK>), grid,             \
                          dim3(256 * (NBW_)), lds, stream, act, wq, ws, sorted_ids, tiles,       \
                          num_tiles, T, H, I, E, k, out);                                        \
   } while (0)
@@ -549,14 +555,18 @@ void launch_expert_gemm(const uint16_t* act, const uint8_t* wq, const uint8_t* w
 void launch_gateup_swiglu(const uint16_t* x, const uint8_t* w13_q, const uint8_t* w13_s,
                           const int32_t* sorted_ids, const int32_t* tiles,
                           const int32_t* num_tiles, int tiles_max, int T, int H, int I, int E,
-                          int k, int BM, uint16_t* h, hipStream_t stream) {
+                          int k, int BM, bool blocked, uint16_t* h, hipStream_t stream) {
   if (expert_mma_ok(T, H, I, E, k, BM)) {
     launch_expert_mma(true, x, w13_q, w13_s, sorted_ids, tiles, num_tiles, tiles_max, T, H, I, E,
-                      k, h, stream);
+                      k, blocked, h, stream);
     return;
   }
-  launch_expert_gemm<true>(x, w13_q, w13_s, sorted_ids, tiles, num_tiles, tiles_max, T, H, I, E,
-                           k, BM, h, stream);
+  if (blocked)
+    launch_expert_gemm<true, true>(x, w13_q, w13_s, sorted_ids, tiles, num_tiles, tiles_max, T,
+                                   H, I, E, k, BM, h, stream);
+  else
+    launch_expert_gemm<true, false>(x, w13_q, w13_s, sorted_ids, tiles, num_tiles, tiles_max, T,
+                                    H, I, E, k, BM, h, stream);
 }
 
 bool down_combine_one_token_ok(int T, int H, int I, int k) {
@@ -566,25 +576,30 @@ bool down_combine_one_token_ok(int T, int H, int I, int k) {
 void launch_down_combine_one_token(const uint16_t* h, const uint8_t* w2_q, const uint8_t* w2_s,
                                    const int32_t* sorted_ids, const int32_t* tiles,
                                    const int32_t* num_tiles, const float* topk_weights, int H,
-                                   int I, int E, int k, uint16_t* out, hipStream_t stream) {
+                                   int I, int E, int k, bool blocked, uint16_t* out,
+                                   hipStream_t stream) {
   const size_t red_bytes = (size_t)kFuseMaxK * 4 * 16 * sizeof(float);
   const size_t lds = (size_t)kFuseMaxK * (fuse_row_region(I) + kScaleRunMax) + red_bytes;
   hipLaunchKernelGGL(down_combine_one_token_kernel, dim3(H / kRowsPerBlock),
                      dim3(256 * kFuseMaxK), lds, stream, h, w2_q, w2_s, sorted_ids, tiles,
-                     num_tiles, topk_weights, H, I, E, k, out);
+                     num_tiles, topk_weights, H, I, E, k, blocked, out);
 }
 
 void launch_down(const uint16_t* h, const uint8_t* w2_q, const uint8_t* w2_s,
                  const int32_t* sorted_ids, const int32_t* tiles, const int32_t* num_tiles,
-                 int tiles_max, int T, int H, int I, int E, int k, int BM, float* y,
-                 hipStream_t stream) {
+                 int tiles_max, int T, int H, int I, int E, int k, int BM, bool blocked,
+                 float* y, hipStream_t stream) {
   if (expert_mma_ok(T, H, I, E, k, BM)) {
     launch_expert_mma(false, h, w2_q, w2_s, sorted_ids, tiles, num_tiles, tiles_max, T, H, I, E,
-                      k, y, stream);
+                      k, blocked, y, stream);
     return;
   }
-  launch_expert_gemm<false>(h, w2_q, w2_s, sorted_ids, tiles, num_tiles, tiles_max, T, H, I, E,
-                            k, BM, y, stream);
+  if (blocked)
+    launch_expert_gemm<false, true>(h, w2_q, w2_s, sorted_ids, tiles, num_tiles, tiles_max, T, H,
+                                    I, E, k, BM, y, stream);
+  else
+    launch_expert_gemm<false, false>(h, w2_q, w2_s, sorted_ids, tiles, num_tiles, tiles_max, T,
+                                     H, I, E, k, BM, y, stream);
 }
 
 }  // namespace moe

@@ -133,6 +133,7 @@ struct UnitCtx {
   const long long* s_rowoff;
   const uint16_t* act;
   const uint8_t* w_row[2];  // this lane's weight row for each of the wave's direct loads
+  int w_pstride;            // bytes between consecutive MX blocks of a row (layout)
   int w_swz[2];             // the MX block (0/1) of the stage it fetches
   int w_dst[2];             // its 1 KB slot within the stage's weight area
   int soff[kNFW];           // slab offset of this lane's row, per fragment
@@ -149,7 +150,7 @@ __device__ __forceinline__ void issue_w(const UnitCtx& c, int it, int st) {
   for (int t = 0; t < 2; ++t) {
     if (t < 2 - c.mg) {
       const int blk = min(2 * it + c.w_swz[t], c.KB - 1);  // past K: any data, scale 0
-      lds_load16(c.w_row[t] + (size_t)blk * 16, wsb + c.w_dst[t]);
+      lds_load16(c.w_row[t] + (size_t)blk * c.w_pstride, wsb + c.w_dst[t]);
     }
   }
 }
@@ -377,7 +378,7 @@ __global__ __launch_bounds__(kThreads, 1) void expert_mma_kernel(
     const uint16_t* __restrict__ act, const uint8_t* __restrict__ wq,
     const uint8_t* __restrict__ ws, const int32_t* sorted_ids,
     const int32_t* __restrict__ tiles, const int32_t* __restrict__ num_tiles, int T, int H,
-    int I, int E, int k, int ncb, void* __restrict__ out) {
+    int I, int E, int k, int ncb, bool blocked, void* __restrict__ out) {
   constexpr int kCols = GATEUP ? kColsGateUp : kColsDown;  // output columns per slice
   constexpr int kRunRows = 4 * kCols;                        // rows per scale run
   constexpr int kRuns = GATEUP ? 2 : 1;                      // gate + up, or w2
@@ -478,10 +479,11 @@ __global__ __launch_bounds__(kThreads, 1) void expert_mma_kernel(
     int ch, rr;
     slice_row(c.wn, rl, ch, rr);
     const size_t gr = (size_t)e * mrows + (size_t)ch * I + min(c.n0 + rr, nvalid - 1);
-    c.w_row[t] = wq + gr * (size_t)(c.K / 2);
+    c.w_row[t] = wq + wq_row_offset(gr, (size_t)(c.K / 2), blocked);
     c.w_swz[t] = (c.lane & 1) ^ ((rl >> 3) & 1);
     c.w_dst[t] = c.wn * kWSlice + q * 1024;
   }
+  c.w_pstride = wq_piece_stride(blocked);
   for (int s = 0; s < 4 && s < c.niters; ++s) issue_w(c, s, s);
 
   // ---- prologue 3: the row table
@@ -551,18 +553,18 @@ bool expert_mma_ok(int T, int H, int I, int E, int k, int BM) {
 
 void launch_expert_mma(bool gateup, const uint16_t* act, const uint8_t* wq, const uint8_t* ws,
                        const int32_t* sorted_ids, const int32_t* tiles, const int32_t* num_tiles,
-                       int tiles_max, int T, int H, int I, int E, int k, void* out,
-                       hipStream_t stream) {
+                       int tiles_max, int T, int H, int I, int E, int k, bool blocked,
+                       void* out, hipStream_t stream) {
   const int N = gateup ? I : H;
   const int ncol = 4 * (gateup ? kColsGateUp : kColsDown);
   const int ncb = (N + ncol - 1) / ncol;
   const dim3 grid((unsigned)tiles_max * (unsigned)ncb);
   if (gateup)
     hipLaunchKernelGGL(expert_mma_kernel<true>, grid, dim3(kThreads), kLdsBytes, stream, act, wq, ws,
-                       sorted_ids, tiles, num_tiles, T, H, I, E, k, ncb, out);
+                       sorted_ids, tiles, num_tiles, T, H, I, E, k, ncb, blocked, out);
   else
     hipLaunchKernelGGL(expert_mma_kernel<false>, grid, dim3(kThreads), kLdsBytes, stream, act, wq, ws,
-                       sorted_ids, tiles, num_tiles, T, H, I, E, k, ncb, out);
+                       sorted_ids, tiles, num_tiles, T, H, I, E, k, ncb, blocked, out);
 }
 
 }  // namespace moe

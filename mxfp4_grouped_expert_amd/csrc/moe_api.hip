@@ -41,6 +41,7 @@ size_t round256(size_t n) { return (n + 255) & ~size_t(255); }
 
 bool valid_bm(int BM) { return BM == 16 || BM == 32 || BM == 64 || BM == 128; }
 bool gating_ok(int gating) { return gating == MOE_GATING_SOFTMAX || gating == MOE_GATING_SIGMOID; }
+bool layout_ok(int layout) { return layout == MOE_LAYOUT_CANONICAL || layout == MOE_LAYOUT_BLOCKED; }
 
 moe_status finish_launches() {
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
@@ -175,11 +176,25 @@ bool forward_shape_ok(int T, int H, int I, int E, int k, int BM) {
 
 }  // namespace
 
+moe_status moe_repack_weights(const uint8_t* q, int64_t rows, int K, uint8_t* q_blocked,
+                              struct ihipStream_t* stream) {
+  if (rows <= 0 || rows % 16 != 0 || K <= 0 || K % 32 != 0 || K > MOE_MAX_DIM ||
+      rows > (int64_t(1) << 40) / K)
+    return MOE_ERR_SHAPE;
+  if (!q || !q_blocked) return MOE_ERR_NULL;
+  if (!aligned16(q) || !aligned16(q_blocked)) return MOE_ERR_ALIGN;
+  moe_status st = check_device();
+  if (st != MOE_OK) return st;
+  (void)hipGetLastError();
+  moe::launch_repack_blocked(q, rows, K, q_blocked, as_stream(stream));
+  return finish_launches();
+}
+
 moe_status moe_gateup_swiglu(const uint16_t* x, const uint8_t* w13_q, const uint8_t* w13_s,
                              const int32_t* sorted_ids, const int32_t* tiles,
                              const int32_t* num_tiles, int T, int H, int I, int E, int k, int BM,
-                             uint16_t* h, struct ihipStream_t* stream) {
-  if (!forward_shape_ok(T, H, I, E, k, BM)) return MOE_ERR_SHAPE;
+                             int layout, uint16_t* h, struct ihipStream_t* stream) {
+  if (!forward_shape_ok(T, H, I, E, k, BM) || !layout_ok(layout)) return MOE_ERR_SHAPE;
   if (T == 0) return MOE_OK;
   if (!x || !w13_q || !w13_s || !sorted_ids || !tiles || !num_tiles || !h) return MOE_ERR_NULL;
   if (!aligned16(x) || !aligned16(w13_q) || !aligned16(w13_s)) return MOE_ERR_ALIGN;
@@ -187,16 +202,16 @@ moe_status moe_gateup_swiglu(const uint16_t* x, const uint8_t* w13_q, const uint
   if (st != MOE_OK) return st;
   (void)hipGetLastError();
   moe::launch_gateup_swiglu(x, w13_q, w13_s, sorted_ids, tiles, num_tiles,
-                            (int)moe_tiles_max(T, k, E, BM), T, H, I, E, k, BM, h,
-                            as_stream(stream));
+                            (int)moe_tiles_max(T, k, E, BM), T, H, I, E, k, BM,
+                            layout == MOE_LAYOUT_BLOCKED, h, as_stream(stream));
   return finish_launches();
 }
 
 moe_status moe_down(const uint16_t* h, const uint8_t* w2_q, const uint8_t* w2_s,
                     const int32_t* sorted_ids, const int32_t* tiles, const int32_t* num_tiles,
-                    int T, int H, int I, int E, int k, int BM, float* y,
+                    int T, int H, int I, int E, int k, int BM, int layout, float* y,
                     struct ihipStream_t* stream) {
-  if (!forward_shape_ok(T, H, I, E, k, BM)) return MOE_ERR_SHAPE;
+  if (!forward_shape_ok(T, H, I, E, k, BM) || !layout_ok(layout)) return MOE_ERR_SHAPE;
   if (T == 0) return MOE_OK;
   if (!h || !w2_q || !w2_s || !sorted_ids || !tiles || !num_tiles || !y) return MOE_ERR_NULL;
   if (!aligned16(h) || !aligned16(w2_q) || !aligned16(w2_s)) return MOE_ERR_ALIGN;
@@ -204,7 +219,7 @@ moe_status moe_down(const uint16_t* h, const uint8_t* w2_q, const uint8_t* w2_s,
   if (st != MOE_OK) return st;
   (void)hipGetLastError();
   moe::launch_down(h, w2_q, w2_s, sorted_ids, tiles, num_tiles, (int)moe_tiles_max(T, k, E, BM),
-                   T, H, I, E, k, BM, y, as_stream(stream));
+                   T, H, I, E, k, BM, layout == MOE_LAYOUT_BLOCKED, y, as_stream(stream));
   return finish_launches();
 }
 
@@ -226,9 +241,9 @@ moe_status moe_combine(const float* y, const float* topk_weights, int T, int H, 
 moe_status moe_forward(const uint16_t* x, const uint8_t* w13_q, const uint8_t* w13_s,
                        const uint8_t* w2_q, const uint8_t* w2_s, const float* topk_weights,
                        const int32_t* sorted_ids, const int32_t* tiles, const int32_t* num_tiles,
-                       int T, int H, int I, int E, int k, int BM, void* workspace,
+                       int T, int H, int I, int E, int k, int BM, int layout, void* workspace,
                        size_t workspace_bytes, uint16_t* out, struct ihipStream_t* stream) {
-  if (!forward_shape_ok(T, H, I, E, k, BM)) return MOE_ERR_SHAPE;
+  if (!forward_shape_ok(T, H, I, E, k, BM) || !layout_ok(layout)) return MOE_ERR_SHAPE;
   if (T == 0) return MOE_OK;
   if (!x || !w13_q || !w13_s || !w2_q || !w2_s || !topk_weights || !sorted_ids || !tiles ||
       !num_tiles || !workspace || !out)
@@ -245,16 +260,17 @@ moe_status moe_forward(const uint16_t* x, const uint8_t* w13_q, const uint8_t* w
   uint16_t* h = static_cast<uint16_t*>(workspace);
   float* y = reinterpret_cast<float*>(static_cast<char*>(workspace) + round256(nslots * I * 2));
   hipStream_t s = as_stream(stream);
+  const bool blocked = layout == MOE_LAYOUT_BLOCKED;
   moe::launch_gateup_swiglu(x, w13_q, w13_s, sorted_ids, tiles, num_tiles, (int)tmax, T, H, I, E,
-                            k, BM, h, s);
+                            k, BM, blocked, h, s);
   if (moe::down_combine_one_token_ok(T, H, I, k)) {
     // one token: down GEMM and combine in one launch, bit-identical to the two
     moe::launch_down_combine_one_token(h, w2_q, w2_s, sorted_ids, tiles, num_tiles, topk_weights,
-                                       H, I, E, k, out, s);
+                                       H, I, E, k, blocked, out, s);
     return finish_launches();
   }
-  moe::launch_down(h, w2_q, w2_s, sorted_ids, tiles, num_tiles, (int)tmax, T, H, I, E, k, BM, y,
-                   s);
+  moe::launch_down(h, w2_q, w2_s, sorted_ids, tiles, num_tiles, (int)tmax, T, H, I, E, k, BM,
+                   blocked, y, s);
   moe::launch_combine(y, topk_weights, T, H, k, out, s);
   return finish_launches();
 }
@@ -272,14 +288,14 @@ size_t moe_layer_one_token_sync_bytes(int H) {
 moe_status moe_layer_one_token(const uint16_t* x, const float* w_router, const float* bias,
                                const uint8_t* w13_q, const uint8_t* w13_s, const uint8_t* w2_q,
                                const uint8_t* w2_s, int H, int I, int E, int k, int gating,
-                               int32_t* topk_ids, float* topk_weights, double* logits,
+                               int layout, int32_t* topk_ids, float* topk_weights, double* logits,
                                int32_t* expert_offsets, int32_t* sorted_ids, int32_t* tiles,
                                int32_t* num_tiles, void* workspace, size_t workspace_bytes,
                                uint16_t* out, struct ihipStream_t* stream) {
   if (H <= 0 || I <= 0 || H > MOE_MAX_DIM || I > MOE_MAX_DIM || E < 1 ||
       E > MOE_MAX_EXPERTS || k < 1 || k > MOE_MAX_TOPK || k > E ||
       (int64_t)E * 2 * I >= (int64_t(1) << 31) || !moe::layer_one_token_ok(H, I, E, k) ||
-      !gating_ok(gating))
+      !gating_ok(gating) || !layout_ok(layout))
     return MOE_ERR_SHAPE;
   if (!x || !w_router || !w13_q || !w13_s || !w2_q || !w2_s || !topk_ids || !topk_weights ||
       !expert_offsets || !sorted_ids || !tiles || !num_tiles || !workspace || !out)
@@ -292,7 +308,7 @@ moe_status moe_layer_one_token(const uint16_t* x, const float* w_router, const f
   if (st != MOE_OK) return st;
   (void)hipGetLastError();
   moe::launch_layer_one_token(x, w_router, bias, w13_q, w13_s, w2_q, w2_s, H, I, E, k, gating,
-                              topk_ids,
+                              layout == MOE_LAYOUT_BLOCKED, topk_ids,
                               topk_weights, logits, expert_offsets, sorted_ids, tiles, num_tiles,
                               workspace, out, as_stream(stream));
   return finish_launches();

@@ -84,6 +84,18 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Layouts of a packed MXFP4 code matrix (K/2 bytes per weight row, one
+// 16-byte piece per 32-element MX block).  Canonical: row-major.  Blocked:
+// within each group of 16 consecutive rows the pieces are stored block by
+// block, piece (row, b) at group offset b*256 + (row % 16)*16, so the 16 rows
+// of one MX block are 256 contiguous bytes and 4 consecutive blocks of a
+// 16-row group are one contiguous kilobyte.  Byte offset of piece (row, 0)
+// and the distance between consecutive pieces of one row:
+__device__ __forceinline__ size_t wq_row_offset(size_t row, size_t row_bytes, bool blocked) {
+  return blocked ? (row & ~size_t(15)) * row_bytes + (row & 15) * 16 : row * row_bytes;
+}
+__device__ __forceinline__ int wq_piece_stride(bool blocked) { return blocked ? 256 : 16; }
+
 // Number of lanes below this one whose bit is set in `mask`.
 __device__ __forceinline__ int lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),

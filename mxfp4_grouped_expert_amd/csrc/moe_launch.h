@@ -43,26 +43,27 @@ void launch_build_tiles(const int32_t* topk_ids, int N, int E, int BM, int32_t* 
 void launch_gateup_swiglu(const uint16_t* x, const uint8_t* w13_q, const uint8_t* w13_s,
                           const int32_t* sorted_ids, const int32_t* tiles,
                           const int32_t* num_tiles, int tiles_max, int T, int H, int I, int E,
-                          int k, int BM, uint16_t* h, hipStream_t stream);
+                          int k, int BM, bool blocked, uint16_t* h, hipStream_t stream);
 void launch_down(const uint16_t* h, const uint8_t* w2_q, const uint8_t* w2_s,
                  const int32_t* sorted_ids, const int32_t* tiles, const int32_t* num_tiles,
-                 int tiles_max, int T, int H, int I, int E, int k, int BM, float* y,
-                 hipStream_t stream);
+                 int tiles_max, int T, int H, int I, int E, int k, int BM, bool blocked,
+                 float* y, hipStream_t stream);
 
 // Down GEMM and combine of a single token in one launch (no y buffer).
 bool down_combine_one_token_ok(int T, int H, int I, int k);
 void launch_down_combine_one_token(const uint16_t* h, const uint8_t* w2_q, const uint8_t* w2_s,
                                    const int32_t* sorted_ids, const int32_t* tiles,
                                    const int32_t* num_tiles, const float* topk_weights, int H,
-                                   int I, int E, int k, uint16_t* out, hipStream_t stream);
+                                   int I, int E, int k, bool blocked, uint16_t* out,
+                                   hipStream_t stream);
 
 // Large-tile (prefill) form of the grouped GEMMs: 128-row tiles, LDS-staged
 // operands.  expert_mma_ok says when the launchers above use it.
 bool expert_mma_ok(int T, int H, int I, int E, int k, int BM);
 void launch_expert_mma(bool gateup, const uint16_t* act, const uint8_t* wq, const uint8_t* ws,
                        const int32_t* sorted_ids, const int32_t* tiles, const int32_t* num_tiles,
-                       int tiles_max, int T, int H, int I, int E, int k, void* out,
-                       hipStream_t stream);
+                       int tiles_max, int T, int H, int I, int E, int k, bool blocked,
+                       void* out, hipStream_t stream);
 
 // The whole layer for one token in one launch (routing, gate/up, down and
 // combine; bit-identical to the separate launches).  The workspace starts
@@ -74,10 +75,14 @@ size_t layer_one_token_bytes(int H, int I, int E, int k);
 void launch_layer_one_token(const uint16_t* x, const float* w_router, const float* bias,
                             const uint8_t* w13_q, const uint8_t* w13_s, const uint8_t* w2_q,
                             const uint8_t* w2_s, int H, int I, int E, int k, int gating,
-                            int32_t* topk_ids,
+                            bool blocked, int32_t* topk_ids,
                             float* topk_weights, double* logits, int32_t* expert_offsets,
                             int32_t* sorted_ids, int32_t* tiles, int32_t* num_tiles,
                             void* workspace, uint16_t* out, hipStream_t stream);
+
+// Code matrix [rows][K/2] (canonical) -> blocked layout, out of place.
+void launch_repack_blocked(const uint8_t* q, long long rows, int K, uint8_t* qb,
+                           hipStream_t stream);
 
 // Weighted combine back to token order.
 void launch_combine(const float* y, const float* topk_weights, int T, int H, int k,

@@ -158,6 +158,7 @@ struct Args {
   const uint8_t* w2_q;
   const uint8_t* w2_s;
   int H, I, E, k, gating;
+  bool blocked;  // code matrices in the blocked layout
   int split_len, splits, n_route;
   int32_t* topk_ids;
   float* topk_weights;
@@ -236,13 +237,15 @@ __device__ void routing_role(const Args& a, int rid, unsigned char* lds) {
 
 // ----------------------------------------------------------------- gate/up
 // Tile g (sorted position g, one row), 16-row block cb of the gate and up
-// halves.  Same lane roles, loads, exchange, MFMA order, split-K order and
-// epilogue as expert_gemm_kernel<true, 1, 1, true> for one token.
+// halves.  Same lane roles, loads, exchange (canonical layout only), MFMA
+// order, split-K order and epilogue as expert_gemm_kernel<true, 1, 1, true,
+// BLK> for one token.
 struct GateupLoads {
   uint4 w[kChunk][2];  // this lane's weight pieces, per step and half
   uint4 spiece;        // this thread's piece of the two scale runs
 };
 
+template <bool BLK>
 __device__ __forceinline__ void gateup_issue(const Args& a, int cb, int e, unsigned char* act,
                                              GateupLoads& L) {
   const int I = a.I, K = a.H, KB = K / 32;
@@ -260,17 +263,22 @@ __device__ __forceinline__ void gateup_issue(const Args& a, int cb, int e, unsig
   L.spiece = *reinterpret_cast<const uint4*>(
       a.w13_s + ((size_t)e * 2 * I + (size_t)pr * I + n_base) * KB + (size_t)min(pp, KB - 1) * 16);
   asm volatile("" ::: "memory");
-  const int l_row = n_base + 4 * kq + (lane >> 4);
+  // canonical: 4 rows x 256 bytes per wave instruction, exchanged later;
+  // blocked: the MFMA mapping itself, one contiguous kilobyte
+  const int l_row = BLK ? n_base + (lane & 15) : n_base + 4 * kq + (lane >> 4);
   const size_t wrow[2] = {(size_t)e * 2 * I + l_row, (size_t)e * 2 * I + I + l_row};
 #pragma unroll
   for (int c = 0; c < kChunk; ++c) {
-    const int bc = min(c * kBlocksPerStep + (lane & 15), KB - 1);
+    const int bc = min(BLK ? c * kBlocksPerStep + kq * 4 + (lane >> 4)
+                           : c * kBlocksPerStep + (lane & 15), KB - 1);
 #pragma unroll
     for (int w = 0; w < 2; ++w)
-      L.w[c][w] = *reinterpret_cast<const uint4*>(a.w13_q + wrow[w] * (K / 2) + (size_t)bc * 16);
+      L.w[c][w] = *reinterpret_cast<const uint4*>(a.w13_q + wq_row_offset(wrow[w], K / 2, BLK) +
+                                                  (size_t)bc * wq_piece_stride(BLK));
   }
 }
 
+template <bool BLK>
 __device__ __forceinline__ void gateup_finish(const Args& a, int g, int cb, unsigned stamp,
                                               unsigned char* lds, GateupLoads& L) {
   constexpr int NW = 2;
@@ -297,17 +305,19 @@ __device__ __forceinline__ void gateup_finish(const Args& a, int g, int cb, unsi
   floatx4 acc[NW] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
   for (int c = 0; c < kChunk; ++c) {
-    unsigned char* slot = s_ring + (c & 1) * NW * kRowsPerBlock * 256;
-    const int wr16 = 4 * kq + (lane >> 4);
+    if constexpr (!BLK) {
+      unsigned char* slot = s_ring + (c & 1) * NW * kRowsPerBlock * 256;
+      const int wr16 = 4 * kq + (lane >> 4);
 #pragma unroll
-    for (int w = 0; w < NW; ++w)
-      *reinterpret_cast<uint4*>(slot + (w * kRowsPerBlock + wr16) * 256 +
-                                (((lane & 15) ^ wr16) << 4)) = L.w[c][w];
-    lds_barrier();
+      for (int w = 0; w < NW; ++w)
+        *reinterpret_cast<uint4*>(slot + (w * kRowsPerBlock + wr16) * 256 +
+                                  (((lane & 15) ^ wr16) << 4)) = L.w[c][w];
+      lds_barrier();
 #pragma unroll
-    for (int w = 0; w < NW; ++w)
-      L.w[c][w] = *reinterpret_cast<const uint4*>(
-          slot + (w * kRowsPerBlock + li) * 256 + (((4 * kq + grp) ^ li) << 4));
+      for (int w = 0; w < NW; ++w)
+        L.w[c][w] = *reinterpret_cast<const uint4*>(
+            slot + (w * kRowsPerBlock + li) * 256 + (((4 * kq + grp) ^ li) << 4));
+    }
 #pragma unroll
     for (int w = 0; w < NW; ++w)
       asm volatile("" : "+v"(L.w[c][w].x), "+v"(L.w[c][w].y), "+v"(L.w[c][w].z),
@@ -366,7 +376,8 @@ __device__ __forceinline__ void down_issue(const Args& a, int cb, int e, DownLoa
 #pragma unroll
   for (int c = 0; c < kChunk; ++c) {
     const int bc = min(c * kBlocksPerStep + kq * 4 + grp, KB - 1);
-    L.w[c] = *reinterpret_cast<const uint4*>(a.w2_q + wrow * (K / 2) + (size_t)bc * 16);
+    L.w[c] = *reinterpret_cast<const uint4*>(a.w2_q + wq_row_offset(wrow, K / 2, a.blocked) +
+                                             (size_t)bc * wq_piece_stride(a.blocked));
   }
   L.spiece = *reinterpret_cast<const uint4*>(
       a.w2_s + ((size_t)e * a.H + n_base) * KB + (size_t)min(tid, KB - 1) * 16);
@@ -470,6 +481,7 @@ __device__ __forceinline__ void down_finish(const Args& a, int g, int cb, int sl
 // other tiles' jobs of that block.  A down job's weights are requested once
 // the workgroup's gate/up job is done (requested together, the two streams
 // measured slower).
+template <bool BLK>
 __device__ void gemm_role(const Args& a, int j, unsigned char* lds) {
   const int ncbI = a.I / kRowsPerBlock, ncbH = a.H / kRowsPerBlock;
   unsigned* s_plan = reinterpret_cast<unsigned*>(lds + kRegion0 + 2 * kScaleRunMax +
@@ -500,8 +512,8 @@ __device__ void gemm_role(const Args& a, int j, unsigned char* lds) {
 
   if (has_gu) {
     GateupLoads gl;
-    gateup_issue(a, j - g_gu * ncbI, expert(p_gu), lds, gl);
-    gateup_finish(a, g_gu, j - g_gu * ncbI, stamp, lds, gl);
+    gateup_issue<BLK>(a, j - g_gu * ncbI, expert(p_gu), lds, gl);
+    gateup_finish<BLK>(a, g_gu, j - g_gu * ncbI, stamp, lds, gl);
   }
   for (int t = t0; t < a.k; ++t) {
     const int cb = j - (t + 1) * ncbI;
@@ -527,12 +539,13 @@ __device__ void gemm_role(const Args& a, int j, unsigned char* lds) {
 
 constexpr int kLdsBytes = kRegion0 + 2 * kScaleRunMax + 2 * 2 * kRowsPerBlock * 256 + 16;
 
+template <bool BLK>
 __global__ __launch_bounds__(kThreads, 4) void moe_layer_one_token_kernel(Args a) {
   __shared__ __align__(16) unsigned char lds[kLdsBytes];
   if ((int)blockIdx.x < a.n_route)
     routing_role(a, blockIdx.x, lds);
   else
-    gemm_role(a, blockIdx.x - a.n_route, lds);
+    gemm_role<BLK>(a, blockIdx.x - a.n_route, lds);
 }
 
 size_t round_up(size_t n) { return (n + 255) / 256 * 256; }
@@ -561,7 +574,7 @@ size_t layer_one_token_bytes(int H, int I, int E, int k) {
 void launch_layer_one_token(const uint16_t* x, const float* w_router, const float* bias,
                             const uint8_t* w13_q, const uint8_t* w13_s, const uint8_t* w2_q,
                             const uint8_t* w2_s, int H, int I, int E, int k, int gating,
-                            int32_t* topk_ids,
+                            bool blocked, int32_t* topk_ids,
                             float* topk_weights, double* logits, int32_t* expert_offsets,
                             int32_t* sorted_ids, int32_t* tiles, int32_t* num_tiles,
                             void* workspace, uint16_t* out, hipStream_t stream) {
@@ -570,7 +583,7 @@ void launch_layer_one_token(const uint16_t* x, const float* w_router, const floa
   Args a;
   a.x = x; a.w_router = w_router; a.bias = bias;
   a.w13_q = w13_q; a.w13_s = w13_s; a.w2_q = w2_q; a.w2_s = w2_s;
-  a.H = H; a.I = I; a.E = E; a.k = k; a.gating = gating;
+  a.H = H; a.I = I; a.E = E; a.k = k; a.gating = gating; a.blocked = blocked;
   a.split_len = p.split_len;
   a.splits = p.splits;
   a.n_route = p.splits * ((E + kExpPerBlock - 1) / kExpPerBlock);
@@ -587,7 +600,11 @@ void launch_layer_one_token(const uint16_t* x, const float* w_router, const floa
   a.out = out;
   const int ncbI = I / kRowsPerBlock, ncbH = H / kRowsPerBlock;
   const int grid = a.n_route + k * ncbI + ncbH;
-  hipLaunchKernelGGL(moe_layer_one_token_kernel, dim3(grid), dim3(kThreads), 0, stream, a);
+  if (blocked)
+    hipLaunchKernelGGL(moe_layer_one_token_kernel<true>, dim3(grid), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(moe_layer_one_token_kernel<false>, dim3(grid), dim3(kThreads), 0, stream,
+                       a);
 }
 
 }  // namespace moe

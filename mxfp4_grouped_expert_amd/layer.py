@@ -4,8 +4,10 @@ A call enqueues the library's entry points (moe_route, moe_build_tiles,
 moe_forward; for small batches moe_route_tiles + moe_forward; for one token
 the single-launch moe_layer_one_token) on the current stream with
 preallocated outputs and workspaces, so it allocates nothing per call and
-can be captured in a HIP graph.  Weights are device tensors in the library's
-canonical layout (see include/moe_mxfp4.h).
+can be captured in a HIP graph.  Weights are given as device tensors in the
+library's canonical layout (see include/moe_mxfp4.h); with layout="blocked"
+the layer repacks the packed codes once, at construction, and its kernels
+read the blocked copy.
 """
 from __future__ import annotations
 
@@ -20,17 +22,23 @@ from . import binding as B
 class MoeLayer:
     def __init__(self, w_router: torch.Tensor, bias: Optional[torch.Tensor],
                  w13_q: torch.Tensor, w13_s: torch.Tensor, w2_q: torch.Tensor,
-                 w2_s: torch.Tensor, k: int, gating: str = "softmax"):
+                 w2_s: torch.Tensor, k: int, gating: str = "softmax",
+                 layout: str = "canonical"):
         self.device = w13_q.device
         self.gating = B.gating_code(gating)
+        self.layout = B.layout_code(layout)
         self.E, I2, Hh = w13_q.shape
         self.H, self.I, self.k = Hh * 2, I2 // 2, int(k)
         self.w_router, self.bias = w_router, bias
-        self.w13_q, self.w13_s, self.w2_q, self.w2_s = w13_q, w13_s, w2_q, w2_s
+        self.set_weights(w13_q, w13_s, w2_q, w2_s, repack=True)
         self.T = None
 
-    def set_weights(self, w13_q, w13_s, w2_q, w2_s):
-        """Point the layer at another copy of the expert weights (same shapes)."""
+    def set_weights(self, w13_q, w13_s, w2_q, w2_s, repack: bool = False):
+        """Point the layer at another copy of the expert weights (same shapes).
+        The codes are taken as they are (already in the layer's layout) unless
+        repack is set, in which case canonical codes are repacked to it."""
+        if repack and self.layout == B.LAYOUTS["blocked"]:
+            w13_q, w2_q = B.moe_repack_weights(w13_q), B.moe_repack_weights(w2_q)
         self.w13_q, self.w13_s, self.w2_q, self.w2_s = w13_q, w13_s, w2_q, w2_s
 
     def plan(self, T: int, BM: Optional[int] = None, one_launch: bool = True):
@@ -110,7 +118,8 @@ class MoeLayer:
         h, _ = self._h_y()
         B._check(lib.moe_gateup_swiglu(p(x), p(self.w13_q), p(self.w13_s), p(self.sorted_ids),
                                        p(self.tiles), p(self.num_tiles), self.T, self.H, self.I,
-                                       self.E, self.k, self.BM, p(h), s), "moe_gateup_swiglu")
+                                       self.E, self.k, self.BM, self.layout, p(h), s),
+                 "moe_gateup_swiglu")
 
     def down_only(self):
         """moe_down from the h workspace into the y workspace."""
@@ -119,7 +128,7 @@ class MoeLayer:
         h, y = self._h_y()
         B._check(lib.moe_down(p(h), p(self.w2_q), p(self.w2_s), p(self.sorted_ids), p(self.tiles),
                               p(self.num_tiles), self.T, self.H, self.I, self.E, self.k, self.BM,
-                              p(y), s), "moe_down")
+                              self.layout, p(y), s), "moe_down")
 
     def combine_only(self):
         """moe_combine from the y workspace into the layer's output."""
@@ -141,7 +150,8 @@ class MoeLayer:
         if self.one_launch:
             B._check(lib.moe_layer_one_token(p(x), p(self.w_router), p(self.bias), p(self.w13_q),
                                              p(self.w13_s), p(self.w2_q), p(self.w2_s), H, I, E,
-                                             k, self.gating, p(self.topk_ids), p(self.topk_weights), None,
+                                             k, self.gating, self.layout, p(self.topk_ids),
+                                             p(self.topk_weights), None,
                                              p(self.offsets), p(self.sorted_ids), p(self.tiles),
                                              p(self.num_tiles), p(self.one_ws),
                                              self.one_ws.numel(), p(self.out), s),
@@ -151,6 +161,6 @@ class MoeLayer:
         self.tiles_only()
         B._check(lib.moe_forward(p(x), p(self.w13_q), p(self.w13_s), p(self.w2_q), p(self.w2_s),
                                  p(self.topk_weights), p(self.sorted_ids), p(self.tiles),
-                                 p(self.num_tiles), T, H, I, E, k, BM, p(self.fwd_ws),
+                                 p(self.num_tiles), T, H, I, E, k, BM, self.layout, p(self.fwd_ws),
                                  self.fwd_ws.numel(), p(self.out), s), "moe_forward")
         return self.out

@@ -90,11 +90,11 @@ def _tiles(**kw):
 
 def _forward(**kw):
     a = dict(x=P, q13=P, s13=P, q2=P, s2=P, w=P, srt=P, tiles=P, nt=P, T=4, H=256, I=512, E=8,
-             k=2, BM=16, ws=P, wsb=1 << 30, out=P)
+             k=2, BM=16, layout=0, ws=P, wsb=1 << 30, out=P)
     a.update(kw)
     return B.load().moe_forward(a["x"], a["q13"], a["s13"], a["q2"], a["s2"], a["w"], a["srt"],
                                 a["tiles"], a["nt"], a["T"], a["H"], a["I"], a["E"], a["k"],
-                                a["BM"], a["ws"], a["wsb"], a["out"], None)
+                                a["BM"], a["layout"], a["ws"], a["wsb"], a["out"], None)
 
 
 @pytest.mark.parametrize("kw,want", [
@@ -124,6 +124,7 @@ def test_build_tiles_validation(kw, want):
     (dict(H=100), SHAPE), (dict(I=48), SHAPE), (dict(k=3, E=2), SHAPE), (dict(BM=24), SHAPE),
     (dict(q13=PMIS), ALIGN), (dict(s13=PMIS), ALIGN), (dict(s2=PMIS), ALIGN),
     (dict(ws=PMIS), ALIGN), (dict(wsb=1000), WORKSPACE), (dict(T=0, x=None), OK),
+    (dict(layout=2), SHAPE), (dict(layout=-1), SHAPE),
 ])
 def test_forward_validation(kw, want):
     assert _forward(**kw) == want
@@ -155,15 +156,17 @@ def test_route_tiles_limits_and_workspace():
 
 
 def _steps(which, **kw):
-    a = dict(x=P, q=P, s=P, srt=P, tiles=P, nt=P, T=4, H=256, I=512, E=8, k=2, BM=16, o=P, w=P)
+    a = dict(x=P, q=P, s=P, srt=P, tiles=P, nt=P, T=4, H=256, I=512, E=8, k=2, BM=16, layout=1,
+             o=P, w=P)
     a.update(kw)
     lib = B.load()
     if which == "gateup":
         return lib.moe_gateup_swiglu(a["x"], a["q"], a["s"], a["srt"], a["tiles"], a["nt"], a["T"],
-                                     a["H"], a["I"], a["E"], a["k"], a["BM"], a["o"], None)
+                                     a["H"], a["I"], a["E"], a["k"], a["BM"], a["layout"], a["o"],
+                                     None)
     if which == "down":
         return lib.moe_down(a["x"], a["q"], a["s"], a["srt"], a["tiles"], a["nt"], a["T"], a["H"],
-                            a["I"], a["E"], a["k"], a["BM"], a["o"], None)
+                            a["I"], a["E"], a["k"], a["BM"], a["layout"], a["o"], None)
     return lib.moe_combine(a["x"], a["w"], a["T"], a["H"], a["k"], a["o"], None)
 
 
@@ -171,11 +174,55 @@ def _steps(which, **kw):
 @pytest.mark.parametrize("kw,want", [
     (dict(x=None), NULL), (dict(o=None), NULL), (dict(H=48), SHAPE), (dict(k=0), SHAPE),
     (dict(x=PMIS), ALIGN), (dict(s=PMIS), ALIGN), (dict(T=0, x=None), OK),
+    (dict(layout=3), SHAPE),
 ])
 def test_step_entry_points_validation(which, kw, want):
-    if which == "combine" and "s" in kw:
-        pytest.skip("moe_combine takes no scale array")
+    if which == "combine" and ("s" in kw or "layout" in kw):
+        pytest.skip("moe_combine takes no weights")
     assert _steps(which, **kw) == want
+
+
+def _one_token(**kw):
+    a = dict(x=P, w=P, bias=None, q13=P, s13=P, q2=P, s2=P, H=256, I=512, E=8, k=2, gating=0,
+             layout=1, ids=P, wts=P, logits=None, off=P, srt=P, tiles=P, nt=P, ws=P,
+             wsb=1 << 24, out=P)
+    a.update(kw)
+    return B.load().moe_layer_one_token(a["x"], a["w"], a["bias"], a["q13"], a["s13"], a["q2"],
+                                        a["s2"], a["H"], a["I"], a["E"], a["k"], a["gating"],
+                                        a["layout"], a["ids"], a["wts"], a["logits"], a["off"],
+                                        a["srt"], a["tiles"], a["nt"], a["ws"], a["wsb"],
+                                        a["out"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(x=None), NULL), (dict(q2=None), NULL), (dict(ws=None), NULL), (dict(out=None), NULL),
+    (dict(H=48), SHAPE), (dict(I=4096), SHAPE), (dict(k=3, E=2), SHAPE), (dict(gating=2), SHAPE),
+    (dict(layout=2), SHAPE), (dict(q13=PMIS), ALIGN), (dict(ws=PMIS), ALIGN),
+    (dict(wsb=256), WORKSPACE),
+])
+def test_one_token_validation(kw, want):
+    assert _one_token(**kw) == want
+
+
+def _repack(**kw):
+    a = dict(q=P, rows=64, K=256, qb=P)
+    a.update(kw)
+    return B.load().moe_repack_weights(a["q"], a["rows"], a["K"], a["qb"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=None), NULL), (dict(qb=None), NULL), (dict(rows=0), SHAPE), (dict(rows=40), SHAPE),
+    (dict(rows=-16), SHAPE), (dict(K=48), SHAPE), (dict(K=0), SHAPE), (dict(K=65536 + 32), SHAPE),
+    (dict(rows=1 << 40, K=65536), SHAPE), (dict(q=PMIS), ALIGN), (dict(qb=PMIS), ALIGN),
+])
+def test_repack_validation(kw, want):
+    assert _repack(**kw) == want
+
+
+def test_layout_names():
+    assert moe.LAYOUTS == {"canonical": 0, "blocked": 1}
+    with pytest.raises(ValueError):
+        B.layout_code("rowmajor")
 
 
 def test_valid_arguments_reach_the_device_check():
@@ -190,6 +237,8 @@ def test_valid_arguments_reach_the_device_check():
     for which in ("gateup", "down", "combine"):
         assert _steps(which) == DEVICE
     assert _route_tiles() == DEVICE
+    assert _one_token() == DEVICE
+    assert _repack() == DEVICE
 
 
 def test_binding_raises_on_error_status():
