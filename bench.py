@@ -51,7 +51,7 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", type=int, default=1, choices=range(7))
     ap.add_argument("--rotations", type=int, default=0, help="weight copies (0 = auto)")
-    ap.add_argument("--layout", default="canonical", choices=("canonical", "blocked"),
+    ap.add_argument("--layout", default="blocked", choices=("canonical", "blocked"),
                     help="byte layout of the packed expert codes (blocked: repacked at load)")
     ap.add_argument("--no-graph", action="store_true", help="time eager calls instead of graphs")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)

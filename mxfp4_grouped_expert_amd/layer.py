@@ -5,9 +5,10 @@ moe_forward; for small batches moe_route_tiles + moe_forward; for one token
 the single-launch moe_layer_one_token) on the current stream with
 preallocated outputs and workspaces, so it allocates nothing per call and
 can be captured in a HIP graph.  Weights are given as device tensors in the
-library's canonical layout (see include/moe_mxfp4.h); with layout="blocked"
-the layer repacks the packed codes once, at construction, and its kernels
-read the blocked copy.
+library's canonical layout (see include/moe_mxfp4.h).  By default
+(layout="blocked") the layer repacks the packed codes once, at construction,
+into a copy its kernels read in the blocked layout (one contiguous kilobyte
+per wave load); layout="canonical" reads the given codes as they are.
 """
 from __future__ import annotations
 
@@ -23,7 +24,7 @@ class MoeLayer:
     def __init__(self, w_router: torch.Tensor, bias: Optional[torch.Tensor],
                  w13_q: torch.Tensor, w13_s: torch.Tensor, w2_q: torch.Tensor,
                  w2_s: torch.Tensor, k: int, gating: str = "softmax",
-                 layout: str = "canonical"):
+                 layout: str = "blocked"):
         self.device = w13_q.device
         self.gating = B.gating_code(gating)
         self.layout = B.layout_code(layout)

@@ -129,7 +129,7 @@ def test_layer_blocked_equals_canonical(T):
     inp = make_random(T=T, H=2880, E=32, k=4, I=2880, seed=55)
     d = to_device(inp)
     args = (d["w_router"], d["bias"], d["w13_q"], d["w13_s"], d["w2_q"], d["w2_s"], 4)
-    canon = moe.MoeLayer(*args).plan(T)
+    canon = moe.MoeLayer(*args, layout="canonical").plan(T)
     blk = moe.MoeLayer(*args, layout="blocked").plan(T)
     log(f"MoeLayer T={T}: canonical and blocked")
     want = canon(d["x"]).clone()
