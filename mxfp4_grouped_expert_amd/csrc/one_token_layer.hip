@@ -210,7 +210,8 @@ __device__ void routing_role(const Args& a, int rid, unsigned char* lds) {
   one_token_logits(a.partial, a.bias, a.E, a.splits, val);
   // top-k and softmax into LDS only: the plan goes out first, the routing
   // outputs for the caller (identical values) after it
-  topk_softmax_wave(val, a.E, a.k, a.gating, 0, nullptr, nullptr, s_ids, s_w);
+  topk_softmax_wave(val, a.E, a.k, a.gating, 0, nullptr, nullptr, s_ids, s_w,
+                    reinterpret_cast<long long*>(lds + 128));
   wave_lds_sync();
   // lane (r, j) writes slot j's entries of replica r, 8 replicas per pass
   for (int r0 = 0; r0 < kReplicas; r0 += kWave / kMaxTopk) {

@@ -136,6 +136,7 @@ __global__ __launch_bounds__(256) void router_topk_softmax(
     const double* __restrict__ partial, const float* __restrict__ bias, int T, int E, int k,
     int gating, int splits, int32_t* __restrict__ topk_ids, float* __restrict__ topk_weights,
     double* __restrict__ logits) {
+  __shared__ __align__(16) long long s_rank[kWavesPerBlock][kRankScratch];
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * kWavesPerBlock + wave;
@@ -161,7 +162,7 @@ __global__ __launch_bounds__(256) void router_topk_softmax(
     }
     val[i] = v;
   }
-  topk_softmax_wave(val, E, k, gating, t, topk_ids, topk_weights, nullptr);
+  topk_softmax_wave(val, E, k, gating, t, topk_ids, topk_weights, nullptr, nullptr, s_rank[wave]);
 }
 
 // ------------------------------------------------------------ fused decode
@@ -184,7 +185,7 @@ __global__ __launch_bounds__(kFusedThreads) void router_decode_fused(
     int32_t* __restrict__ num_tiles) {
   __shared__ double s_logits[kFusedMaxTE];
   __shared__ int s_ids[kFusedMaxSlots];
-  __shared__ long long s_key[kFusedMaxTE];
+  __shared__ __align__(16) long long s_key[kFusedMaxTE];
   __shared__ int s_sel_e[kFusedMaxSlots];
   __shared__ double s_sel_v[kFusedMaxSlots];
   __shared__ double s_z[kFusedMaxSlots];
@@ -214,7 +215,7 @@ __global__ __launch_bounds__(kFusedThreads) void router_decode_fused(
       double val[4];
       one_token_logits(partial, bias, E, splits, val);
       tail_one_token(val, E, k, gating, topk_ids, topk_weights, logits, s_ids, expert_offsets,
-                     sorted_ids, tiles, num_tiles);
+                     sorted_ids, tiles, num_tiles, nullptr, s_key);
       if (threadIdx.x == 0)
         __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
