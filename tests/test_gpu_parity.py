@@ -65,6 +65,33 @@ def test_gptoss120b_prefill_T4096(w120b):
     assert sorted(res["gpu"]["sorted_ids"].tolist()) == list(range(inp["T"] * inp["k"]))
 
 
+# The benchmark's own configuration: MoeLayer with its default plan (the
+# weights repacked into the blocked layout, the single launch at T = 1, the
+# fused routing up to 16 tokens), one call per workload, against the oracle.
+BENCH_TOKENS = {1: None, 2: None, 3: np.arange(0, 64, 4), 4: np.array([0, 7, 1500, 2048, 4095])}
+
+
+@pytest.mark.parametrize("wid", [1, 2, 3, 4])
+def test_bench_configuration_matches_oracle(wid, w120b):
+    inp = make_workload(wid, weights=wid < 3)
+    if wid >= 3:
+        inp.update(w120b)
+    d = to_device(inp)
+    layer = moe.MoeLayer(d["w_router"], d["bias"], d["w13_q"], d["w13_s"], d["w2_q"], d["w2_s"],
+                         inp["k"], gating=inp["gating"]).plan(inp["T"])
+    log(f"bench configuration, workload {wid}: MoeLayer (layout blocked, BM {layer.BM})")
+    out = layer(d["x"]).float().cpu().numpy().astype(np.float64)
+    ids = layer.topk_ids.cpu().numpy()
+    wts = layer.topk_weights.cpu().numpy()
+    del layer, d
+    log(f"bench configuration, workload {wid}: oracle")
+    r = oracle.moe_layer(inp, BM=moe.pick_bm(inp["T"], inp["k"], inp["E"]),
+                         tokens=BENCH_TOKENS[wid])
+    np.testing.assert_array_equal(ids, r["topk_ids"])
+    np.testing.assert_allclose(wts, r["topk_weights"], rtol=0, atol=1e-6)
+    assert_out_close(out[r["tokens"]], r["out"])
+
+
 @pytest.mark.parametrize("BM", [16, 32, 64, 128])
 def test_tile_table_all_bm_at_prefill(w120b, BM):
     inp = make_workload(4, weights=False)
