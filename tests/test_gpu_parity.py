@@ -126,6 +126,10 @@ RANDOM_CASES = [
     (300, 160, 4, 2, 224, False, 0.3, 128),
     (512, 2880, 16, 2, 2880, True, 0.5, 128),
     (160, 96, 2, 1, 32, False, 0.3, 128),
+    # the largest H and I the library accepts (65536): 22 K chunks of 3072
+    # with a ragged last one, on the gate/up and on the down GEMM
+    (3, 65536, 2, 2, 64, False, 0.02, 16),
+    (3, 64, 2, 1, 65536, True, 0.3, 16),
 ]
 
 
