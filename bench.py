@@ -51,6 +51,8 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", type=int, default=1, choices=range(7))
     ap.add_argument("--rotations", type=int, default=0, help="weight copies (0 = auto)")
+    ap.add_argument("--bm", type=int, default=None, choices=(16, 32, 64, 128),
+                    help="token tile (default: the library's moe_pick_bm rule)")
     ap.add_argument("--layout", default="blocked", choices=("canonical", "blocked"),
                     help="byte layout of the packed expert codes (blocked: repacked at load)")
     ap.add_argument("--no-graph", action="store_true", help="time eager calls instead of graphs")
@@ -156,7 +158,7 @@ def main():
         + 2 * T * H * 2
     layer_flops = 2 * T * k * 3 * I * H + 2 * T * E * H
     R = args.rotations or max(1, min(32, math.ceil(3 * INFINITY_CACHE / touched)))
-    layer = moe.MoeLayer(wr, bias, *w0, k, gating=inp["gating"], layout=args.layout).plan(T)
+    layer = moe.MoeLayer(wr, bias, *w0, k, gating=inp["gating"], layout=args.layout).plan(T, BM=args.bm)
     w0 = [layer.w13_q, layer.w13_s, layer.w2_q, layer.w2_s]  # in the layer's layout
     copies = [w0] + [[w.clone() for w in w0] for _ in range(R - 1)]
     BM = layer.BM
