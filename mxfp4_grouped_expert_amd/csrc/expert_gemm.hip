@@ -18,9 +18,10 @@
 // b = 16*step + 4*kq + group goes to lane group `group` (lanes 16*group ..
 // +15) of the block's wave kq.  A lane thus loads exactly one MX block (16
 // bytes, 32 codes) plus its scale byte per weight row and step, and a wave
-// needs 64 contiguous bytes of each of its 16 rows (the one-chunk gate/up
-// kernel loads them in a faster pattern and regroups them through LDS, as
-// described at its loads).  An MFMA sums over its
+// needs 64 bytes of each of its 16 rows: one contiguous kilobyte in the
+// blocked weight layout, 16 separate runs in the canonical one (where the
+// one-chunk gate/up kernel loads a faster pattern and regroups it through
+// LDS, as described at its loads).  An MFMA sums over its
 // whole K range, so the K order is free as long as the activation operand
 // uses the same assignment: for MFMA j (0..3) of a step, group g supplies
 // elements 32*b + 8*j .. +8 of both operands.
