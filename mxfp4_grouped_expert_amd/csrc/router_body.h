@@ -74,21 +74,43 @@ __device__ void logits_partial_body(const uint16_t* __restrict__ x,
     }
   }
 
+  // Sum each of the N = TPW*4 values over the wave's 64 lanes, as a
+  // reduce-scatter: at lane offsets 32, 16, ... a lane keeps one half of its
+  // live values, receives its partner's copy of that half and adds it, so
+  // after log2(N) steps it holds one value (index = its lane bits 5, 4, ...)
+  // that the remaining offsets finish as a plain butterfly: N - 1 + 6 -
+  // log2(N) exchanges instead of 6N.  Every lane of a group ends with the
+  // same bits (a + b and b + a are the same double).
+  constexpr int N = TPW * kExpPerWave;
+  constexpr int LOGN = N == 16 ? 4 : N == 8 ? 3 : N == 4 ? 2 : N == 2 ? 1 : 0;
+  static_assert((1 << LOGN) == N, "a power of two");
+  double v[N];
 #pragma unroll
-  for (int t = 0; t < TPW; ++t) {
+  for (int t = 0; t < TPW; ++t)
 #pragma unroll
-    for (int e = 0; e < kExpPerWave; ++e) {
-      double v = acc[t][e];
+    for (int e = 0; e < kExpPerWave; ++e) v[t * kExpPerWave + e] = acc[t][e];
 #pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-      if (lane == 0 && t0 + t < T && e0 + e < E) {
-        double* dst = &partial[((size_t)s * T + (t0 + t)) * E + (e0 + e)];
-        if (ATOMIC_OUT)
-          __hip_atomic_store(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        else
-          *dst = v;
-      }
+  for (int st = 0; st < LOGN; ++st) {
+    const int off = 32 >> st;
+    const int half = N >> (st + 1);
+    const bool up = (lane & off) != 0;
+#pragma unroll
+    for (int i = 0; i < half; ++i) {
+      const double send = up ? v[i] : v[i + half];
+      const double keep = up ? v[i + half] : v[i];
+      v[i] = keep + __shfl_xor(send, off);
     }
+  }
+#pragma unroll
+  for (int off = 32 >> LOGN; off >= 1; off >>= 1) v[0] += __shfl_xor(v[0], off);
+  const int idx = lane >> (6 - LOGN);  // the value this lane holds
+  const int t = idx / kExpPerWave, e = idx % kExpPerWave;
+  if ((lane & ((64 >> LOGN) - 1)) == 0 && t0 + t < T && e0 + e < E) {
+    double* dst = &partial[((size_t)s * T + (t0 + t)) * E + (e0 + e)];
+    if (ATOMIC_OUT)
+      __hip_atomic_store(dst, v[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+      *dst = v[0];
   }
 }
 
