@@ -15,6 +15,16 @@ constexpr int kExpPerWave = 4;
 constexpr int kWavesPerBlock = 4;
 constexpr int kExpPerBlock = kExpPerWave * kWavesPerBlock;
 
+// v of the lane that DPP control CTRL selects (every lane has a source for
+// the row rotations and quad permutations used here)
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(b & 0xffffffffLL), CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(b >> 32), CTRL, 0xF, 0xF, false);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+
 // One workgroup's share of the partial logits: tokens [TPW*bx, +TPW), experts
 // [16*by, +16) (4 per wave), K-range bz.  ATOMIC_OUT stores with agent-scope
 // atomics so another workgroup of the same launch may read them.
@@ -101,8 +111,13 @@ __device__ void logits_partial_body(const uint16_t* __restrict__ x,
       v[i] = keep + __shfl_xor(send, off);
     }
   }
-#pragma unroll
-  for (int off = 32 >> LOGN; off >= 1; off >>= 1) v[0] += __shfl_xor(v[0], off);
+  // the rest within 16-lane rows, on DPP (no LDS): rotations by 8 and 4,
+  // then quad swaps 2 and 1; lane 0 of each row ends with the row's sum
+  static_assert(LOGN >= 2, "the rest fits one 16-lane row");
+  if constexpr (LOGN <= 2) v[0] += dpp_f64<0x128>(v[0]);  // row_ror:8
+  if constexpr (LOGN <= 3) v[0] += dpp_f64<0x124>(v[0]);  // row_ror:4
+  v[0] += dpp_f64<0x4E>(v[0]);                            // quad_perm [2,3,0,1]
+  v[0] += dpp_f64<0xB1>(v[0]);                            // quad_perm [1,0,3,2]
   const int idx = lane >> (6 - LOGN);  // the value this lane holds
   const int t = idx / kExpPerWave, e = idx % kExpPerWave;
   if ((lane & ((64 >> LOGN) - 1)) == 0 && t0 + t < T && e0 + e < E) {
