@@ -138,3 +138,46 @@ def test_fused_graph_replays():
         moe.moe_route_tiles(d[0], d[1], d[2], k, BM, workspace=layer_ws)
         torch.cuda.synchronize()
         assert int(layer_ws[:256].count_nonzero().item()) == 0
+
+
+@pytest.mark.parametrize("E,k", [(40, 4), (64, 8), (100, 4)])
+def test_ties_on_every_routing_path(E, k):
+    """Equal logits go to the lower expert on every path that selects: the
+    unfused top-k (T > 16), the fused launch (one and several tokens) and the
+    one-launch layer; at 40 and 64 experts the rank count runs, at 100 the
+    argmax rounds.  Rows of the router are duplicated in pairs, so every
+    logit has a twin, and an all-zero router ties everything."""
+    for zero in (False, True):
+        inp = make_random(T=20, H=128, E=E, k=k, I=64, seed=E + k, router_std=0.5)
+        wr = inp["w_router"]
+        if zero:
+            wr[:] = 0
+        else:
+            wr[1::2] = wr[0::2][: wr[1::2].shape[0]]
+        x, wrd, _ = _router_inputs(inp)
+        # logits by one elementwise product and sum per (token, expert), so
+        # duplicated router rows give bitwise equal logits here as well
+        xf = oracle.bf16_to_f64(inp["x"])
+        L = (xf[:, None, :] * wr.astype(np.float64)[None, :, :]).sum(axis=2)
+        ref_ids = oracle.top_k(L, k)
+        ref_w = oracle.softmax_selected(L, ref_ids)
+        if zero:
+            assert np.all(ref_ids == np.arange(k))
+        log(f"ties E={E} k={k} zero={zero}: moe_route at T=20")
+        ids, wts, _ = moe.moe_route(x, wrd, None, k)
+        np.testing.assert_array_equal(ids.cpu().numpy(), ref_ids)
+        np.testing.assert_allclose(wts.cpu().numpy(), ref_w, rtol=0, atol=1e-6)
+        for T in (1, 5):
+            log(f"ties E={E} k={k} zero={zero}: moe_route_tiles at T={T}")
+            f = moe.moe_route_tiles(x[:T].contiguous(), wrd, None, k, moe.pick_bm(T, k, E))
+            np.testing.assert_array_equal(f[0].cpu().numpy(), ref_ids[:T])
+            np.testing.assert_allclose(f[1].cpu().numpy(), ref_w[:T], rtol=0, atol=1e-6)
+        d = {key: torch.from_numpy(np.ascontiguousarray(inp[key])).cuda()
+             for key in ("w13_q", "w13_s", "w2_q", "w2_s")}
+        log(f"ties E={E} k={k} zero={zero}: one-launch layer")
+        o = moe.moe_layer_one_token(x[:1].contiguous(), wrd, None, d["w13_q"], d["w13_s"],
+                                    d["w2_q"], d["w2_s"], k, moe.pick_bm(1, k, E),
+                                    layout="canonical")
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(o[1].cpu().numpy(), ref_ids[:1])
+        np.testing.assert_allclose(o[2].cpu().numpy(), ref_w[:1], rtol=0, atol=1e-6)
