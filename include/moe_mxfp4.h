@@ -77,7 +77,8 @@ typedef enum {
   MOE_ERR_ALIGN = 3,     /* a pointer is not 16-byte aligned */
   MOE_ERR_WORKSPACE = 4, /* workspace smaller than the *_workspace_bytes query */
   MOE_ERR_DEVICE = 5,    /* current device is not gfx950 or cannot be queried */
-  MOE_ERR_HIP = 6        /* a kernel launch failed */
+  MOE_ERR_HIP = 6,       /* a kernel launch failed */
+  MOE_ERR_OVERLAP = 7    /* an output buffer overlaps an input it must not */
 } moe_status;
 
 /* Static description of a status code (host). */
@@ -127,9 +128,10 @@ const char* moe_version(void);
  *              K = H; w2_q: rows = E*H, K = I), 16-byte aligned, read only
  *   rows       > 0, a multiple of 16;  K: > 0, a multiple of 32, <= 65536
  *   q_blocked  device, uint8 [rows][K/2], 16-byte aligned, written; must not
- *              overlap q
+ *              overlap q (MOE_ERR_OVERLAP)
  * Scales are not touched.  Errors: MOE_ERR_SHAPE (sizes), MOE_ERR_NULL,
- * MOE_ERR_ALIGN, MOE_ERR_DEVICE, MOE_ERR_HIP; on error nothing is written. */
+ * MOE_ERR_ALIGN, MOE_ERR_OVERLAP, MOE_ERR_DEVICE, MOE_ERR_HIP; on error
+ * nothing is written. */
 moe_status moe_repack_weights(const uint8_t* q, int64_t rows, int K, uint8_t* q_blocked,
                               struct ihipStream_t* stream);
 

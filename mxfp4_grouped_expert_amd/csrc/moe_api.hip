@@ -62,6 +62,7 @@ const char* moe_status_string(int status) {
     case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace is too small";
     case MOE_ERR_DEVICE: return "MOE_ERR_DEVICE: current device is not gfx950 or not usable";
     case MOE_ERR_HIP: return "MOE_ERR_HIP: a kernel launch failed";
+    case MOE_ERR_OVERLAP: return "MOE_ERR_OVERLAP: an output overlaps an input";
     default: return "unknown moe_status";
   }
 }
@@ -183,6 +184,11 @@ moe_status moe_repack_weights(const uint8_t* q, int64_t rows, int K, uint8_t* q_
     return MOE_ERR_SHAPE;
   if (!q || !q_blocked) return MOE_ERR_NULL;
   if (!aligned16(q) || !aligned16(q_blocked)) return MOE_ERR_ALIGN;
+  {
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(q), b0 = reinterpret_cast<uintptr_t>(q_blocked);
+    const uintptr_t n = (uintptr_t)rows * (uintptr_t)(K / 2);
+    if (a0 < b0 + n && b0 < a0 + n) return MOE_ERR_OVERLAP;
+  }
   moe_status st = check_device();
   if (st != MOE_OK) return st;
   (void)hipGetLastError();

@@ -16,7 +16,7 @@ from mxfp4_grouped_expert_amd import binding as B
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "moe_mxfp4.h")
 
-OK, NULL, SHAPE, ALIGN, WORKSPACE, DEVICE = 0, 1, 2, 3, 4, 5
+OK, NULL, SHAPE, ALIGN, WORKSPACE, DEVICE, OVERLAP = 0, 1, 2, 3, 4, 5, 7
 P = 0x10000          # fake, 16-byte aligned "device" address (never dereferenced)
 PMIS = 0x10004       # misaligned
 
@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings_and_version():
-    for s in range(7):
+    for s in range(8):
         assert moe.status_string(s).startswith("MOE_")
     assert "unknown" in moe.status_string(99)
     assert re.match(r"\d+\.\d+\.\d+", moe.version())
@@ -205,7 +205,7 @@ def test_one_token_validation(kw, want):
 
 
 def _repack(**kw):
-    a = dict(q=P, rows=64, K=256, qb=P)
+    a = dict(q=P, rows=64, K=256, qb=P + (1 << 20))
     a.update(kw)
     return B.load().moe_repack_weights(a["q"], a["rows"], a["K"], a["qb"], None)
 
@@ -214,6 +214,7 @@ def _repack(**kw):
     (dict(q=None), NULL), (dict(qb=None), NULL), (dict(rows=0), SHAPE), (dict(rows=40), SHAPE),
     (dict(rows=-16), SHAPE), (dict(K=48), SHAPE), (dict(K=0), SHAPE), (dict(K=65536 + 32), SHAPE),
     (dict(rows=1 << 40, K=65536), SHAPE), (dict(q=PMIS), ALIGN), (dict(qb=PMIS), ALIGN),
+    (dict(qb=P), OVERLAP), (dict(qb=P + 64 * 128 - 16), OVERLAP), (dict(q=P + (1 << 20) - 4096), OVERLAP),
 ])
 def test_repack_validation(kw, want):
     assert _repack(**kw) == want
