@@ -44,6 +44,8 @@
 // memory system, so hot words have their own 128-byte lines: the plan is
 // written to 16 replica lines (workgroup i reads replica i % 16) and the
 // arrival tree spreads its counters over 16 leaf lines and a top line.
+#include <cstdlib>
+
 #include "expert_common.h"
 #include "moe_device.h"
 #include "moe_launch.h"
@@ -111,7 +113,7 @@ __device__ __forceinline__ void st64(u64* p, unsigned stamp, unsigned payload) {
 // the payloads in v's low halves.
 template <int N>
 __device__ __forceinline__ void settle(const u64* const (&p)[N], const bool (&use)[N], u64 (&v)[N],
-                                       unsigned stamp, int* error) {
+                                       unsigned stamp, int* error, int spin_limit) {
 #pragma unroll
   for (int i = 0; i < N; ++i) v[i] = use[i] ? ld64(p[i]) : ((u64)stamp << 32);
   for (int round = 0;; ++round) {
@@ -119,7 +121,7 @@ __device__ __forceinline__ void settle(const u64* const (&p)[N], const bool (&us
 #pragma unroll
     for (int i = 0; i < N; ++i) stale |= (unsigned)(v[i] >> 32) != stamp;
     if (!stale) return;
-    if (round == kSpinLimit) {
+    if (round >= spin_limit) {
       st_agent(error, 1);
       return;
     }
@@ -160,7 +162,8 @@ struct Args {
   const uint8_t* w2_q;
   const uint8_t* w2_s;
   int H, I, E, k, gating;
-  bool blocked;  // code matrices in the blocked layout
+  bool blocked;    // code matrices in the blocked layout
+  int spin_limit;  // polls before a wait gives up
   int split_len, splits, n_route;
   int32_t* topk_ids;
   float* topk_weights;
@@ -206,7 +209,7 @@ __device__ void routing_role(const Args& a, int rid, unsigned char* lds) {
       use[i] = w < a.n_route - 1;
       src[i] = &a.sync->routed[min(w, kMaxRoute - 1)];
     }
-    settle(src, use, v, stamp, &a.sync->error);
+    settle(src, use, v, stamp, &a.sync->error, a.spin_limit);
   }
   double val[4];
   one_token_logits(a.partial, a.bias, a.E, a.splits, val);
@@ -415,7 +418,7 @@ __device__ __forceinline__ void down_finish(const Args& a, int g, int cb, int sl
       use[i] = d < spr * 4;
       src[i] = hrow + min(min(d, spr * 4 - 1) >> 2, cpr - 1) * 4 + (d & 3);
     }
-    settle(src, use, v, stamp, &a.sync->error);
+    settle(src, use, v, stamp, &a.sync->error, a.spin_limit);
 #pragma unroll
     for (int i = 0; i < kPer; ++i)
       if (use[i]) dst[tid + i * kThreads] = (unsigned)v[i];
@@ -462,7 +465,7 @@ __device__ __forceinline__ void down_finish(const Args& a, int g, int cb, int sl
     src[kMaxTopk + j] = a.y + (size_t)jc * H + n_base + tid;
     use[kMaxTopk + j] = j < a.k && j != slot;
   }
-  settle(src, use, v, stamp, &a.sync->error);
+  settle(src, use, v, stamp, &a.sync->error, a.spin_limit);
   float wj[kMaxTopk], yj[kMaxTopk];
 #pragma unroll
   for (int j = 0; j < kMaxTopk; ++j) {
@@ -503,7 +506,7 @@ __device__ void gemm_role(const Args& a, int j, unsigned char* lds) {
     const u64* src[2] = {&R->plan[g_gu], &R->plan[min(t0, a.k - 1)]};
     const bool use[2] = {true, true};
     u64 v[2];
-    settle(src, use, v, stamp, &a.sync->error);
+    settle(src, use, v, stamp, &a.sync->error, a.spin_limit);
     s_plan[0] = (unsigned)v[0];
     s_plan[1] = (unsigned)v[1];
   }
@@ -528,7 +531,7 @@ __device__ void gemm_role(const Args& a, int j, unsigned char* lds) {
         const u64* src[1] = {&R->plan[t]};
         const bool use[1] = {true};
         u64 v[1];
-        settle(src, use, v, stamp, &a.sync->error);
+        settle(src, use, v, stamp, &a.sync->error, a.spin_limit);
         s_plan[2] = (unsigned)v[0];
       }
       __syncthreads();
@@ -544,7 +547,7 @@ __device__ void gemm_role(const Args& a, int j, unsigned char* lds) {
         const u64* src[1] = {a.h + (size_t)t * a.I / 2 + (size_t)(cb % (a.I / 32)) * 16};
         const bool use[1] = {true};
         u64 v[1];
-        settle(src, use, v, stamp, &a.sync->error);
+        settle(src, use, v, stamp, &a.sync->error, a.spin_limit);
       }
       __syncthreads();
     }
@@ -601,6 +604,13 @@ void launch_layer_one_token(const uint16_t* x, const float* w_router, const floa
   a.x = x; a.w_router = w_router; a.bias = bias;
   a.w13_q = w13_q; a.w13_s = w13_s; a.w2_q = w2_q; a.w2_s = w2_s;
   a.H = H; a.I = I; a.E = E; a.k = k; a.gating = gating; a.blocked = blocked;
+  // A test of the give-up path lowers the poll bound through the
+  // environment (read at every call; values outside [0, kSpinLimit) ignored).
+  a.spin_limit = kSpinLimit;
+  if (const char* env = getenv("MOE_ONE_TOKEN_SPIN_LIMIT")) {
+    const long v = strtol(env, nullptr, 10);
+    if (v >= 0 && v < kSpinLimit) a.spin_limit = (int)v;
+  }
   a.split_len = p.split_len;
   a.splits = p.splits;
   a.n_route = p.splits * ((E + kExpPerBlock - 1) / kExpPerBlock);
