@@ -52,7 +52,8 @@ namespace {
 // !GATEUP: A rows are h[r], K = I, weights are rows of w2, output
 //         y[sorted_ids[r]][n] in fp32.
 // BLK: the code matrix is in the blocked layout (see wq_row_offset).
-template <bool GATEUP, int NBW, int XR, bool ONECHUNK, bool BLK>
+// G: passes that share each load of a K chunk's weights (several chunks).
+template <bool GATEUP, int NBW, int XR, bool ONECHUNK, bool BLK, int G = 1>
 __global__ __launch_bounds__(256 * NBW) void expert_gemm_kernel(
     const uint16_t* __restrict__ act, const uint8_t* __restrict__ wq,
     const uint8_t* __restrict__ ws, const int32_t* sorted_ids,  // not restrict: see below
@@ -253,12 +254,16 @@ __global__ __launch_bounds__(256 * NBW) void expert_gemm_kernel(
   if (tid < rows) s_slot[tid] = my_slot;
   lds_barrier();  // this wave's staging loads have landed (waited above)
 
-  for (int pass = 0; pass < npass; ++pass) {
-    const int p0 = pass * XR;
-    const int prow = min(XR, rows - p0);
-    if (ONECHUNK && pass > 0) {
+  // With several K chunks a lane holds one chunk of weights at a time, so
+  // G passes share each load of a chunk (their accumulators stay in
+  // registers across the chunks) instead of every pass fetching all of K
+  // again.  Each pass still accumulates its chunks and steps in order, so
+  // the results do not depend on G.
+  static_assert(G == 1 || !ONECHUNK, "pass groups only with several chunks");
+  for (int g0 = 0; g0 < npass; g0 += G) {
+    if (ONECHUNK && g0 > 0) {
       __syncthreads();  // previous pass done with LDS
-      stage_acts(p0, prow, 0, K);
+      stage_acts(g0 * XR, min(XR, rows - g0 * XR), 0, K);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     }
@@ -272,95 +277,111 @@ __global__ __launch_bounds__(256 * NBW) void expert_gemm_kernel(
         for (int w = 0; w < NW; ++w) sreg[c][w] = s_sc[(nb * NW + w) * kScaleRunMax + li * KB + bc];
       }
     }
-    floatx4 acc[NW];
+    floatx4 acc[G][NW];
 #pragma unroll
-    for (int w = 0; w < NW; ++w) acc[w] = floatx4{0.f, 0.f, 0.f, 0.f};
-    const unsigned char* arow = smem + min(li, prow - 1) * stride;
+    for (int pg = 0; pg < G; ++pg)
+#pragma unroll
+      for (int w = 0; w < NW; ++w) acc[pg][w] = floatx4{0.f, 0.f, 0.f, 0.f};
+    const unsigned char* arow = smem + min(li, min(XR, rows - g0 * XR) - 1) * stride;
     int chunk_kb = KB;  // MX blocks of the staged K-range
 
     for (int ch = 0; ch < nchunks; ++ch) {
-      if constexpr (!ONECHUNK) {
-        const int k0 = ch * kChunkK, klen = min(K - k0, kChunkK);
-        if (pass > 0 || ch > 0) __syncthreads();  // every wave done with the LDS
-        load_weights(ch);
-        stage_acts(p0, prow, k0, klen);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        arow = smem + min(li, prow - 1) * act_stride_bytes(klen);
-        chunk_kb = klen / 32;
-      }
 #pragma unroll
-      for (int c = 0; c < kChunk; ++c) {
-        if (XCHG && pass == 0) {  // uniform: exchange step c's pieces
-          unsigned char* slot = s_ring + (c % kRing) * kSlotBytes;
-          if (kRing == 1 && c > 0) lds_barrier();  // every wave done reading step c-1
-          const int wr16 = 4 * kq + (lane >> 4);
-#pragma unroll
-          for (int w = 0; w < NW; ++w)
-            *reinterpret_cast<uint4*>(slot + ((w * NBW + nb) * kRowsPerBlock + wr16) * 256 +
-                                      (((lane & 15) ^ wr16) << 4)) = wreg[c][w];
-          lds_barrier();
-#pragma unroll
-          for (int w = 0; w < NW; ++w)
-            wreg[c][w] = *reinterpret_cast<const uint4*>(
-                slot + ((w * NBW + nb) * kRowsPerBlock + li) * 256 + (((4 * kq + grp) ^ li) << 4));
+      for (int pg = 0; pg < G; ++pg) {
+        const int pass = g0 + pg;
+        if (pass >= npass) break;  // uniform
+        if constexpr (!ONECHUNK) {
+          const int p0 = pass * XR;
+          const int prow = min(XR, rows - p0);
+          const int k0 = ch * kChunkK, klen = min(K - k0, kChunkK);
+          if (g0 > 0 || ch > 0 || pg > 0) __syncthreads();  // every wave done with the LDS
+          if (pg == 0) load_weights(ch);
+          stage_acts(p0, prow, k0, klen);
+          __builtin_amdgcn_s_waitcnt(0);
+          __syncthreads();
+          arow = smem + min(li, prow - 1) * act_stride_bytes(klen);
+          chunk_kb = klen / 32;
         }
-        // Step c's weights are decoded here and no earlier: an empty asm that
-        // "modifies" them stops the compiler from hoisting the decode (which
-        // would quadruple their register footprint) and makes this step wait
-        // for its own loads only.
 #pragma unroll
-        for (int w = 0; w < NW; ++w)
-          asm volatile("" : "+v"(wreg[c][w].x), "+v"(wreg[c][w].y), "+v"(wreg[c][w].z),
-                       "+v"(wreg[c][w].w), "+v"(sreg[c][w]));
-        const int b = (ch * kChunk + c) * kBlocksPerStep + kq * 4 + grp;
-        const bool valid = b < KB;
-        // block within the staged K-range (the whole of K with one chunk)
-        const int bl = min(c * kBlocksPerStep + kq * 4 + grp, chunk_kb - 1);
-        float scale[NW];
+        for (int c = 0; c < kChunk; ++c) {
+          if (XCHG && pass == 0) {  // uniform: exchange step c's pieces
+            unsigned char* slot = s_ring + (c % kRing) * kSlotBytes;
+            if (kRing == 1 && c > 0) lds_barrier();  // every wave done reading step c-1
+            const int wr16 = 4 * kq + (lane >> 4);
 #pragma unroll
-        for (int w = 0; w < NW; ++w) scale[w] = valid ? e8m0_to_float(sreg[c][w]) : 0.f;
-        const uint4* ap = reinterpret_cast<const uint4*>(arow + bl * 64);
+            for (int w = 0; w < NW; ++w)
+              *reinterpret_cast<uint4*>(slot + ((w * NBW + nb) * kRowsPerBlock + wr16) * 256 +
+                                        (((lane & 15) ^ wr16) << 4)) = wreg[c][w];
+            lds_barrier();
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const bf16x8 a = as_bf16x8(ap[j]);
+            for (int w = 0; w < NW; ++w)
+              wreg[c][w] = *reinterpret_cast<const uint4*>(
+                  slot + ((w * NBW + nb) * kRowsPerBlock + li) * 256 + (((4 * kq + grp) ^ li) << 4));
+          }
+          // Step c's weights are decoded here and no earlier: an empty asm that
+          // "modifies" them stops the compiler from hoisting the decode (which
+          // would quadruple their register footprint) and makes this step wait
+          // for its own loads only.
 #pragma unroll
           for (int w = 0; w < NW; ++w)
-            acc[w] = mfma16x16x32(a, dequant8_bf16(word(wreg[c][w], j), scale[w]), acc[w]);
+            asm volatile("" : "+v"(wreg[c][w].x), "+v"(wreg[c][w].y), "+v"(wreg[c][w].z),
+                         "+v"(wreg[c][w].w), "+v"(sreg[c][w]));
+          const int b = (ch * kChunk + c) * kBlocksPerStep + kq * 4 + grp;
+          const bool valid = b < KB;
+          // block within the staged K-range (the whole of K with one chunk)
+          const int bl = min(c * kBlocksPerStep + kq * 4 + grp, chunk_kb - 1);
+          float scale[NW];
+#pragma unroll
+          for (int w = 0; w < NW; ++w) scale[w] = valid ? e8m0_to_float(sreg[c][w]) : 0.f;
+          const uint4* ap = reinterpret_cast<const uint4*>(arow + bl * 64);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const bf16x8 a = as_bf16x8(ap[j]);
+#pragma unroll
+            for (int w = 0; w < NW; ++w)
+              acc[pg][w] = mfma16x16x32(a, dequant8_bf16(word(wreg[c][w], j), scale[w]), acc[pg][w]);
+          }
         }
       }
     }
 
-    // split-K reduction: waves kq = 0..3 of each 16-row block, fixed order
-    __syncthreads();  // every wave done reading the staged activations
-    float* red = reinterpret_cast<float*>(smem);  // [NBW][4][NW][256]
 #pragma unroll
-    for (int w = 0; w < NW; ++w)
+    for (int pg = 0; pg < G; ++pg) {
+      const int pass = g0 + pg;
+      if (pass >= npass) break;  // uniform
+      const int p0 = pass * XR;
+      const int prow = min(XR, rows - p0);
+      // split-K reduction: waves kq = 0..3 of each 16-row block, fixed order
+      __syncthreads();  // every wave done reading the staged activations
+      float* red = reinterpret_cast<float*>(smem);  // [NBW][4][NW][256]
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        red[((nb * 4 + kq) * NW + w) * 256 + (4 * grp + r) * kRowsPerBlock + li] = acc[w][r];
-    __syncthreads();
-    {
-      const int obl = tid >> 8;       // output block handled by this thread
-      const int idx = tid & 255;      // 16 tokens x 16 rows
-      const int tm = idx / kRowsPerBlock;
-      const int tn = idx % kRowsPerBlock;
-      const int on = (blockIdx.x * NBW + obl) * kRowsPerBlock + tn;
-      float v[NW];
+      for (int w = 0; w < NW; ++w)
 #pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        v[w] = red[((obl * 4 + 0) * NW + w) * 256 + idx];
+        for (int r = 0; r < 4; ++r)
+          red[((nb * 4 + kq) * NW + w) * 256 + (4 * grp + r) * kRowsPerBlock + li] = acc[pg][w][r];
+      __syncthreads();
+      {
+        const int obl = tid >> 8;       // output block handled by this thread
+        const int idx = tid & 255;      // 16 tokens x 16 rows
+        const int tm = idx / kRowsPerBlock;
+        const int tn = idx % kRowsPerBlock;
+        const int on = (blockIdx.x * NBW + obl) * kRowsPerBlock + tn;
+        float v[NW];
 #pragma unroll
-        for (int q = 1; q < 4; ++q) v[w] += red[((obl * 4 + q) * NW + w) * 256 + idx];
-      }
-      if (tm < prow && on < N) {
-        const int r = r0 + p0 + tm;
-        if (GATEUP) {
-          reinterpret_cast<uint16_t*>(out)[(size_t)r * I + on] =
-              float_to_bf16(silu(v[0]) * v[NW - 1]);
-        } else {
-          const long long p = s_slot[p0 + tm];
-          if (p >= 0 && p < nslots) reinterpret_cast<float*>(out)[(size_t)p * H + on] = v[0];
+        for (int w = 0; w < NW; ++w) {
+          v[w] = red[((obl * 4 + 0) * NW + w) * 256 + idx];
+#pragma unroll
+          for (int q = 1; q < 4; ++q) v[w] += red[((obl * 4 + q) * NW + w) * 256 + idx];
+        }
+        if (tm < prow && on < N) {
+          const int r = r0 + p0 + tm;
+          if (GATEUP) {
+            reinterpret_cast<uint16_t*>(out)[(size_t)r * I + on] =
+                float_to_bf16(silu(v[0]) * v[NW - 1]);
+          } else {
+            const long long p = s_slot[p0 + tm];
+            if (p >= 0 && p < nslots) reinterpret_cast<float*>(out)[(size_t)p * H + on] = v[0];
+          }
         }
       }
     }
@@ -527,6 +548,10 @@ void launch_expert_gemm(const uint16_t* act, const uint8_t* wq, const uint8_t* w
   const int nblk16 = N / kRowsPerBlock;
   const bool one_chunk = K <= kChunk * kBlocksPerStep * 32;
   const size_t red_bytes_1 = (size_t)4 * (GATEUP ? 2 : 1) * 256 * sizeof(float);
+  // several chunks and more expected rows per expert than one pass holds:
+  // two passes share each chunk's weights (with one pass expected, the
+  // larger register footprint only costs)
+  const bool group2 = (long long)T * k > (long long)xr * E;
 #define MOE_LAUNCH(NBW_, XR_)                                                                  \
   do {                                                                                          \
     size_t lds = ((size_t)(XR_) * act_stride_bytes(one_chunk ? K : kChunkK) + 1023) / 1024 * 1024; \
@@ -536,8 +561,12 @@ void launch_expert_gemm(const uint16_t* act, const uint8_t* wq, const uint8_t* w
       hipLaunchKernelGGL((expert_gemm_kernel<GATEUP, NBW_, XR_, true, BLK>), grid, dim3(256 * (NBW_)), \
                          lds, stream, act, wq, ws, sorted_ids, tiles, num_tiles, T, H, I, E, k,  \
                          out);                                                                  \
+    else if (group2)                                                                            \
+      hipLaunchKernelGGL((expert_gemm_kernel<GATEUP, NBW_, XR_, false, BLK, 2>), grid,          \
+                         dim3(256 * (NBW_)), lds, stream, act, wq, ws, sorted_ids, tiles,       \
+                         num_tiles, T, H, I, E, k, out);                                        \
     else                                                                                        \
-      hipLaunchKernelGGL((expert_gemm_kernel<GATEUP, NBW_, XR_, false, BLK>), grid,             \
+      hipLaunchKernelGGL((expert_gemm_kernel<GATEUP, NBW_, XR_, false, BLK, 1>), grid,          \
                          dim3(256 * (NBW_)), lds, stream, act, wq, ws, sorted_ids, tiles,       \
                          num_tiles, T, H, I, E, k, out);                                        \
   } while (0)

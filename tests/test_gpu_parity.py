@@ -130,6 +130,10 @@ RANDOM_CASES = [
     # with a ragged last one, on the gate/up and on the down GEMM
     (3, 65536, 2, 2, 64, False, 0.02, 16),
     (3, 64, 2, 1, 65536, True, 0.3, 16),
+    # K > 3072 with three 16-row passes per tile: two passes share each
+    # chunk's weights, the third runs alone (gate/up side, then down side)
+    (70, 4096, 2, 1, 64, False, 0.3, 128),
+    (70, 64, 2, 1, 4096, False, 0.3, 128),
 ]
 
 
