@@ -121,9 +121,10 @@ __global__ __launch_bounds__(256 * NBW) void expert_gemm_kernel(
   uint4 wreg[kChunk][NW];
   uint32_t sreg[kChunk][NW];
 
-  auto load_weights = [&](int ch) {
+  auto load_weights = [&](int ch, int c0 = 0, int c1 = kChunk) {
 #pragma unroll
     for (int c = 0; c < kChunk; ++c) {
+      if (c < c0 || c >= c1) continue;
       const int b = XCHG ? c * kBlocksPerStep + (lane & 15)
                              : (ch * kChunk + c) * kBlocksPerStep + kq * 4 + grp;
       const int bc = min(b, KB - 1);  // clamped: always a valid address
@@ -223,8 +224,15 @@ __global__ __launch_bounds__(256 * NBW) void expert_gemm_kernel(
     load_weights(0);
     wait_vmcnt<kChunk * NW>();      // all but the weight loads
   } else {
+    // SPLIT (several 16-row blocks per workgroup, which then runs alone on
+    // its CU): the first half of the steps' weights and the scale piece go
+    // first, the second half after the activation staging, so the wait below
+    // leaves it in flight while the first steps' MFMAs run (20b T = 64
+    // gate/up 62.4 -> 58.9 us; with one block per workgroup other
+    // workgroups already fill that gap and the split measured slower)
+    constexpr bool SPLIT = ONECHUNK && NBW > 1;
     if constexpr (ONECHUNK) {  // depends only on the tile row
-      load_weights(0);
+      load_weights(0, 0, SPLIT ? kChunk / 2 : kChunk);
       load_scale_runs();
     }
     // Row offsets: for down they are the tile's own rows of h, and with one
@@ -248,7 +256,13 @@ __global__ __launch_bounds__(256 * NBW) void expert_gemm_kernel(
     // Pass 0's activations are staged while the weight stream is in flight;
     // one wait covers both.  (With several chunks each chunk stages its own.)
     if constexpr (ONECHUNK) stage_acts(0, min(XR, rows), 0, K);
-    __builtin_amdgcn_s_waitcnt(0);
+    if constexpr (SPLIT) {
+      asm volatile("" ::: "memory");  // the second half stays behind the staging
+      load_weights(0, kChunk / 2, kChunk);
+      wait_vmcnt<(kChunk - kChunk / 2) * NW>();
+    } else {
+      __builtin_amdgcn_s_waitcnt(0);
+    }
   }
   if constexpr (ONECHUNK) store_scale_runs();
   if (tid < rows) s_slot[tid] = my_slot;
