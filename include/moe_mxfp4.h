@@ -12,10 +12,16 @@
  * gating and top-k, permute, expert FFN, unpermute.
  *
  * One layer call is three entry points, all enqueued on one stream:
- *   moe_route        router logits -> top-k -> softmax over the k selected
+ *   moe_route        router logits -> top-k -> softmax (or sigmoid) over
+ *                    the k selected
  *   moe_build_tiles  per-expert counts, offsets, stable sort, tile table
  *   moe_forward      grouped gate/up GEMM + SwiGLU, grouped down GEMM,
  *                    weighted combine back to token order
+ * with fewer launches for small batches: moe_route_tiles (the first two in
+ * one launch, up to 16 tokens) and moe_layer_one_token (all of it in one
+ * launch, one token).  moe_repack_weights prepares, once at load, the
+ * blocked layout of the packed codes that every expert kernel streams
+ * fastest.
  *
  * Conventions shared by every entry point:
  *   - Every array argument is a DEVICE pointer on the current HIP device,
