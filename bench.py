@@ -9,21 +9,30 @@ single-launch moe_layer_one_token.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1]
 
-Default workload: the gpt-oss-20b-shaped decode layer at T=1 (H=2880, E=32,
-k=4, I=2880).  Timing:
-  * headline: HIP graphs, each holding one call per rotating weight copy,
-    replayed back to back; exactly K steps between two events on the replay
-    stream, synchronised on both sides.  R copies of the expert weights are
-    rotated so that R x (bytes one call touches) >= 3 x the 256 MB Infinity
-    Cache, which keeps repeated calls from being served by it;
+Method (the SimpleLLM README, "How we measured": three runs per point, each
+in a process of its own, the median reported):
+  * this process never touches the GPU.  For the headline workload (default:
+    the gpt-oss-20b-shaped decode layer at T=1) and for each of the other
+    gpt-oss workloads (20b T=64 with a skewed router, 120b T=64, 120b
+    T=4096) it starts `--runs` fresh child processes (`bench.py --child`),
+    each of which measures the workload once and prints one JSON record; the
+    record with the median µs/call is kept, with every run's value beside
+    it.  The headline child times exactly K steps after W warmup steps.
+  * within a child: HIP graphs, each holding one call per rotating weight
+    copy, replayed back to back; exactly K steps between two events on the
+    replay stream, synchronised on both sides.  R copies of the expert
+    weights rotate so that R x (bytes one call touches) >= 3 x the 256 MB
+    Infinity Cache (R = 1 is also timed and reported as the cache-inflated
+    figure), and eager calls are timed as the stream-enqueue figure.
   * per-kernel durations: for each entry point a HIP graph of back-to-back
     launches of it alone, timed with HIP events on the launch stream; the
     dominant kernel's average launch duration gives the roofline fraction
     (for one token the whole step is one kernel, timed by the headline loop
     itself; the separate entry points are then reported as components);
   * cpu_baseline: the float64 oracle on this host's cores, on a bounded
-    sample of the same workload.
-Prints one JSON line.
+    sample of each workload, run by this (GPU-free) process.
+Prints one JSON line.  Under a profiler (or with --child) the measurement
+runs in this process instead, once, with no child processes.
 """
 from __future__ import annotations
 
@@ -31,6 +40,9 @@ import argparse
 import json
 import math
 import os
+import re
+import statistics
+import subprocess
 import sys
 import time
 
@@ -42,25 +54,33 @@ METRIC = "MoE layer µs/call + HBM GB/s at T=1,64; TFLOP/s (MFMA util) at T=4096
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 INFINITY_CACHE = 256 << 20
+GPTOSS_WORKLOADS = (1, 2, 3, 4)
+CHILD_TIMEOUT_S = 300
 
 
-def parse_args():
+def parse_args(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", type=int, default=1, choices=range(7))
+    ap.add_argument("--others", default=None,
+                    help="comma-separated workload ids measured beside the headline "
+                         "(default: the other gpt-oss workloads; 'none' for none)")
+    ap.add_argument("--runs", type=int, default=3, help="child processes per workload")
     ap.add_argument("--rotations", type=int, default=0, help="weight copies (0 = auto)")
     ap.add_argument("--bm", type=int, default=None, choices=(16, 32, 64, 128),
                     help="token tile (default: the library's moe_pick_bm rule)")
     ap.add_argument("--layout", default="blocked", choices=("canonical", "blocked"),
                     help="byte layout of the packed expert codes (blocked: repacked at load)")
     ap.add_argument("--no-graph", action="store_true", help="time eager calls instead of graphs")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB device copy (known bytes) for counter scaling")
-    return ap.parse_args()
+    ap.add_argument("--child", action="store_true",
+                    help="measure in this process (one run, no CPU baseline unless asked)")
+    return ap.parse_args(argv)
 
 
 def expert_bytes(H, I):
@@ -71,67 +91,121 @@ def gateup_bytes(H, I):
     return 2 * I * H // 2 + 2 * I * H // 32
 
 
+# ------------------------------------------------------------ CPU baseline --
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(inp, seconds):
+    """The float64 oracle, as it stands, on this host.  Up to 64 tokens: whole
+    layer calls, repeated for about `seconds`.  Above that the oracle's own
+    steps are timed on a sample: routing and the tile table for every token,
+    the expert FFN (decode + matmuls) of a sample of the touched experts with
+    all their rows, scaled by touched / sampled, and the combine."""
     import numpy as np
     import oracle
+    affinity = len(os.sched_getaffinity(0))
     try:
         from threadpoolctl import threadpool_info
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        threads = len(os.sched_getaffinity(0))
-    T = inp["T"]
+        threads = affinity
+    T, k = inp["T"], inp["k"]
     if T <= 64:
-        tokens, what = None, f"full layer (all {T} tokens)"
+        calls, t0 = 0, time.perf_counter()
+        while True:
+            oracle.moe_layer(inp, BM=16)
+            calls += 1
+            el = time.perf_counter() - t0
+            if el >= seconds or calls >= 50:
+                break
+        per_call = el / calls
+        what = f"full layer (all {T} tokens); {calls} call(s) in {el:.1f} s"
     else:
-        tokens = np.arange(0, T, T // 16)
-        what = (f"routing + tile table for all {T} tokens, expert FFN + combine for "
-                f"{len(tokens)} evenly spaced tokens, scaled by {T}/{len(tokens)}")
-    calls, t0 = 0, time.perf_counter()
-    while True:
-        oracle.moe_layer(inp, BM=16, tokens=tokens)
-        calls += 1
-        el = time.perf_counter() - t0
-        if el >= seconds or calls >= 50:
-            break
-    per_call = el / calls
-    if tokens is not None:
-        per_call *= T / len(tokens)
+        t0 = time.perf_counter()
+        ids, w, _ = oracle.route(inp["x"], inp["w_router"], inp.get("bias"), k,
+                                 inp.get("gating", "softmax"))
+        E = inp["w13_q"].shape[0]
+        off, srt, _, _ = oracle.build_tiles(ids, E, 128)
+        x64 = oracle.bf16_to_f64(inp["x"])
+        t_route = time.perf_counter() - t0
+        touched = [e for e in range(E) if off[e + 1] > off[e]]
+        y = np.zeros((T * k, inp["H"]))
+        t1, done = time.perf_counter(), 0
+        for e in touched[:: max(1, len(touched) // 64)]:
+            slots = srt[off[e]:off[e + 1]].astype(np.int64)
+            y[slots] = oracle.expert_ffn(x64[slots // k], inp["w13_q"][e], inp["w13_s"][e],
+                                         inp["w2_q"][e], inp["w2_s"][e])
+            done += 1
+            if time.perf_counter() - t1 >= seconds:
+                break
+        t_ffn = time.perf_counter() - t1
+        t2 = time.perf_counter()
+        oracle.combine(y, w)
+        t_comb = time.perf_counter() - t2
+        per_call = t_route + t_ffn * len(touched) / done + t_comb
+        what = (f"routing + tile table for all {T} tokens ({t_route:.2f} s), expert FFN of "
+                f"{done} of the {len(touched)} touched experts with all their rows "
+                f"({t_ffn:.1f} s, scaled by {len(touched)}/{done}), combine ({t_comb:.2f} s)")
     return {"value": round(per_call * 1e6, 1), "unit": "us/call", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"{what}; {calls} call(s) in {el:.1f} s of float64 numpy"}
+            "kind": "oracle", "sample": f"{what}; float64 numpy",
+            "affinity_cores": affinity, "blas_threads": int(threads), "cpu_model": cpu_model()}
+
+
+# ---------------------------------------------------- counter cross-check --
+
+def _source_hash(src_rel: str) -> str:
+    """sha256 prefix of a kernel source together with every local header it
+    includes (recursively), so an edit to any of them invalidates counters."""
+    import hashlib
+    seen, order = set(), []
+
+    def visit(path):
+        path = os.path.normpath(path)
+        if path in seen or not os.path.exists(path):
+            return
+        seen.add(path)
+        order.append(path)
+        for m in re.finditer(r'#include\s+"([^"]+)"', open(path, encoding="utf-8").read()):
+            visit(os.path.join(os.path.dirname(path), m.group(1)))
+
+    visit(os.path.join(ROOT, src_rel))
+    h = hashlib.sha256()
+    for path in order:
+        h.update(os.path.relpath(path, ROOT).encode())
+        h.update(open(path, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(workload, kernel):
     """HBM bytes per launch of `kernel` at `workload` from the rocprofv3
     FETCH_SIZE/WRITE_SIZE summary in profiles/, or None when there is no row
-    or the kernel source changed since the counters were taken."""
-    import hashlib
-    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
-                        "traffic_counters.md")
+    or the kernel source (or a header it includes) changed since the
+    counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic_counters.md")
     if not os.path.exists(path):
         return None
-    root = os.path.dirname(path)[: -len("profiles")]
     for line in open(path):
         cells = [c.strip() for c in line.strip().strip("|").split("|")]
         if len(cells) != 9 or cells[0] != workload or cells[1] != kernel:
             continue
-        src = os.path.join(root, cells[7])
-        if not os.path.exists(src):
-            return None
-        if hashlib.sha256(open(src, "rb").read()).hexdigest()[:16] != cells[8]:
+        if not os.path.exists(os.path.join(ROOT, cells[7])) or _source_hash(cells[7]) != cells[8]:
             return None
         return int(cells[6])
     return None
 
 
-def main():
-    args = parse_args()
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: the library has no multi-GPU path "
-              "(run with --gpus 1)", file=sys.stderr)
-        sys.exit(2)
+# ------------------------------------------------ one measurement (child) --
 
+def measure(args) -> dict:
+    """Measures one workload in this process (the GPU is used here)."""
     import numpy as np
     import torch
 
@@ -173,24 +247,36 @@ def main():
     torch.cuda.synchronize()
 
     stream = torch.cuda.Stream()
+
+    def capture(fn, n):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(g, stream=stream):
+                for r in range(n):
+                    fn(r)
+        torch.cuda.synchronize()
+        return g
+
+    def time_graph(g, reps, per):
+        """µs per call of `reps` replays of a graph holding `per` calls."""
+        with torch.cuda.stream(stream):
+            g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                g.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (reps * per)
+
     mode = "hip_graph"
     graphs = []
     if not args.no_graph:
         try:
-            with torch.cuda.stream(stream):
-                g_full = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g_full, stream=stream):
-                    for r in range(R):
-                        step(r)
-                graphs.append(g_full)
-                rem = steps % R
-                if rem:
-                    g_rem = torch.cuda.CUDAGraph()
-                    with torch.cuda.graph(g_rem, stream=stream):
-                        for r in range(rem):
-                            step(r)
-                    graphs.append(g_rem)
-            torch.cuda.synchronize()
+            graphs.append(capture(step, R))
+            if steps % R:
+                graphs.append(capture(step, steps % R))
         except Exception as exc:  # graph capture unavailable: time eagerly
             print(f"graph capture failed ({exc}); timing eager calls", file=sys.stderr)
             graphs = []
@@ -221,6 +307,25 @@ def main():
     ms_per_step = start.elapsed_time(end) / steps
     us = ms_per_step * 1e3
 
+    # stream-enqueue figure: the same K steps as eager calls from the host
+    with torch.cuda.stream(stream):
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(steps):
+            step(i % R)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    eager_us = e0.elapsed_time(e1) * 1e3 / steps
+    # cache-inflated figure: one weight copy, so repeated calls may hit the
+    # Infinity Cache
+    r1_us = None
+    if graphs:
+        L1 = 16
+        g1 = capture(lambda r: step(0), L1)
+        r1_us = time_graph(g1, max(1, min(steps, 256) // L1), L1)
+        del g1
+
     # ---- per-kernel durations: for each entry point, a HIP graph of max(R, 16)
     # back-to-back launches of it alone (weights rotating as in the headline
     # loop), replayed between two events on the launch stream.  The layer
@@ -238,28 +343,20 @@ def main():
     L = max(R, 16)
     reps = max(1, min(steps, 256) // L)
     for name, fn in parts.items():
-        with torch.cuda.stream(stream):
-            if graphs:
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g, stream=stream):
-                    for r in range(L):
-                        fn(r % R)
-                g.replay()
-                torch.cuda.synchronize()
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                for _ in range(reps):
-                    g.replay()
-                e1.record(stream)
-            else:
+        if graphs:
+            g = capture(lambda r, fn=fn: fn(r % R), L)
+            kernel_us[name] = time_graph(g, reps, L)
+            del g
+        else:
+            with torch.cuda.stream(stream):
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record(stream)
                 for _ in range(reps):
                     for r in range(L):
                         fn(r % R)
                 e1.record(stream)
-        torch.cuda.synchronize()
-        kernel_us[name] = e0.elapsed_time(e1) * 1e3 / (reps * L)
+            torch.cuda.synchronize()
+            kernel_us[name] = e0.elapsed_time(e1) * 1e3 / (reps * L)
 
     if args.calibrate_copy:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
@@ -302,7 +399,7 @@ def main():
 
     gbps = touched / (us * 1e-6) / 1e9
     tflops = layer_flops / (us * 1e-6) / 1e12
-    result = {
+    return {
         "metric": METRIC,
         "value": round(us, 2),
         "unit": "us/call",
@@ -325,13 +422,96 @@ def main():
         "hbm_gbps": round(gbps, 1),
         "hbm_frac": round(gbps / HBM_PEAK_GBS, 4),
         "tflops": round(tflops, 3),
+        "tflops_frac": round(tflops / BF16_PEAK_TFLOPS, 4),
         "algorithmic_bytes_per_call": touched,
+        "algorithmic_flops_per_call": layer_flops,
+        "stream_enqueue_us": round(eager_us, 2),
+        "cache_inflated_r1_us": None if r1_us is None else round(r1_us, 2),
         "kernel_us": {n: round(v, 2) for n, v in kernel_us.items()},
         "roofline": roof,
     }
+
+
+# --------------------------------------------------- orchestration (parent) --
+
+def _under_profiler() -> bool:
+    return any(key.startswith("ROCPROF") for key in os.environ)
+
+
+def run_children(args, wid, steps, warmup):
+    """`args.runs` fresh processes measuring workload `wid`; returns their
+    records sorted by value (µs/call)."""
+    cmd = [sys.executable, os.path.abspath(__file__), "--child", "--no-cpu-baseline",
+           "--workload", str(wid), "--layout", args.layout]
+    if steps is not None:
+        cmd += ["--steps", str(steps)]
+    if warmup is not None:
+        cmd += ["--warmup", str(warmup)]
+    if args.rotations:
+        cmd += ["--rotations", str(args.rotations)]
+    if args.bm is not None:
+        cmd += ["--bm", str(args.bm)]
+    if args.no_graph:
+        cmd += ["--no-graph"]
+    recs = []
+    for run in range(args.runs):
+        t0 = time.perf_counter()
+        p = subprocess.run(cmd, stdout=subprocess.PIPE, text=True, timeout=CHILD_TIMEOUT_S)
+        if p.returncode != 0:
+            print(f"bench child (workload {wid}, run {run}) failed with status {p.returncode}",
+                  file=sys.stderr)
+            sys.exit(p.returncode if p.returncode > 0 else 1)
+        line = [ln for ln in p.stdout.splitlines() if ln.startswith("{")][-1]
+        recs.append(json.loads(line))
+        print(f"[bench] workload {wid} run {run}: {recs[-1]['value']} us/call "
+              f"({time.perf_counter() - t0:.1f} s)", file=sys.stderr, flush=True)
+    return sorted(recs, key=lambda r: r["value"])
+
+
+def median_record(recs):
+    rec = dict(recs[(len(recs) - 1) // 2])  # recs are sorted: the (lower) middle run
+    vals = [r["value"] for r in recs]
+    rec["runs_us"] = vals
+    rec["value"] = round(statistics.median(vals), 2)
+    rec["method"] = f"median of {len(recs)} processes"
+    return rec
+
+
+def main():
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    if args.child or _under_profiler():
+        result = measure(args)
+        if not args.no_cpu_baseline and not args.child:
+            from moe_inputs import make_workload
+            result["cpu_baseline"] = cpu_baseline(make_workload(args.workload), args.cpu_seconds)
+        print(json.dumps(result), flush=True)
+        return
+
+    # this process only starts children and runs the CPU oracle
+    from moe_inputs import make_workload
+    others = ([w for w in GPTOSS_WORKLOADS if w != args.workload] if args.others is None
+              else [] if args.others == "none" else [int(w) for w in args.others.split(",")])
+    result = median_record(run_children(args, args.workload, args.steps, args.warmup))
+    subs = {}
+    for wid in others:
+        subs[wid] = median_record(run_children(args, wid, None, None))
     if not args.no_cpu_baseline:
-        full = make_workload(wid)
-        result["cpu_baseline"] = cpu_baseline(full, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(make_workload(args.workload), args.cpu_seconds)
+        for wid in others:
+            subs[wid]["cpu_baseline"] = cpu_baseline(make_workload(wid), args.cpu_seconds)
+    keep = ("value", "unit", "method", "runs_us", "steps", "warmup", "ms_per_step", "config",
+            "tokens_per_s", "hbm_gbps", "hbm_frac", "tflops", "tflops_frac",
+            "algorithmic_bytes_per_call", "algorithmic_flops_per_call", "stream_enqueue_us",
+            "cache_inflated_r1_us", "kernel_us", "roofline", "cpu_baseline")
+    result["workloads"] = {subs[w]["config"]["workload"]: {key: subs[w][key] for key in keep
+                                                            if key in subs[w]}
+                           for w in others}
     print(json.dumps(result), flush=True)
 
 

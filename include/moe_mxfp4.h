@@ -301,10 +301,12 @@ moe_status moe_route_tiles(const uint16_t* x, const float* w_router, const float
  *               workspace must not overlap in time.  If a wait ever gave up
  *               (a GPU too busy to run the grid for about a second), the
  *               int at byte 8 is set and the outputs are unspecified until
- *               the region is zeroed.  The environment variable
- *               MOE_ONE_TOKEN_SPIN_LIMIT (read on the host at every call)
- *               lowers the number of polls a wait makes before it gives up,
- *               for tests of that path; unset, the bound is 2^20 polls.
+ *               the region is zeroed.  The int at byte 12 bounds the
+ *               polls: zero (as zeroed) keeps the default of 2^20 re-polls
+ *               per wait; a value n > 0, written by the caller between
+ *               calls, lowers it to n - 1 re-polls (a test of the give-up
+ *               path writes 1).  It is read on the device at every call, so
+ *               a captured graph follows the current value.
  */
 size_t moe_layer_one_token_workspace_bytes(int H, int I, int E, int k);
 size_t moe_layer_one_token_sync_bytes(int H);

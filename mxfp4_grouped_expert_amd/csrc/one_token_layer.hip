@@ -37,15 +37,16 @@
 // last routing workgroup waits for the others' stamps.  The
 // epoch is read by every workgroup at its start and advanced by the last
 // of them to check in (a two-level arrival tree), so each call sees its own
-// value.  Polls are bounded: one that gives up sets the error word and its
-// workgroup carries on with whatever it read (the launch still ends).
+// value.  Only thread 0 of a workgroup reads the epoch; the others take it
+// from LDS after a barrier, so no wave can read an epoch that its own
+// workgroup's check-in already advanced.  Polls are bounded: one that gives
+// up sets the error word and its workgroup carries on with whatever it read
+// (the launch still ends).
 //
 // Contention.  Atomics and polls on one address are serialised by the
 // memory system, so hot words have their own 128-byte lines: the plan is
 // written to 16 replica lines (workgroup i reads replica i % 16) and the
 // arrival tree spreads its counters over 16 leaf lines and a top line.
-#include <cstdlib>
-
 #include "expert_common.h"
 #include "moe_device.h"
 #include "moe_launch.h"
@@ -82,7 +83,8 @@ struct Sync {
   int reserved;
   int epoch;             // calls begun by every workgroup
   int error;             // set (sticky) when a poll gives up
-  int pad0[kLine - 3];
+  int poll_limit;        // 0: kSpinLimit; n > 0: waits give up after n - 1 re-polls
+  int pad0[kLine - 4];
   Tree arrivals;         // every workgroup, once it has read the epoch
   ReplicaLine rep[kReplicas];
   u64 routed[kMaxRoute]; // routing workgroup i: stamp once its partials are stored
@@ -163,7 +165,6 @@ struct Args {
   const uint8_t* w2_s;
   int H, I, E, k, gating;
   bool blocked;    // code matrices in the blocked layout
-  int spin_limit;  // polls before a wait gives up
   int split_len, splits, n_route;
   int32_t* topk_ids;
   float* topk_weights;
@@ -179,15 +180,32 @@ struct Args {
   uint16_t* out;
 };
 
+// This call's epoch and poll bound, as thread 0 read them (the caller
+// publishes them to the workgroup through LDS and a barrier).
+struct CallState {
+  int epoch;
+  int spin_limit;
+};
+__device__ __forceinline__ CallState read_call_state(const Sync* S) {
+  const int epoch = ld_agent(&S->epoch);
+  const int pl = ld_agent(&S->poll_limit);
+  return CallState{epoch, pl > 0 ? pl - 1 : kSpinLimit};
+}
+
 // ---------------------------------------------------------------- routing
-__device__ void routing_role(const Args& a, int rid, unsigned char* lds) {
-  const int epoch = ld_agent(&a.sync->epoch);
-  const unsigned stamp = (unsigned)epoch + 1u;
+__device__ void routing_role(const Args& a, int rid, unsigned char* lds, CallState* s_call) {
+  // thread 0's loads stay in flight while the partial logits are computed
+  CallState cs{0, 0};
+  if (threadIdx.x == 0) cs = read_call_state(a.sync);
   const int eb = (a.E + kExpPerBlock - 1) / kExpPerBlock;
   logits_partial_body<true, 1>(a.x, a.w_router, 1, a.H, a.E, a.split_len, a.partial, 0, rid % eb,
                                rid / eb);
+  if (threadIdx.x == 0) *s_call = cs;
   __builtin_amdgcn_s_waitcnt(0);  // this workgroup's partials are stored
   __syncthreads();
+  cs = *s_call;
+  const int epoch = cs.epoch, spin_limit = cs.spin_limit;
+  const unsigned stamp = (unsigned)epoch + 1u;
   int* s_ids = reinterpret_cast<int*>(lds);
   float* s_w = reinterpret_cast<float*>(s_ids + kMaxTopk);
   if (threadIdx.x == 0) {
@@ -209,7 +227,7 @@ __device__ void routing_role(const Args& a, int rid, unsigned char* lds) {
       use[i] = w < a.n_route - 1;
       src[i] = &a.sync->routed[min(w, kMaxRoute - 1)];
     }
-    settle(src, use, v, stamp, &a.sync->error, a.spin_limit);
+    settle(src, use, v, stamp, &a.sync->error, spin_limit);
   }
   double val[4];
   one_token_logits(a.partial, a.bias, a.E, a.splits, val);
@@ -390,7 +408,7 @@ __device__ __forceinline__ void down_issue(const Args& a, int cb, int e, DownLoa
 }
 
 __device__ __forceinline__ void down_finish(const Args& a, int g, int cb, int slot,
-                                            unsigned stamp, const ReplicaLine* R,
+                                            unsigned stamp, int spin_limit, const ReplicaLine* R,
                                             unsigned char* lds, DownLoads& L) {
   const int H = a.H, I = a.I, K = I, KB = K / 32;
   const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, grp = lane >> 4;
@@ -418,7 +436,7 @@ __device__ __forceinline__ void down_finish(const Args& a, int g, int cb, int sl
       use[i] = d < spr * 4;
       src[i] = hrow + min(min(d, spr * 4 - 1) >> 2, cpr - 1) * 4 + (d & 3);
     }
-    settle(src, use, v, stamp, &a.sync->error, a.spin_limit);
+    settle(src, use, v, stamp, &a.sync->error, spin_limit);
 #pragma unroll
     for (int i = 0; i < kPer; ++i)
       if (use[i]) dst[tid + i * kThreads] = (unsigned)v[i];
@@ -465,7 +483,7 @@ __device__ __forceinline__ void down_finish(const Args& a, int g, int cb, int sl
     src[kMaxTopk + j] = a.y + (size_t)jc * H + n_base + tid;
     use[kMaxTopk + j] = j < a.k && j != slot;
   }
-  settle(src, use, v, stamp, &a.sync->error, a.spin_limit);
+  settle(src, use, v, stamp, &a.sync->error, spin_limit);
   float wj[kMaxTopk], yj[kMaxTopk];
 #pragma unroll
   for (int j = 0; j < kMaxTopk; ++j) {
@@ -488,7 +506,7 @@ __device__ __forceinline__ void down_finish(const Args& a, int g, int cb, int sl
 // the workgroup's gate/up job is done (requested together, the two streams
 // measured slower).
 template <bool BLK>
-__device__ void gemm_role(const Args& a, int j, unsigned char* lds) {
+__device__ void gemm_role(const Args& a, int j, unsigned char* lds, CallState* s_call) {
   const int ncbI = a.I / kRowsPerBlock, ncbH = a.H / kRowsPerBlock;
   unsigned* s_plan = reinterpret_cast<unsigned*>(lds + kRegion0 + 2 * kScaleRunMax +
                                                  2 * 2 * kRowsPerBlock * 256);
@@ -498,19 +516,22 @@ __device__ void gemm_role(const Args& a, int j, unsigned char* lds) {
   for (int t = a.k - 1; t >= 0; --t)
     if (j >= (t + 1) * ncbI && j < (t + 1) * ncbI + ncbH) t0 = t;
 
-  const int epoch = ld_agent(&a.sync->epoch);
-  const unsigned stamp = (unsigned)epoch + 1u;
   const ReplicaLine* R = &a.sync->rep[blockIdx.x % kReplicas];
   if (threadIdx.x == 0) {
-    check_in(a.sync, epoch);
+    const CallState cs = read_call_state(a.sync);
+    *s_call = cs;
+    check_in(a.sync, cs.epoch);
     const u64* src[2] = {&R->plan[g_gu], &R->plan[min(t0, a.k - 1)]};
     const bool use[2] = {true, true};
     u64 v[2];
-    settle(src, use, v, stamp, &a.sync->error, a.spin_limit);
+    settle(src, use, v, (unsigned)cs.epoch + 1u, &a.sync->error, cs.spin_limit);
     s_plan[0] = (unsigned)v[0];
     s_plan[1] = (unsigned)v[1];
   }
   __syncthreads();
+  const CallState cs = *s_call;
+  const unsigned stamp = (unsigned)cs.epoch + 1u;
+  const int spin_limit = cs.spin_limit;
   // clamped: the indices stay in bounds whatever the words hold
   auto expert = [&](unsigned p) { return min((int)(p & 0xffffu), a.E - 1); };
   auto slot_of = [&](unsigned p) { return min((int)(p >> 16), a.k - 1); };
@@ -531,7 +552,7 @@ __device__ void gemm_role(const Args& a, int j, unsigned char* lds) {
         const u64* src[1] = {&R->plan[t]};
         const bool use[1] = {true};
         u64 v[1];
-        settle(src, use, v, stamp, &a.sync->error, a.spin_limit);
+        settle(src, use, v, stamp, &a.sync->error, spin_limit);
         s_plan[2] = (unsigned)v[0];
       }
       __syncthreads();
@@ -547,13 +568,13 @@ __device__ void gemm_role(const Args& a, int j, unsigned char* lds) {
         const u64* src[1] = {a.h + (size_t)t * a.I / 2 + (size_t)(cb % (a.I / 32)) * 16};
         const bool use[1] = {true};
         u64 v[1];
-        settle(src, use, v, stamp, &a.sync->error, a.spin_limit);
+        settle(src, use, v, stamp, &a.sync->error, spin_limit);
       }
       __syncthreads();
     }
     DownLoads dl;
     down_issue(a, cb, expert(p), dl);
-    down_finish(a, t, cb, slot_of(p), stamp, R, lds, dl);
+    down_finish(a, t, cb, slot_of(p), stamp, spin_limit, R, lds, dl);
   }
 }
 
@@ -562,10 +583,11 @@ constexpr int kLdsBytes = kRegion0 + 2 * kScaleRunMax + 2 * 2 * kRowsPerBlock * 
 template <bool BLK>
 __global__ __launch_bounds__(kThreads, 4) void moe_layer_one_token_kernel(Args a) {
   __shared__ __align__(16) unsigned char lds[kLdsBytes];
+  __shared__ CallState s_call;
   if ((int)blockIdx.x < a.n_route)
-    routing_role(a, blockIdx.x, lds);
+    routing_role(a, blockIdx.x, lds, &s_call);
   else
-    gemm_role<BLK>(a, blockIdx.x - a.n_route, lds);
+    gemm_role<BLK>(a, blockIdx.x - a.n_route, lds, &s_call);
 }
 
 size_t round_up(size_t n) { return (n + 255) / 256 * 256; }
@@ -604,13 +626,6 @@ void launch_layer_one_token(const uint16_t* x, const float* w_router, const floa
   a.x = x; a.w_router = w_router; a.bias = bias;
   a.w13_q = w13_q; a.w13_s = w13_s; a.w2_q = w2_q; a.w2_s = w2_s;
   a.H = H; a.I = I; a.E = E; a.k = k; a.gating = gating; a.blocked = blocked;
-  // A test of the give-up path lowers the poll bound through the
-  // environment (read at every call; values outside [0, kSpinLimit) ignored).
-  a.spin_limit = kSpinLimit;
-  if (const char* env = getenv("MOE_ONE_TOKEN_SPIN_LIMIT")) {
-    const long v = strtol(env, nullptr, 10);
-    if (v >= 0 && v < kSpinLimit) a.spin_limit = (int)v;
-  }
   a.split_len = p.split_len;
   a.splits = p.splits;
   a.n_route = p.splits * ((E + kExpPerBlock - 1) / kExpPerBlock);

@@ -20,16 +20,44 @@ import torch
 from . import binding as B
 
 
+def _expect(t, name: str, dtypes, shape, device=None):
+    """Raises ValueError unless t is a contiguous tensor of one of `dtypes`
+    and exactly `shape`, on `device` (when given) and on a GPU.  Shape, dtype
+    and layout are checked before the device, so a malformed argument is
+    named whatever device it is on; nothing is enqueued either way."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a tensor")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
 class MoeLayer:
     def __init__(self, w_router: torch.Tensor, bias: Optional[torch.Tensor],
                  w13_q: torch.Tensor, w13_s: torch.Tensor, w2_q: torch.Tensor,
                  w2_s: torch.Tensor, k: int, gating: str = "softmax",
                  layout: str = "blocked"):
-        self.device = w13_q.device
         self.gating = B.gating_code(gating)
         self.layout = B.layout_code(layout)
+        if not isinstance(w13_q, torch.Tensor) or w13_q.dim() != 3:
+            raise ValueError("w13_q must be a uint8 tensor [E, 2I, H/2]")
         self.E, I2, Hh = w13_q.shape
         self.H, self.I, self.k = Hh * 2, I2 // 2, int(k)
+        if self.H % 32 or self.I % 32 or self.H == 0 or self.I == 0:
+            raise ValueError("H and I must be positive multiples of 32")
+        if not 1 <= self.k <= min(self.E, 8):
+            raise ValueError("k must lie in [1, min(E, 8)]")
+        _expect(w_router, "w_router", (torch.float32,), (self.E, self.H))
+        self.device = w_router.device
+        if bias is not None:
+            _expect(bias, "bias", (torch.float32,), (self.E,), self.device)
         self.w_router, self.bias = w_router, bias
         self.set_weights(w13_q, w13_s, w2_q, w2_s, repack=True)
         self.T = None
@@ -38,6 +66,11 @@ class MoeLayer:
         """Point the layer at another copy of the expert weights (same shapes).
         The codes are taken as they are (already in the layer's layout) unless
         repack is set, in which case canonical codes are repacked to it."""
+        E, H, I = self.E, self.H, self.I
+        _expect(w13_q, "w13_q", (torch.uint8,), (E, 2 * I, H // 2), self.device)
+        _expect(w13_s, "w13_s", (torch.uint8,), (E, 2 * I, H // 32), self.device)
+        _expect(w2_q, "w2_q", (torch.uint8,), (E, H, I // 2), self.device)
+        _expect(w2_s, "w2_s", (torch.uint8,), (E, H, I // 32), self.device)
         if repack and self.layout == B.LAYOUTS["blocked"]:
             w13_q, w2_q = B.moe_repack_weights(w13_q), B.moe_repack_weights(w2_q)
         self.w13_q, self.w13_s, self.w2_q, self.w2_s = w13_q, w13_s, w2_q, w2_s
@@ -82,6 +115,9 @@ class MoeLayer:
 
     def route_only(self, x: torch.Tensor):
         """moe_route (or, for small batches, moe_route_tiles) into the layer's buffers."""
+        self.check_input(x)
+        if x.shape[0] != self.T:
+            raise ValueError(f"x has {x.shape[0]} tokens; the layer is planned for {self.T}")
         lib, s = self._args()
         p = self._p
         T, E, H, k = x.shape[0], self.E, self.H, self.k
@@ -114,6 +150,9 @@ class MoeLayer:
 
     def gateup_only(self, x: torch.Tensor):
         """moe_gateup_swiglu into the layer's h workspace."""
+        self.check_input(x)
+        if x.shape[0] != self.T:
+            raise ValueError(f"x has {x.shape[0]} tokens; the layer is planned for {self.T}")
         lib, s = self._args()
         p = self._p
         h, _ = self._h_y()
@@ -139,9 +178,18 @@ class MoeLayer:
         B._check(lib.moe_combine(p(y), p(self.topk_weights), self.T, self.H, self.k, p(self.out),
                                  s), "moe_combine")
 
+    def check_input(self, x: torch.Tensor):
+        """Raises ValueError unless x is a contiguous bf16 [T, H] tensor (or its
+        bits as int16 or uint16) on the
+        layer's device (the kernels read T*H elements of it)."""
+        if not isinstance(x, torch.Tensor) or x.dim() != 2:
+            raise ValueError("x must be a bf16 tensor [T, H]")
+        _expect(x, "x", B._BF16, (x.shape[0], self.H), self.device)
+
     def __call__(self, x: torch.Tensor) -> torch.Tensor:
         """One layer call: routing and tiles, then moe_forward (one launch for
-        one token)."""
+        one token).  x: contiguous bf16 [T, H] on the layer's device."""
+        self.check_input(x)
         T = x.shape[0]
         if self.T != T:
             self.plan(T)

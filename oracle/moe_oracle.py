@@ -237,7 +237,7 @@ def combine(y: np.ndarray, w: np.ndarray) -> np.ndarray:
     return np.einsum("tj,tjh->th", w, y.reshape(T, k, -1))
 
 
-def moe_layer(inp: dict, BM: int = 16, tokens=None) -> dict:
+def moe_layer(inp: dict, BM: int = 16, tokens=None, progress=None) -> dict:
     """The whole layer in float64.
 
     inp holds x, w_router, bias, w13_q, w13_s, w2_q, w2_s and k (and
@@ -245,6 +245,8 @@ def moe_layer(inp: dict, BM: int = 16, tokens=None) -> dict:
     ``tokens`` (an index array) only those tokens' outputs are evaluated
     (routing and the tile table still cover every token); experts are
     decoded one at a time so the largest layer stays within memory.
+    ``progress``, if given, is called as progress(e, E) after expert e's
+    rows are done (for logging only; it sees no values).
     """
     k = int(inp["k"])
     E = inp["w13_q"].shape[0]
@@ -266,6 +268,8 @@ def moe_layer(inp: dict, BM: int = 16, tokens=None) -> dict:
             continue
         y[slots] = expert_ffn(x64[slots // k], inp["w13_q"][e], inp["w13_s"][e],
                               inp["w2_q"][e], inp["w2_s"][e])
+        if progress is not None:
+            progress(e, E)
     out = combine(y, w)
     return dict(topk_ids=ids, topk_weights=w, logits=L, expert_offsets=offsets,
                 sorted_ids=sorted_ids, tiles=tiles, num_tiles=num_tiles,

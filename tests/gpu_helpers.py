@@ -76,19 +76,36 @@ def assert_tiles_equal(g: dict, r: dict):
 def assert_out_close(got: np.ndarray, want: np.ndarray, what: str = "out"):
     assert np.all(np.isfinite(got)), f"{what}: non-finite values"
     rel_l2, max_abs, scale = out_errors(got, want)
-    log(f"{what}: relL2={rel_l2:.3e} max_abs={max_abs:.3e} max|ref|={scale:.3e}")
+    log(f"{what}: {got.shape[0]} rows relL2={rel_l2:.3e} max_abs={max_abs:.3e} "
+        f"max|ref|={scale:.3e} max/scale={max_abs / max(scale, 1e-300):.3e}")
     assert rel_l2 <= REL_L2, f"{what}: relative L2 {rel_l2:.3e} > {REL_L2}"
     assert max_abs <= MAX_REL * scale, f"{what}: max abs {max_abs:.3e} > {MAX_REL} * {scale:.3e}"
 
 
-def check_all(inp: dict, BM: int, tokens=None, dev="cuda") -> dict:
-    """Run the GPU path on `inp` and hold every output to the parity bar."""
+def progress_logger(what: str, every: int = 16):
+    """An oracle progress callback that logs every `every` experts."""
+    def cb(e, E):
+        if (e + 1) % every == 0 or e + 1 == E:
+            log(f"{what}: oracle expert {e + 1}/{E}")
+    return cb
+
+
+def oracle_layer(inp: dict, BM: int, tokens=None) -> dict:
+    """oracle.moe_layer with progress lines (long at the 120b shapes)."""
+    what = f"{inp.get('name', '?')} BM={BM}"
+    log(f"{what}: oracle over {inp['T'] if tokens is None else len(tokens)} tokens")
+    return oracle.moe_layer(inp, BM=BM, tokens=tokens, progress=progress_logger(what))
+
+
+def check_all(inp: dict, BM: int, tokens=None, dev="cuda", ref=None) -> dict:
+    """Run the GPU path on `inp` and hold every output to the parity bar
+    (against `ref`, an oracle result for the same input and BM, when given)."""
     log(f"{inp.get('name', '?')} BM={BM}: upload")
     d = to_device(inp, dev)
     log(f"{inp.get('name', '?')} BM={BM}: run")
     g = run_gpu(d, inp["k"], BM)
-    log(f"{inp.get('name', '?')} BM={BM}: oracle")
-    r = oracle.moe_layer(inp, BM=BM, tokens=tokens)
+    del d
+    r = ref if ref is not None else oracle_layer(inp, BM, tokens)
     assert_routing_equal(g, r)
     assert_tiles_equal(g, r)
     sel = r["tokens"]

@@ -137,24 +137,23 @@ def test_layer_graph_replays_one_launch():
         assert _calls_and_error(layer.one_ws) == (calls + 2 * (rep + 1), 0)
 
 
-def test_bounded_wait_gives_up_reports_and_recovers(monkeypatch):
-    """With the poll bound forced to zero (from the host) a wait that finds
-    its data not yet there gives up at once: the call still completes, its
-    error word is set, and after the sync region is zeroed the next call is
-    exact again."""
+def test_bounded_wait_gives_up_reports_and_recovers():
+    """With the poll bound lowered to zero re-polls (the sync region's int at
+    byte 12 set to 1 from the host) a wait that finds its data not yet there
+    gives up at once: the call still completes, its error word is set, and
+    after the sync region is zeroed the next call is exact again."""
     H, I, E, k = 256, 256, 16, 4
     inp = make_random(T=1, H=H, E=E, k=k, I=I, seed=77)
     d = to_device(inp)
     BM = moe.pick_bm(1, k, E)
     want = _unfused(d, k, BM)
     ws = moe.zeroed_layer_one_token_workspace(H, I, E, k, d["x"].device)
-    monkeypatch.setenv("MOE_ONE_TOKEN_SPIN_LIMIT", "0")
+    ws[12:16].view(torch.int32).fill_(1)
     log("one-token layer: poll bound 0")
     _fused(d, k, BM, ws)
     torch.cuda.synchronize()
     calls, err = _calls_and_error(ws)
     assert calls == 1 and err == 1, (calls, err)
-    monkeypatch.delenv("MOE_ONE_TOKEN_SPIN_LIMIT")
     ws.zero_()
     log("one-token layer: normal bound after zeroing")
     got = _fused(d, k, BM, ws)

@@ -1,10 +1,11 @@
 """GPU parity: the HIP library against the float64 oracle (needs a gfx950 GPU).
 
 Covers the five gpt-oss-shaped workloads (tiny; 20b decode T=1; 20b decode
-T=64 with a skewed router; 120b decode T=64; 120b prefill T=4096), small
-random shapes with ragged K-block counts and multi-chunk tile scatters, and
-the method's degenerate cases.  At the two 120b workloads routing and the
-tile table are compared in full and the output on sampled tokens.
+T=64 with a skewed router; 120b decode T=64; 120b prefill T=4096), every
+token of each, small random shapes with ragged K-block counts and
+multi-chunk tile scatters, a constructed routing that gives the 128-row
+matrix-core kernel every fragment count, and the method's degenerate
+cases.
 """
 import numpy as np
 import pytest
@@ -16,7 +17,7 @@ from moe_inputs import (identical_experts, make_activations, make_random, make_w
                         make_workload, WORKLOADS)
 
 from gpu_helpers import (assert_out_close, assert_routing_equal, assert_tiles_equal, check_all,
-                         log, run_gpu, to_device)
+                         log, oracle_layer, run_gpu, to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -34,6 +35,30 @@ def w120b():
     return make_weights(w.E, w.H, w.I, w.model_id)
 
 
+# Oracle results over every token of a workload, by (workload, BM): the
+# separate-launch test and the benchmark-configuration test of a workload
+# compare against the same float64 result.  At the 120b shapes the oracle's
+# cost is dominated by decoding each expert once (about 40 s for all 128),
+# not by the number of tokens, so every token is compared.
+_ORACLE = {}
+
+
+def full_oracle(inp: dict, BM: int) -> dict:
+    key = (inp["wid"], BM)
+    if key not in _ORACLE:
+        r = oracle_layer(inp, BM)
+        r.pop("y")  # [T*k, H] float64: not needed after the combine
+        _ORACLE[key] = r
+    return _ORACLE[key]
+
+
+def workload_input(wid: int, w120b) -> dict:
+    inp = make_workload(wid, weights=wid < 3)
+    if wid >= 3:
+        inp.update(w120b)
+    return inp
+
+
 # ------------------------------------------------------------- workloads --
 
 @pytest.mark.parametrize("BM", [16, 32, 64, 128])
@@ -44,22 +69,29 @@ def test_tiny_workload(BM):
 @pytest.mark.parametrize("wid", [1, 2])
 def test_gptoss20b_decode(wid):
     inp = make_workload(wid)
-    check_all(inp, moe.pick_bm(inp["T"], inp["k"], inp["E"]))
-
-
-def test_gptoss120b_decode_T64(w120b):
-    inp = make_workload(3, weights=False)
-    inp.update(w120b)
-    check_all(inp, moe.pick_bm(inp["T"], inp["k"], inp["E"]), tokens=np.arange(0, 64, 4))
-
-
-def test_gptoss120b_prefill_T4096(w120b):
-    inp = make_workload(4, weights=False)
-    inp.update(w120b)
     BM = moe.pick_bm(inp["T"], inp["k"], inp["E"])
-    toks = np.array([0, 1, 511, 1024, 2047, 2048, 3000, 4095])
-    res = check_all(inp, BM, tokens=toks)
-    # every token has k distinct experts and the table covers every slot once
+    check_all(inp, BM, ref=full_oracle(inp, BM))
+
+
+@pytest.mark.timeout(600)
+def test_gptoss120b_decode_T64(w120b):
+    inp = workload_input(3, w120b)
+    BM = moe.pick_bm(inp["T"], inp["k"], inp["E"])
+    res = check_all(inp, BM, ref=full_oracle(inp, BM))
+    assert len(res["ref"]["tokens"]) == inp["T"]
+
+
+@pytest.mark.timeout(600)
+def test_gptoss120b_prefill_T4096(w120b):
+    inp = workload_input(4, w120b)
+    BM = moe.pick_bm(inp["T"], inp["k"], inp["E"])
+    res = check_all(inp, BM, ref=full_oracle(inp, BM))
+    # every token is compared, so every (expert, tile) pair of the table and
+    # every row of each partial tile is checked
+    assert len(res["ref"]["tokens"]) == inp["T"]
+    tiles = res["ref"]["tiles"]
+    log(f"prefill: {len(tiles)} tiles, {int((tiles[:, 2] < BM).sum())} partial, rows "
+        f"{int(tiles[:, 2].min())}..{int(tiles[:, 2].max())}")
     ids = res["gpu"]["topk_ids"]
     assert all(len(set(r)) == inp["k"] for r in ids)
     assert sorted(res["gpu"]["sorted_ids"].tolist()) == list(range(inp["T"] * inp["k"]))
@@ -67,15 +99,12 @@ def test_gptoss120b_prefill_T4096(w120b):
 
 # The benchmark's own configuration: MoeLayer with its default plan (the
 # weights repacked into the blocked layout, the single launch at T = 1, the
-# fused routing up to 16 tokens), one call per workload, against the oracle.
-BENCH_TOKENS = {1: None, 2: None, 3: np.arange(0, 64, 4), 4: np.array([0, 7, 1500, 2048, 4095])}
-
-
+# fused routing up to 16 tokens), one call per workload, against the oracle
+# over every token.
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("wid", [1, 2, 3, 4])
 def test_bench_configuration_matches_oracle(wid, w120b):
-    inp = make_workload(wid, weights=wid < 3)
-    if wid >= 3:
-        inp.update(w120b)
+    inp = workload_input(wid, w120b)
     d = to_device(inp)
     layer = moe.MoeLayer(d["w_router"], d["bias"], d["w13_q"], d["w13_s"], d["w2_q"], d["w2_s"],
                          inp["k"], gating=inp["gating"]).plan(inp["T"])
@@ -84,12 +113,64 @@ def test_bench_configuration_matches_oracle(wid, w120b):
     ids = layer.topk_ids.cpu().numpy()
     wts = layer.topk_weights.cpu().numpy()
     del layer, d
-    log(f"bench configuration, workload {wid}: oracle")
-    r = oracle.moe_layer(inp, BM=moe.pick_bm(inp["T"], inp["k"], inp["E"]),
-                         tokens=BENCH_TOKENS[wid])
+    r = full_oracle(inp, moe.pick_bm(inp["T"], inp["k"], inp["E"]))
     np.testing.assert_array_equal(ids, r["topk_ids"])
     np.testing.assert_allclose(wts, r["topk_weights"], rtol=0, atol=1e-6)
-    assert_out_close(out[r["tokens"]], r["out"])
+    assert len(r["tokens"]) == inp["T"]
+    assert_out_close(out, r["out"], f"bench configuration, workload {wid}")
+
+
+# Constructed routing for the 128-row matrix-core kernel: expert loads chosen
+# so that the tiles hold every fragment count 1..8 (rows 1..128, with both
+# parities of the split between a SIMD's two waves), full tiles followed by
+# remainders, and a 256-row expert; partial column blocks on both GEMMs (I =
+# 320: 192 + 128 gate/up columns; H = 256 of a 384-column down unit) and
+# ragged K (5 stages of 64 on the down side).  The oracle side is composed of
+# the oracle's own steps (tile table, per-expert FFN, combine).
+MMA_COUNTS = [1, 16, 17, 33, 48, 49, 65, 80, 81, 96, 97, 112, 113, 127, 128, 129, 160, 256]
+
+
+def test_mma_kernel_every_fragment_count():
+    E, k, H, I = len(MMA_COUNTS), 2, 256, 320
+    flat_sorted = np.repeat(np.arange(E, dtype=np.int32), MMA_COUNTS)
+    N = flat_sorted.size
+    assert N % k == 0 and max(MMA_COUNTS) <= N // k
+    T = N // k
+    ids = np.stack([flat_sorted[:T], flat_sorted[T:]], axis=1)  # distinct per token
+    assert np.all(ids[:, 0] != ids[:, 1])
+    rng = np.random.default_rng(2024)
+    w = rng.uniform(0.1, 1.0, size=(T, k))
+    w = (w / w.sum(axis=1, keepdims=True)).astype(np.float32)
+    inp = make_random(T=T, H=H, E=E, k=k, I=I, seed=909)
+    BM = 128
+    assert T * k >= 32 * E  # the launchers pick the matrix-core kernel
+    d = to_device(inp)
+    ids_d = torch.from_numpy(ids.astype(np.int32)).cuda()
+    off, srt, tiles, nt = moe.moe_build_tiles(ids_d, E, BM)
+    for layout in ("canonical", "blocked"):
+        if layout == "blocked":
+            q13, q2 = moe.moe_repack_weights(d["w13_q"]), moe.moe_repack_weights(d["w2_q"])
+        else:
+            q13, q2 = d["w13_q"], d["w2_q"]
+        log(f"matrix-core fragments, layout {layout}")
+        out = moe.moe_forward(d["x"], q13, d["w13_s"], q2, d["w2_s"],
+                              torch.from_numpy(w).cuda(), srt, tiles, nt, BM, layout=layout)
+        torch.cuda.synchronize()
+        got = out.float().cpu().numpy().astype(np.float64)
+        r_off, r_srt, r_tiles, r_n = oracle.build_tiles(ids, E, BM)
+        assert int(nt.item()) == r_n
+        np.testing.assert_array_equal(tiles[:r_n].cpu().numpy(), r_tiles)
+        np.testing.assert_array_equal(srt.cpu().numpy(), r_srt)
+        rows = r_tiles[:, 2]
+        assert set(((rows + 15) // 16).tolist()) == set(range(1, 9))
+        x64 = oracle.bf16_to_f64(inp["x"])
+        y = np.zeros((T * k, H))
+        for e in range(E):
+            slots = r_srt[r_off[e]:r_off[e + 1]].astype(np.int64)
+            y[slots] = oracle.expert_ffn(x64[slots // k], inp["w13_q"][e], inp["w13_s"][e],
+                                         inp["w2_q"][e], inp["w2_s"][e])
+        want = oracle.combine(y, w.astype(np.float64))
+        assert_out_close(got, want, f"matrix-core fragments ({layout})")
 
 
 @pytest.mark.parametrize("BM", [16, 32, 64, 128])
