@@ -281,11 +281,13 @@ moe_status moe_route_tiles(const uint16_t* x, const float* w_router, const float
  * own cost of a decode step ("Where the time went": "Launch and host gaps");
  * with one token, five dependent launches leave the GPU waiting between
  * steps.  Here the routing, gate/up and down workgroups share one grid: each
- * waits (by polling counters in the workspace) only for workgroups with a
- * lower index, the down weights stream while gate/up still runs, and the
- * last down workgroup of each 16-row block combines its k slots.  Every
- * output is bit-identical to moe_route_tiles + moe_forward with the same
- * arguments (BM any valid value: one token gives k one-row tiles).
+ * waits (by polling words in the workspace) only for workgroups with a
+ * lower index; up to 32 routing workgroups each compute the top-k from the
+ * published partial logits and publish the plan, so the GEMM workgroups
+ * learn their experts without a single serial tail; the last down
+ * workgroup of each 16-row block combines its k slots.  Every output is
+ * bit-identical to moe_route_tiles + moe_forward with the same arguments
+ * (BM any valid value: one token gives k one-row tiles).
  *
  *   arguments as for moe_route_tiles and moe_forward with T = 1 (layout
  *   included: it follows gating); logits may

@@ -7,46 +7,63 @@
 // own row of a decode step.  With one token each step is short, so the gaps
 // between dependent launches and the time each launch takes to fill the GPU
 // with workgroups are a large share of the layer.  Here one grid holds all
-// of it, every workgroup resident from the start:
+// of it:
 //   routing   splits x ceil(E/16) workgroups compute fp64 partial logits (as
-//             router_decode_fused does); the last of them sums them, runs
-//             the wave top-k and softmax, publishes the plan (expert and
-//             slot of each sorted position, weight of each slot), then
-//             writes the routing outputs and the tile table for the caller.
-//   GEMM      workgroup j runs gate/up job j (tile g = j / (I/16), 16-row
-//             block j % (I/16)) with exactly the arithmetic of the one-token
-//             gate/up kernel (expert_gemm_kernel<gate/up, 1, 1>), then the
-//             down job(s) of the tile t with (t+1) * I/16 <= j <
+//             router_decode_fused does) and publish them.  The first
+//             min(that, 32) of them, the publishers, then each read all the
+//             partials, sum them in split order and run the wave top-k, all
+//             in parallel and with identical results, and each publishes the
+//             plan (expert and slot of each sorted position) in a line of
+//             its own, then the routing weights; publisher 0 also writes the
+//             routing outputs and the tile table for the caller.
+//   GEMM      workgroup j polls the plan words it needs in replica
+//             j % publishers, then runs gate/up job j (tile g = j / (I/16),
+//             16-row block j % (I/16)) with exactly the arithmetic of the
+//             one-token gate/up kernel (expert_gemm_kernel<gate/up, 1, 1>),
+//             then the down job(s) of the tile t with (t+1) * I/16 <= j <
 //             (t+1) * I/16 + H/16 with exactly the arithmetic of the
 //             one-token down kernel.  The last tile's down job of each
 //             16-row block also combines the block's k slots in ascending
 //             slot order, as combine_kernel does.
 // Every value is therefore bit-identical to moe_route_tiles + moe_forward.
 //
-// Handshakes.  A workgroup only ever waits for data produced by workgroups
-// with a lower index (a tile's gate/up jobs sit below its down jobs, the
-// other tiles' down jobs below the combining one), and workgroups are
-// dispatched in index order, so no wait can deadlock however few
-// workgroups fit on the GPU at once.  Each value that crosses workgroups
-// (plan entries, routing weights, h pairs, y values) travels in one 64-bit
-// word together with a stamp, the call's epoch + 1, written and read with
-// agent-scope atomics (coherent across the XCDs' L2 caches); a consumer
-// polls the words it needs until their stamps match, so no producer waits
-// for its stores to complete and no counter sits on the critical path.
-// Each routing workgroup stamps a word once its partials are stored; the
-// last routing workgroup waits for the others' stamps.  The
-// epoch is read by every workgroup at its start and advanced by the last
-// of them to check in (a two-level arrival tree), so each call sees its own
-// value.  Only thread 0 of a workgroup reads the epoch; the others take it
-// from LDS after a barrier, so no wave can read an epoch that its own
-// workgroup's check-in already advanced.  Polls are bounded: one that gives
-// up sets the error word and its workgroup carries on with whatever it read
-// (the launch still ends).
+// Handshakes and why they are sound.
+//  * Progress.  A workgroup only ever waits for data produced by workgroups
+//    with a lower index (routing below GEMM, a tile's gate/up jobs below its
+//    down jobs, the other tiles' down jobs below the combining one), and the
+//    dispatcher starts workgroups in index order, so the lowest-index
+//    unfinished workgroup is always resident and never waits on anything
+//    unfinished: the waits cannot deadlock however few workgroups fit at
+//    once.  Every poll is also bounded (about a second); one that gives up
+//    sets the sticky error word and its workgroup carries on with whatever
+//    it read, so the launch ends even if the premise were broken.
+//  * Visibility.  Values that cross workgroups are written and read with
+//    agent-scope atomic stores and loads, which gfx950 serves from the
+//    memory side of its caches (coherent across the XCDs' L2s), and each
+//    value carries its own validity in the same 64-bit word: nothing relies
+//    on the order in which two different stores become visible, so no
+//    release/acquire fence (and no wait for a store to complete) is needed
+//    on the critical path.  Partial logits are stored as their bit pattern
+//    plus one in a buffer chosen by the call's parity, zero meaning "not yet
+//    written" (no fp64 value that the router arithmetic can produce has all
+//    bits set: NaNs that propagate from fp32 or bf16 inputs have their low
+//    29 bits clear); the routing workgroups clear the other parity's buffer
+//    for the next call.  h pairs and y values carry a stamp, the call's
+//    epoch + 1, in their upper half.
+//  * Epoch.  Thread 0 of each workgroup reads the epoch (in routing
+//    workgroups every thread does, and all of them wait for the load before
+//    the barrier that precedes the check-in); the others take it from LDS
+//    after a barrier.  The last workgroup to check in (a two-level arrival
+//    tree) advances it, so no workgroup of a call can see the next call's
+//    value.
 //
 // Contention.  Atomics and polls on one address are serialised by the
-// memory system, so hot words have their own 128-byte lines: the plan is
-// written to 16 replica lines (workgroup i reads replica i % 16) and the
-// arrival tree spreads its counters over 16 leaf lines and a top line.
+// memory system (tens of nanoseconds per access to one line), so no line is
+// read by many workgroups: the partials by the publishers only, each plan
+// replica by about (GEMM workgroups / publishers) threads, and the arrival
+// tree spreads its counters over 16 leaf lines and a top line.  (Every GEMM
+// workgroup reading all partials itself measured slower than the old single
+// tail: 900 workgroups polling the same 44 lines.)
 #include "expert_common.h"
 #include "moe_device.h"
 #include "moe_launch.h"
@@ -65,20 +82,15 @@ constexpr int kRegion0 = kActRegion > kRedBytes ? kActRegion : kRedBytes;
 
 typedef unsigned long long u64;
 
-// The sync region at the start of the workspace, in 128-byte lines (zero
-// before the first call; afterwards each call leaves it consistent).
+// The sync region at the start of the workspace, in 128-byte lines, then
+// the two parity buffers of published partial logits (zero before the first
+// call; afterwards each call leaves the region consistent for the next).
 constexpr int kLine = 32;      // ints per line
-constexpr int kReplicas = 16;  // plan replicas
 constexpr int kLeaves = 16;    // leaves of the arrival tree
 struct Tree {
   int leaf[kLeaves][kLine];
   int top[kLine];
 };
-struct ReplicaLine {
-  u64 plan[kMaxTopk];    // sorted position g: stamp | slot << 16 | expert
-  u64 weight[kMaxTopk];  // slot j: stamp | routing weight bits
-};
-constexpr int kMaxRoute = 32 * (kMaxExperts / 16);  // routing workgroups at most
 struct Sync {
   int reserved;
   int epoch;             // calls begun by every workgroup
@@ -86,11 +98,22 @@ struct Sync {
   int poll_limit;        // 0: kSpinLimit; n > 0: waits give up after n - 1 re-polls
   int pad0[kLine - 4];
   Tree arrivals;         // every workgroup, once it has read the epoch
-  ReplicaLine rep[kReplicas];
-  u64 routed[kMaxRoute]; // routing workgroup i: stamp once its partials are stored
 };
-static_assert(sizeof(ReplicaLine) == 128, "one line per replica");
 static_assert(sizeof(Sync) % 128 == 0, "whole lines");
+// K-ranges of the router at one token: router_plan keeps each >= 128
+// elements, and this kernel takes H <= kMaxK.
+constexpr int kMaxSplits = kMaxK / 128;
+// words per parity buffer: [split][expert] at a fixed stride, bit pattern
+// + 1 (0: not yet), so any shape finds its words where the last call of any
+// shape cleared them
+constexpr size_t kPartialWords = (size_t)kMaxSplits * kMaxExperts;
+// the plan as a publisher leaves it, one 128-byte line each
+constexpr int kMaxPublishers = 32;
+struct PlanLine {
+  u64 plan[kMaxTopk];    // sorted position g: stamp | slot << 16 | expert
+  u64 weight[kMaxTopk];  // slot j: stamp | routing weight bits
+};
+static_assert(sizeof(PlanLine) == 128, "one line per replica");
 
 __device__ __forceinline__ int ld_agent(const int* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -104,9 +127,11 @@ __device__ __forceinline__ int add_agent(int* p, int v) {
 __device__ __forceinline__ u64 ld64(const u64* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ void st64w(u64* p, u64 v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 __device__ __forceinline__ void st64(u64* p, unsigned stamp, unsigned payload) {
-  __hip_atomic_store(p, ((u64)stamp << 32) | payload, __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
+  st64w(p, ((u64)stamp << 32) | payload);
 }
 
 // Reads the N stamped words p[i] (those with use[i]) until every stamp is
@@ -134,6 +159,36 @@ __device__ __forceinline__ void settle(const u64* const (&p)[N], const bool (&us
     for (int i = 0; i < N; ++i)
       if ((unsigned)(v[i] >> 32) != stamp) v[i] = ld64(p[i]);
   }
+}
+
+// The partial logits of expert e, splits words at base + c * stride: read
+// until each is nonzero (published), every stale word re-requested at once
+// per round (all loads unconditional, surplus ones at a clamped address).
+// Returns the sum of the decoded values in split order.
+__device__ __forceinline__ double settle_partials(const u64* base, size_t stride, int splits,
+                                                  int* error, int spin_limit) {
+  u64 v[kMaxSplits];
+#pragma unroll
+  for (int c = 0; c < kMaxSplits; ++c) v[c] = ld64(base + (size_t)min(c, splits - 1) * stride);
+  for (int round = 0;; ++round) {
+    bool stale = false;
+#pragma unroll
+    for (int c = 0; c < kMaxSplits; ++c) stale |= v[c] == 0ull;
+    if (!stale) break;
+    if (round >= spin_limit) {
+      st_agent(error, 1);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(2);
+#pragma unroll
+    for (int c = 0; c < kMaxSplits; ++c)
+      if (v[c] == 0ull) v[c] = ld64(base + (size_t)min(c, splits - 1) * stride);
+  }
+  double sum = 0.0;
+#pragma unroll
+  for (int c = 0; c < kMaxSplits; ++c)
+    if (c < splits) sum += __longlong_as_double((long long)(v[c] - 1ull));
+  return sum;
 }
 
 // Arrival i of n at the tree (one thread).  True for exactly one arrival,
@@ -174,14 +229,15 @@ struct Args {
   int32_t* tiles;
   int32_t* num_tiles;
   Sync* sync;
-  double* partial;  // [splits][E]
+  u64* partials;    // [2][kPartialWords]: parity buffers of published partial logits
+  PlanLine* plans;  // [kMaxPublishers]
+  int n_pub;        // publishers: min(n_route, kMaxPublishers)
   u64* h;           // [k][I/2] stamped bf16 pairs
   u64* y;           // [k][H] stamped fp32
   uint16_t* out;
 };
 
-// This call's epoch and poll bound, as thread 0 read them (the caller
-// publishes them to the workgroup through LDS and a barrier).
+// This call's epoch and poll bound.
 struct CallState {
   int epoch;
   int spin_limit;
@@ -192,71 +248,106 @@ __device__ __forceinline__ CallState read_call_state(const Sync* S) {
   return CallState{epoch, pl > 0 ? pl - 1 : kSpinLimit};
 }
 
-// ---------------------------------------------------------------- routing
-__device__ void routing_role(const Args& a, int rid, unsigned char* lds, CallState* s_call) {
-  // thread 0's loads stay in flight while the partial logits are computed
-  CallState cs{0, 0};
-  if (threadIdx.x == 0) cs = read_call_state(a.sync);
-  const int eb = (a.E + kExpPerBlock - 1) / kExpPerBlock;
-  logits_partial_body<true, 1>(a.x, a.w_router, 1, a.H, a.E, a.split_len, a.partial, 0, rid % eb,
-                               rid / eb);
-  if (threadIdx.x == 0) *s_call = cs;
-  __builtin_amdgcn_s_waitcnt(0);  // this workgroup's partials are stored
+// LDS of a workgroup's own routing: logits, the rank scratch of the wave
+// top-k, and the selected experts and weights in slot order.
+struct RouteLds {
+  double logit[kMaxExperts];
+  long long scratch[kRankScratch];
+  int ids[kMaxTopk];
+  float w[kMaxTopk];
+};
+
+// The token's logits from the published partials, by the whole workgroup
+// (barriers inside): wave w sums the partials of experts w*64 + lane in
+// split order and adds the bias, exactly as one_token_logits does, into
+// r->logit; then wave 0 runs the wave top-k, as moe_route_tiles does, and
+// the selected ids end in r->ids (slot order).
+__device__ void route_ids(const Args& a, const CallState& cs, RouteLds* r) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int e = lane + kWave * wave;
+  const u64* cur = a.partials + (size_t)(cs.epoch & 1) * kPartialWords;
+  if (e < a.E) {
+    double sum = settle_partials(cur + e, (size_t)kMaxExperts, a.splits, &a.sync->error,
+                                 cs.spin_limit);
+    if (a.bias) sum += (double)a.bias[e];
+    r->logit[e] = sum;
+  }
   __syncthreads();
-  cs = *s_call;
-  const int epoch = cs.epoch, spin_limit = cs.spin_limit;
-  const unsigned stamp = (unsigned)epoch + 1u;
-  int* s_ids = reinterpret_cast<int*>(lds);
-  float* s_w = reinterpret_cast<float*>(s_ids + kMaxTopk);
-  if (threadIdx.x == 0) {
-    if (rid != a.n_route - 1) st64(&a.sync->routed[rid], stamp, 1u);
-    check_in(a.sync, epoch);
-  }
-  // the last routing workgroup finishes the token with one wave, once every
-  // other routing workgroup has stamped its word
-  if (rid != a.n_route - 1 || threadIdx.x >= kWave) return;
-  const int lane = threadIdx.x;
-  {
-    constexpr int kPer = kMaxRoute / kWave;
-    const u64* src[kPer];
-    bool use[kPer];
-    u64 v[kPer];
+  if (wave == 0) {
+    double val[4];
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int w = lane + i * kWave;
-      use[i] = w < a.n_route - 1;
-      src[i] = &a.sync->routed[min(w, kMaxRoute - 1)];
-    }
-    settle(src, use, v, stamp, &a.sync->error, spin_limit);
+    for (int i = 0; i < 4; ++i) val[i] = lane + kWave * i < a.E ? r->logit[lane + kWave * i] : 0.0;
+    topk_softmax_wave<false>(val, a.E, a.k, a.gating, 0, nullptr, nullptr, r->ids, nullptr,
+                             r->scratch);
   }
+  __syncthreads();
+}
+
+// The routing weights of the token (wave 0, after route_ids): the same wave
+// top-k and gating as moe_route_tiles, so the ids (r->ids) are the same and
+// the weights (r->w) identical.
+__device__ void route_weights(const Args& a, RouteLds* r) {
+  const int lane = threadIdx.x & 63;
   double val[4];
-  one_token_logits(a.partial, a.bias, a.E, a.splits, val);
-  // top-k and softmax into LDS only: the plan goes out first, the routing
-  // outputs for the caller (identical values) after it
-  topk_softmax_wave(val, a.E, a.k, a.gating, 0, nullptr, nullptr, s_ids, s_w,
-                    reinterpret_cast<long long*>(lds + 128));
-  wave_lds_sync();
-  // lane (r, j) writes slot j's entries of replica r, 8 replicas per pass
-  for (int r0 = 0; r0 < kReplicas; r0 += kWave / kMaxTopk) {
-    const int r = r0 + lane / kMaxTopk, j = lane % kMaxTopk;
-    if (j < a.k) {
-      const int e = s_ids[j];
-      int pos = 0;  // sorted position of slot j: selected experts below e
-      for (int q = 0; q < a.k; ++q) pos += s_ids[q] < e;
-      ReplicaLine* L = &a.sync->rep[r];
-      st64(&L->plan[pos], stamp, ((unsigned)j << 16) | (unsigned)e);
-      st64(&L->weight[j], stamp, __float_as_uint(s_w[j]));
-    }
-  }
-  if (a.logits)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (lane + kWave * i < a.E) a.logits[lane + kWave * i] = val[i];
+  for (int i = 0; i < 4; ++i) val[i] = lane + kWave * i < a.E ? r->logit[lane + kWave * i] : 0.0;
+  topk_softmax_wave<true>(val, a.E, a.k, a.gating, 0, nullptr, nullptr, r->ids, r->w,
+                          r->scratch);
+  wave_lds_sync();
+}
+
+// Publishes the plan of the ids in `ids` (slot order) into line L: the
+// sorted position of slot j is the number of selected experts below its
+// own (one wave; lanes < k store).
+__device__ void publish_plan(const Args& a, const int* ids, PlanLine* L, unsigned stamp) {
+  const int lane = threadIdx.x & 63;
   if (lane < a.k) {
-    a.topk_ids[lane] = s_ids[lane];
-    a.topk_weights[lane] = s_w[lane];
+    const int e = ids[lane];
+    int pos = 0;
+    for (int q = 0; q < a.k; ++q) pos += ids[q] < e;
+    st64(&L->plan[pos], stamp, ((unsigned)lane << 16) | (unsigned)e);
   }
-  one_token_tables(a.E, a.k, s_ids, a.expert_offsets, a.sorted_ids, a.tiles, a.num_tiles);
+}
+
+// ---------------------------------------------------------------- routing
+__device__ void routing_role(const Args& a, int rid, RouteLds* r) {
+  // every thread reads the epoch (it picks the parity buffer); all of those
+  // loads have returned before the barrier that precedes the check-in
+  const CallState cs = read_call_state(a.sync);
+  u64* cur = a.partials + (size_t)(cs.epoch & 1) * kPartialWords;
+  u64* nxt = a.partials + (size_t)((cs.epoch & 1) ^ 1) * kPartialWords;
+  const int eb = (a.E + kExpPerBlock - 1) / kExpPerBlock;
+  logits_partial_compute<1>(a.x, a.w_router, 1, a.H, a.E, a.split_len, 0, rid % eb, rid / eb,
+                            [&](int s, int, int e, double v) {
+                              st64w(cur + (size_t)s * kMaxExperts + e,
+                                    (u64)__double_as_longlong(v) + 1ull);
+                            });
+  // the next call's buffer starts empty whatever shape wrote it last
+  for (size_t i = (size_t)rid * kThreads + threadIdx.x; i < kPartialWords;
+       i += (size_t)a.n_route * kThreads)
+    st64w(nxt + i, 0ull);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 3 * kWave) check_in(a.sync, cs.epoch);
+  if (rid >= a.n_pub) return;
+  // a publisher: the ids first (the GEMM workgroups wait for them), then the
+  // weights (only the combining workgroups need them)
+  route_ids(a, cs, r);
+  if (threadIdx.x >= kWave) return;
+  const int lane = threadIdx.x;
+  const unsigned stamp = (unsigned)cs.epoch + 1u;
+  PlanLine* L = &a.plans[rid];
+  publish_plan(a, r->ids, L, stamp);
+  route_weights(a, r);
+  if (lane < a.k) st64(&L->weight[lane], stamp, __float_as_uint(r->w[lane]));
+  if (rid != 0) return;
+  if (a.logits)
+    for (int e = lane; e < a.E; e += kWave) a.logits[e] = r->logit[e];
+  if (lane < a.k) {
+    a.topk_ids[lane] = r->ids[lane];
+    a.topk_weights[lane] = r->w[lane];
+  }
+  one_token_tables(a.E, a.k, r->ids, a.expert_offsets, a.sorted_ids, a.tiles, a.num_tiles);
 }
 
 // ----------------------------------------------------------------- gate/up
@@ -269,13 +360,12 @@ struct GateupLoads {
   uint4 spiece;        // this thread's piece of the two scale runs
 };
 
-template <bool BLK>
-__device__ __forceinline__ void gateup_issue(const Args& a, int cb, int e, unsigned char* act,
-                                             GateupLoads& L) {
-  const int I = a.I, K = a.H, KB = K / 32;
+// The token's activation row into LDS (16-byte slots, the pad slot
+// repeating the last chunk).  It does not depend on the routing, so it is
+// requested at the workgroup's start.
+__device__ __forceinline__ void gateup_prefetch_act(const Args& a, unsigned char* act) {
+  const int K = a.H;
   const int tid = threadIdx.x, lane = tid & 63, kq = tid >> 6;
-  const int n_base = cb * kRowsPerBlock;
-  // activations (token 0) first, then the scale piece, then the weights
   const int cpr = K / 8, spr = cpr + 1;
   for (int ins = kq; ins < (spr + 63) / 64; ins += 4) {
     const int c = min(ins * 64 + lane, cpr - 1);
@@ -283,6 +373,14 @@ __device__ __forceinline__ void gateup_issue(const Args& a, int cb, int e, unsig
                                      (__attribute__((address_space(3))) void*)(act + ins * 1024),
                                      16, 0, 0);
   }
+}
+
+// The scale piece, then the weights (the activations are already requested).
+template <bool BLK>
+__device__ __forceinline__ void gateup_issue(const Args& a, int cb, int e, GateupLoads& L) {
+  const int I = a.I, K = a.H, KB = K / 32;
+  const int tid = threadIdx.x, lane = tid & 63, kq = tid >> 6;
+  const int n_base = cb * kRowsPerBlock;
   const int pr = min(tid / KB, 1), pp = tid - pr * KB;
   L.spiece = *reinterpret_cast<const uint4*>(
       a.w13_s + ((size_t)e * 2 * I + (size_t)pr * I + n_base) * KB + (size_t)min(pp, KB - 1) * 16);
@@ -408,7 +506,7 @@ __device__ __forceinline__ void down_issue(const Args& a, int cb, int e, DownLoa
 }
 
 __device__ __forceinline__ void down_finish(const Args& a, int g, int cb, int slot,
-                                            unsigned stamp, int spin_limit, const ReplicaLine* R,
+                                            unsigned stamp, int spin_limit, const PlanLine* R,
                                             unsigned char* lds, DownLoads& L) {
   const int H = a.H, I = a.I, K = I, KB = K / 32;
   const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, grp = lane >> 4;
@@ -470,8 +568,9 @@ __device__ __forceinline__ void down_finish(const Args& a, int g, int cb, int sl
     st64(a.y + (size_t)slot * H + n_base + tid, stamp, __float_as_uint(yv));
     return;
   }
-  // the last tile's job combines the block: the other slots' y as their
-  // stamped words arrive, then fma in ascending slot order
+  // the last tile's job combines the block: the routing weights and the
+  // other slots' y as their stamped words arrive, then fma in ascending slot
+  // order
   const u64* src[2 * kMaxTopk];
   bool use[2 * kMaxTopk];
   u64 v[2 * kMaxTopk];
@@ -506,21 +605,20 @@ __device__ __forceinline__ void down_finish(const Args& a, int g, int cb, int sl
 // the workgroup's gate/up job is done (requested together, the two streams
 // measured slower).
 template <bool BLK>
-__device__ void gemm_role(const Args& a, int j, unsigned char* lds, CallState* s_call) {
+__device__ void gemm_role(const Args& a, int j, unsigned char* lds, CallState* s_call,
+                          unsigned* s_plan) {
   const int ncbI = a.I / kRowsPerBlock, ncbH = a.H / kRowsPerBlock;
-  unsigned* s_plan = reinterpret_cast<unsigned*>(lds + kRegion0 + 2 * kScaleRunMax +
-                                                 2 * 2 * kRowsPerBlock * 256);
   const bool has_gu = j < a.k * ncbI;
   const int g_gu = min(j / ncbI, a.k - 1);
   int t0 = a.k;  // first tile with a down job here
   for (int t = a.k - 1; t >= 0; --t)
     if (j >= (t + 1) * ncbI && j < (t + 1) * ncbI + ncbH) t0 = t;
 
-  const ReplicaLine* R = &a.sync->rep[blockIdx.x % kReplicas];
+  if (has_gu) gateup_prefetch_act(a, lds);
+  const PlanLine* R = &a.plans[blockIdx.x % a.n_pub];
   if (threadIdx.x == 0) {
     const CallState cs = read_call_state(a.sync);
     *s_call = cs;
-    check_in(a.sync, cs.epoch);
     const u64* src[2] = {&R->plan[g_gu], &R->plan[min(t0, a.k - 1)]};
     const bool use[2] = {true, true};
     u64 v[2];
@@ -539,9 +637,11 @@ __device__ void gemm_role(const Args& a, int j, unsigned char* lds, CallState* s
 
   if (has_gu) {
     GateupLoads gl;
-    gateup_issue<BLK>(a, j - g_gu * ncbI, expert(p_gu), lds, gl);
+    gateup_issue<BLK>(a, j - g_gu * ncbI, expert(p_gu), gl);
     gateup_finish<BLK>(a, g_gu, j - g_gu * ncbI, stamp, lds, gl);
   }
+  // the check-in's atomics wait on wave 3 where it has nothing else to do
+  if (threadIdx.x == 3 * kWave) check_in(a.sync, cs.epoch);
   for (int t = t0; t < a.k; ++t) {
     const int cb = j - (t + 1) * ncbI;
     if (cb < 0 || cb >= ncbH) continue;
@@ -563,7 +663,9 @@ __device__ void gemm_role(const Args& a, int j, unsigned char* lds, CallState* s
       // its tile's h has begun to arrive (one word, a different one per
       // workgroup), so they do not compete with the gate/up stream at its
       // start; they still land before the tile's h is complete (0.1 us per
-      // call faster at 20b)
+      // call faster at 20b; requesting every down job's weights together with
+      // the gate/up ones, straight into LDS, measured 2.3 us slower: the
+      // mixed stream ran at 4.4 TB/s instead of 5.3)
       if (threadIdx.x == 0) {
         const u64* src[1] = {a.h + (size_t)t * a.I / 2 + (size_t)(cb % (a.I / 32)) * 16};
         const bool use[1] = {true};
@@ -578,16 +680,25 @@ __device__ void gemm_role(const Args& a, int j, unsigned char* lds, CallState* s
   }
 }
 
-constexpr int kLdsBytes = kRegion0 + 2 * kScaleRunMax + 2 * 2 * kRowsPerBlock * 256 + 16;
+template <bool BLK>
+constexpr int lds_bytes() {
+  // GEMM workgroups: region 0 (x row / split-K table / h row), two scale
+  // runs (the down job's reduction table sits in the second), the canonical
+  // layout's exchange ring.  Routing workgroups use the start of the same
+  // space for their RouteLds.
+  return kRegion0 + 2 * kScaleRunMax + (BLK ? 0 : 2 * 2 * kRowsPerBlock * 256) + 16;
+}
+static_assert(sizeof(RouteLds) <= lds_bytes<true>(), "routing scratch fits");
 
 template <bool BLK>
 __global__ __launch_bounds__(kThreads, 4) void moe_layer_one_token_kernel(Args a) {
-  __shared__ __align__(16) unsigned char lds[kLdsBytes];
+  __shared__ __align__(16) unsigned char lds[lds_bytes<BLK>()];
   __shared__ CallState s_call;
+  __shared__ unsigned s_plan[4];
   if ((int)blockIdx.x < a.n_route)
-    routing_role(a, blockIdx.x, lds, &s_call);
+    routing_role(a, blockIdx.x, reinterpret_cast<RouteLds*>(lds));
   else
-    gemm_role<BLK>(a, blockIdx.x - a.n_route, lds, &s_call);
+    gemm_role<BLK>(a, blockIdx.x - a.n_route, lds, &s_call, s_plan);
 }
 
 size_t round_up(size_t n) { return (n + 255) / 256 * 256; }
@@ -599,18 +710,19 @@ bool layer_one_token_ok(int H, int I, int E, int k) {
         E <= kMaxExperts && k >= 1 && k <= kMaxTopk && k <= E))
     return false;
   const RouterPlan p = router_plan(1, H, E);
-  return p.splits * ((E + kExpPerBlock - 1) / kExpPerBlock) <= kMaxRoute;
+  return p.splits <= kMaxSplits;
 }
 
 size_t layer_one_token_sync_bytes(int H) {
   (void)H;
-  return round_up(sizeof(Sync));
+  return round_up(sizeof(Sync)) + 2 * kPartialWords * sizeof(u64) +
+         kMaxPublishers * sizeof(PlanLine);
 }
 
 size_t layer_one_token_bytes(int H, int I, int E, int k) {
-  const RouterPlan p = router_plan(1, H, E);
-  return layer_one_token_sync_bytes(H) + round_up((size_t)p.splits * E * sizeof(double)) +
-         round_up((size_t)k * (I / 2) * sizeof(u64)) + round_up((size_t)k * H * sizeof(u64));
+  (void)E;
+  return layer_one_token_sync_bytes(H) + round_up((size_t)k * (I / 2) * sizeof(u64)) +
+         round_up((size_t)k * H * sizeof(u64));
 }
 
 void launch_layer_one_token(const uint16_t* x, const float* w_router, const float* bias,
@@ -633,9 +745,11 @@ void launch_layer_one_token(const uint16_t* x, const float* w_router, const floa
   a.expert_offsets = expert_offsets; a.sorted_ids = sorted_ids; a.tiles = tiles;
   a.num_tiles = num_tiles;
   a.sync = reinterpret_cast<Sync*>(ws);
+  a.partials = reinterpret_cast<u64*>(ws + round_up(sizeof(Sync)));
+  a.plans = reinterpret_cast<PlanLine*>(ws + round_up(sizeof(Sync)) +
+                                        2 * kPartialWords * sizeof(u64));
+  a.n_pub = a.n_route < kMaxPublishers ? a.n_route : kMaxPublishers;
   size_t off = layer_one_token_sync_bytes(H);
-  a.partial = reinterpret_cast<double*>(ws + off);
-  off += round_up((size_t)p.splits * E * sizeof(double));
   a.h = reinterpret_cast<u64*>(ws + off);
   off += round_up((size_t)k * (I / 2) * sizeof(u64));
   a.y = reinterpret_cast<u64*>(ws + off);

@@ -26,13 +26,12 @@ __device__ __forceinline__ double dpp_f64(double v) {
 }
 
 // One workgroup's share of the partial logits: tokens [TPW*bx, +TPW), experts
-// [16*by, +16) (4 per wave), K-range bz.  ATOMIC_OUT stores with agent-scope
-// atomics so another workgroup of the same launch may read them.
-template <bool ATOMIC_OUT, int TPW = kTokPerWave>
-__device__ void logits_partial_body(const uint16_t* __restrict__ x,
-                                    const float* __restrict__ w_router, int T, int H, int E,
-                                    int split_len, double* __restrict__ partial, int bx, int by,
-                                    int bz) {
+// [16*by, +16) (4 per wave), K-range bz.  Each finished value is handed to
+// store(split, token, expert, value), called by one lane per value.
+template <int TPW, typename Store>
+__device__ void logits_partial_compute(const uint16_t* __restrict__ x,
+                                       const float* __restrict__ w_router, int T, int H, int E,
+                                       int split_len, int bx, int by, int bz, Store store) {
   const int wave = (threadIdx.x >> 6) & 3;  // wave within this 256-thread expert block
   const int lane = threadIdx.x & 63;
   const int t0 = bx * TPW;
@@ -120,13 +119,27 @@ __device__ void logits_partial_body(const uint16_t* __restrict__ x,
   v[0] += dpp_f64<0xB1>(v[0]);                            // quad_perm [1,0,3,2]
   const int idx = lane >> (6 - LOGN);  // the value this lane holds
   const int t = idx / kExpPerWave, e = idx % kExpPerWave;
-  if ((lane & ((64 >> LOGN) - 1)) == 0 && t0 + t < T && e0 + e < E) {
-    double* dst = &partial[((size_t)s * T + (t0 + t)) * E + (e0 + e)];
-    if (ATOMIC_OUT)
-      __hip_atomic_store(dst, v[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    else
-      *dst = v[0];
-  }
+  if ((lane & ((64 >> LOGN) - 1)) == 0 && t0 + t < T && e0 + e < E)
+    store(s, t0 + t, e0 + e, v[0]);
+}
+
+// logits_partial_compute into partial[split][token][expert].  ATOMIC_OUT
+// stores with agent-scope atomics so another workgroup of the same launch
+// may read them.
+template <bool ATOMIC_OUT, int TPW = kTokPerWave>
+__device__ void logits_partial_body(const uint16_t* __restrict__ x,
+                                    const float* __restrict__ w_router, int T, int H, int E,
+                                    int split_len, double* __restrict__ partial, int bx, int by,
+                                    int bz) {
+  logits_partial_compute<TPW>(x, w_router, T, H, E, split_len, bx, by, bz,
+                              [&](int s, int t, int e, double v) {
+                                double* dst = &partial[((size_t)s * T + t) * E + e];
+                                if (ATOMIC_OUT)
+                                  __hip_atomic_store(dst, v, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+                                else
+                                  *dst = v;
+                              });
 }
 
 // Total order on doubles as int64 (larger key = larger value); -0 is folded
@@ -224,6 +237,7 @@ __device__ __forceinline__ void wave_lds_order() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+template <bool WEIGHTS = true>
 __device__ void topk_softmax_rank(double v0, int E, int k, int gating, int t,
                                   int32_t* __restrict__ topk_ids,
                                   float* __restrict__ topk_weights, int* ids_lds, float* w_lds,
@@ -256,6 +270,14 @@ __device__ void topk_softmax_rank(double v0, int E, int k, int gating, int t,
     s_v[rank] = v0;
   }
   wave_lds_order();
+  if constexpr (!WEIGHTS) {  // the selection only: ids in slot order
+    if (lane < k) {
+      const int el = (int)s_e[lane];
+      if (topk_ids) topk_ids[(size_t)t * k + lane] = el;
+      if (ids_lds) ids_lds[t * k + lane] = el;
+    }
+    return;
+  }
   double m = s_v[0];
 #pragma unroll
   for (int j = 1; j < kMaxTopk; ++j)
@@ -277,12 +299,16 @@ __device__ void topk_softmax_rank(double v0, int E, int k, int gating, int t,
   }
 }
 
+// With WEIGHTS false only the selection is made (ids_lds / topk_ids, the
+// same ids in the same slot order); the gating is skipped.
+template <bool WEIGHTS = true>
 __device__ void topk_softmax_wave(const double (&val)[4], int E, int k, int gating, int t,
                                   int32_t* __restrict__ topk_ids,
                                   float* __restrict__ topk_weights, int* ids_lds,
                                   float* w_lds = nullptr, long long* scratch = nullptr) {
   if (scratch && E <= kWave) {  // uniform
-    topk_softmax_rank(val[0], E, k, gating, t, topk_ids, topk_weights, ids_lds, w_lds, scratch);
+    topk_softmax_rank<WEIGHTS>(val[0], E, k, gating, t, topk_ids, topk_weights, ids_lds, w_lds,
+                               scratch);
     return;
   }
   const int lane = threadIdx.x & 63;
@@ -322,6 +348,17 @@ __device__ void topk_softmax_wave(const double (&val)[4], int E, int k, int gati
       if (i == slot && lane == src) key[i] = LLONG_MIN;
   }
 
+  if constexpr (!WEIGHTS) {
+    int el = sel_e[0];
+#pragma unroll
+    for (int j = 1; j < kMaxTopk; ++j)
+      if (lane == j) el = sel_e[j];
+    if (lane < k) {
+      if (topk_ids) topk_ids[(size_t)t * k + lane] = el;
+      if (ids_lds) ids_lds[t * k + lane] = el;
+    }
+    return;
+  }
   double m = sel_v[0];
 #pragma unroll
   for (int j = 1; j < kMaxTopk; ++j)
@@ -351,7 +388,7 @@ constexpr int kFusedMaxSplits = 32;
 // The logits of a single token, lane l holding experts l, l+64, ...: the
 // K-range partials (agent-scope atomic loads, all in flight at once) summed
 // in order plus the bias, as router_topk_softmax sums them.
-__device__ void one_token_logits(const double* __restrict__ partial,
+[[maybe_unused]] __device__ void one_token_logits(const double* __restrict__ partial,
                                  const float* __restrict__ bias, int E, int splits,
                                  double (&val)[4]) {
   const int lane = threadIdx.x & 63;
@@ -411,7 +448,7 @@ __device__ void one_token_tables(int E, int k, const int* s_ids,
 // experts below its own, every selected expert gets one tile of one row, and
 // build_tiles_small would produce exactly this table.  The selected ids go
 // to s_ids (LDS) and, if s_w is given, their weights to s_w.
-__device__ void tail_one_token(const double (&val)[4], int E, int k, int gating,
+[[maybe_unused]] __device__ void tail_one_token(const double (&val)[4], int E, int k, int gating,
                                int32_t* __restrict__ topk_ids,
                                float* __restrict__ topk_weights, double* __restrict__ logits,
                                int* s_ids, int32_t* __restrict__ expert_offsets,
