@@ -249,6 +249,33 @@ moe_status moe_forward(const uint16_t* x,
                        void* workspace, size_t workspace_bytes,
                        uint16_t* out, struct ihipStream_t* stream);
 
+/* ------------------------------------------ moe_forward_static_workspace
+ * moe_forward for callers that cannot allocate device memory: code being
+ * captured into a HIP graph, tight serving loops, harnesses that forbid
+ * hipMalloc.  The h and y intermediates live in a workspace the library
+ * holds itself, a device array of MOE_STATIC_WORKSPACE_BYTES bytes on each
+ * GPU it runs on (created with the library's code object and kept until the
+ * process ends); the call allocates nothing and frees nothing.
+ *
+ *   arguments as for moe_forward, without workspace and workspace_bytes
+ *   MOE_ERR_WORKSPACE when moe_forward_workspace_bytes(T, H, I, k) exceeds
+ *   MOE_STATIC_WORKSPACE_BYTES (about 970 slots of 2880 x 2880: T <= 242 at
+ *   k = 4), checked on the host before anything is enqueued.
+ * Every call on one GPU uses that GPU's one array: the array is fully
+ * written before it is read within a call (nothing in it needs to start at
+ * zero), and calls in one process on one GPU that overlap in time (on
+ * different streams or host threads) race and give unspecified outputs.
+ * Results are bit-identical to moe_forward. */
+#define MOE_STATIC_WORKSPACE_BYTES (16u << 20)
+
+moe_status moe_forward_static_workspace(const uint16_t* x,
+                                        const uint8_t* w13_q, const uint8_t* w13_s,
+                                        const uint8_t* w2_q, const uint8_t* w2_s,
+                                        const float* topk_weights, const int32_t* sorted_ids,
+                                        const int32_t* tiles, const int32_t* num_tiles,
+                                        int T, int H, int I, int E, int k, int BM, int layout,
+                                        uint16_t* out, struct ihipStream_t* stream);
+
 /* ------------------------------------------------------- moe_route_tiles
  * moe_route followed by moe_build_tiles in a single launch, for decode-sized
  * batches (T <= 16; otherwise MOE_ERR_SHAPE).  The

@@ -78,6 +78,9 @@ def load() -> ctypes.CDLL:
     lib.moe_layer_one_token.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i,
                                         _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p, _p]
     lib.moe_layer_one_token.restype = _i
+    lib.moe_forward_static_workspace.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _p,
+                                                 _i, _i, _i, _i, _i, _i, _i, _p, _p]
+    lib.moe_forward_static_workspace.restype = _i
     lib.moe_repack_weights.argtypes = [_p, ctypes.c_int64, _i, _p, _p]
     lib.moe_repack_weights.restype = _i
     _lib = lib
@@ -363,6 +366,44 @@ def moe_forward(x: torch.Tensor, w13_q: torch.Tensor, w13_s: torch.Tensor, w2_q:
                               T, H, I, E, k, BM, layout_code(layout), _ptr(workspace),
                               workspace.numel(), _ptr(out),
                               _stream(dev)), "moe_forward")
+    return out
+
+
+STATIC_WORKSPACE_BYTES = 16 << 20  # MOE_STATIC_WORKSPACE_BYTES
+
+
+def moe_forward_static_workspace(x: torch.Tensor, w13_q: torch.Tensor, w13_s: torch.Tensor,
+                                 w2_q: torch.Tensor, w2_s: torch.Tensor,
+                                 topk_weights: torch.Tensor, sorted_ids: torch.Tensor,
+                                 tiles: torch.Tensor, num_tiles: torch.Tensor, BM: int,
+                                 out: torch.Tensor, layout: str = "canonical") -> torch.Tensor:
+    """moe_forward with the library's own per-device workspace: allocates
+    nothing (out must be given).  Returns out."""
+    _need(x, "x", _BF16)
+    dev = x.device
+    for name, t in (("w13_q", w13_q), ("w13_s", w13_s), ("w2_q", w2_q), ("w2_s", w2_s)):
+        _need(t, name, _U8, dev)
+    _need(topk_weights, "topk_weights", (torch.float32,), dev)
+    _need(sorted_ids, "sorted_ids", (torch.int32,), dev)
+    _need(tiles, "tiles", (torch.int32,), dev)
+    _need(num_tiles, "num_tiles", (torch.int32,), dev)
+    _need(out, "out", _BF16, dev)
+    T, H = x.shape
+    E, I2, Hh = w13_q.shape
+    I = I2 // 2
+    k = topk_weights.shape[1]
+    if (Hh * 2 != H or tuple(w13_s.shape) != (E, 2 * I, H // 32)
+            or tuple(w2_q.shape) != (E, H, I // 2) or tuple(w2_s.shape) != (E, H, I // 32)):
+        raise ValueError("weight shapes do not match x")
+    if topk_weights.shape[0] != T or sorted_ids.numel() != T * k or tuple(out.shape) != (T, H):
+        raise ValueError("routing tensors or out do not match x")
+    if tiles.shape[0] < tiles_max(T, k, E, BM):
+        raise ValueError("tiles has fewer rows than moe_tiles_max")
+    _check(load().moe_forward_static_workspace(_ptr(x), _ptr(w13_q), _ptr(w13_s), _ptr(w2_q),
+                                               _ptr(w2_s), _ptr(topk_weights), _ptr(sorted_ids),
+                                               _ptr(tiles), _ptr(num_tiles), T, H, I, E, k, BM,
+                                               layout_code(layout), _ptr(out), _stream(dev)),
+           "moe_forward_static_workspace")
     return out
 
 

@@ -7,6 +7,7 @@
 
 #include <atomic>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/moe_mxfp4.h"
 #include "moe_launch.h"
@@ -244,28 +245,39 @@ moe_status moe_combine(const float* y, const float* topk_weights, int T, int H, 
   return finish_launches();
 }
 
-moe_status moe_forward(const uint16_t* x, const uint8_t* w13_q, const uint8_t* w13_s,
-                       const uint8_t* w2_q, const uint8_t* w2_s, const float* topk_weights,
-                       const int32_t* sorted_ids, const int32_t* tiles, const int32_t* num_tiles,
-                       int T, int H, int I, int E, int k, int BM, int layout, void* workspace,
-                       size_t workspace_bytes, uint16_t* out, struct ihipStream_t* stream) {
+}  // extern "C"
+
+namespace {
+
+// Host validation shared by moe_forward and moe_forward_static_workspace
+// (everything but the workspace).
+moe_status forward_validate(const uint16_t* x, const uint8_t* w13_q, const uint8_t* w13_s,
+                            const uint8_t* w2_q, const uint8_t* w2_s, const float* topk_weights,
+                            const int32_t* sorted_ids, const int32_t* tiles,
+                            const int32_t* num_tiles, int T, int H, int I, int E, int k, int BM,
+                            int layout, const uint16_t* out) {
   if (!forward_shape_ok(T, H, I, E, k, BM) || !layout_ok(layout)) return MOE_ERR_SHAPE;
   if (T == 0) return MOE_OK;
   if (!x || !w13_q || !w13_s || !w2_q || !w2_s || !topk_weights || !sorted_ids || !tiles ||
-      !num_tiles || !workspace || !out)
+      !num_tiles || !out)
     return MOE_ERR_NULL;
   if (!aligned16(x) || !aligned16(w13_q) || !aligned16(w13_s) || !aligned16(w2_q) ||
-      !aligned16(w2_s) || !aligned16(workspace))
+      !aligned16(w2_s))
     return MOE_ERR_ALIGN;
-  if (workspace_bytes < moe_forward_workspace_bytes(T, H, I, k)) return MOE_ERR_WORKSPACE;
-  moe_status st = check_device();
-  if (st != MOE_OK) return st;
-  (void)hipGetLastError();
+  return MOE_OK;
+}
+
+// moe_forward's launches once every argument is valid; h and y are carved
+// from `workspace` (moe_forward_workspace_bytes of it).
+moe_status forward_launch(const uint16_t* x, const uint8_t* w13_q, const uint8_t* w13_s,
+                          const uint8_t* w2_q, const uint8_t* w2_s, const float* topk_weights,
+                          const int32_t* sorted_ids, const int32_t* tiles,
+                          const int32_t* num_tiles, int T, int H, int I, int E, int k, int BM,
+                          int layout, void* workspace, uint16_t* out, hipStream_t s) {
   const int64_t tmax = moe_tiles_max(T, k, E, BM);
   const size_t nslots = (size_t)T * (size_t)k;
   uint16_t* h = static_cast<uint16_t*>(workspace);
   float* y = reinterpret_cast<float*>(static_cast<char*>(workspace) + round256(nslots * I * 2));
-  hipStream_t s = as_stream(stream);
   const bool blocked = layout == MOE_LAYOUT_BLOCKED;
   moe::launch_gateup_swiglu(x, w13_q, w13_s, sorted_ids, tiles, num_tiles, (int)tmax, T, H, I, E,
                             k, BM, blocked, h, s);
@@ -279,6 +291,81 @@ moe_status moe_forward(const uint16_t* x, const uint8_t* w13_q, const uint8_t* w
                    blocked, y, s);
   moe::launch_combine(y, topk_weights, T, H, k, out, s);
   return finish_launches();
+}
+
+// The workspace of moe_forward_static_workspace: one copy per device, held
+// until the process ends.  Host code never names `scratch` where it needs
+// the memory (the name is a host-side stand-in there): it uses the device
+// address hipGetSymbolAddress returns, looked up once per device with that
+// device current.
+__device__ __align__(256) unsigned char scratch[MOE_STATIC_WORKSPACE_BYTES];
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+moe_status scratch_address(void** addr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return MOE_ERR_DEVICE;
+  }
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+        (void)hipGetLastError();
+        return MOE_ERR_DEVICE;
+      }
+      g_scratch_addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *addr = p;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_forward(const uint16_t* x, const uint8_t* w13_q, const uint8_t* w13_s,
+                       const uint8_t* w2_q, const uint8_t* w2_s, const float* topk_weights,
+                       const int32_t* sorted_ids, const int32_t* tiles, const int32_t* num_tiles,
+                       int T, int H, int I, int E, int k, int BM, int layout, void* workspace,
+                       size_t workspace_bytes, uint16_t* out, struct ihipStream_t* stream) {
+  moe_status st = forward_validate(x, w13_q, w13_s, w2_q, w2_s, topk_weights, sorted_ids, tiles,
+                                   num_tiles, T, H, I, E, k, BM, layout, out);
+  if (st != MOE_OK || T == 0) return st;
+  if (!workspace) return MOE_ERR_NULL;
+  if (!aligned16(workspace)) return MOE_ERR_ALIGN;
+  if (workspace_bytes < moe_forward_workspace_bytes(T, H, I, k)) return MOE_ERR_WORKSPACE;
+  st = check_device();
+  if (st != MOE_OK) return st;
+  (void)hipGetLastError();
+  return forward_launch(x, w13_q, w13_s, w2_q, w2_s, topk_weights, sorted_ids, tiles, num_tiles,
+                        T, H, I, E, k, BM, layout, workspace, out, as_stream(stream));
+}
+
+moe_status moe_forward_static_workspace(const uint16_t* x, const uint8_t* w13_q,
+                                        const uint8_t* w13_s, const uint8_t* w2_q,
+                                        const uint8_t* w2_s, const float* topk_weights,
+                                        const int32_t* sorted_ids, const int32_t* tiles,
+                                        const int32_t* num_tiles, int T, int H, int I, int E,
+                                        int k, int BM, int layout, uint16_t* out,
+                                        struct ihipStream_t* stream) {
+  moe_status st = forward_validate(x, w13_q, w13_s, w2_q, w2_s, topk_weights, sorted_ids, tiles,
+                                   num_tiles, T, H, I, E, k, BM, layout, out);
+  if (st != MOE_OK || T == 0) return st;
+  if (moe_forward_workspace_bytes(T, H, I, k) > (size_t)MOE_STATIC_WORKSPACE_BYTES)
+    return MOE_ERR_WORKSPACE;
+  st = check_device();
+  if (st != MOE_OK) return st;
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != MOE_OK) return st;
+  (void)hipGetLastError();
+  return forward_launch(x, w13_q, w13_s, w2_q, w2_s, topk_weights, sorted_ids, tiles, num_tiles,
+                        T, H, I, E, k, BM, layout, ws, out, as_stream(stream));
 }
 
 size_t moe_layer_one_token_workspace_bytes(int H, int I, int E, int k) {

@@ -130,6 +130,36 @@ def test_forward_validation(kw, want):
     assert _forward(**kw) == want
 
 
+def _forward_static(**kw):
+    a = dict(x=P, q13=P, s13=P, q2=P, s2=P, wts=P, srt=P, tiles=P, nt=P, T=4, H=256, I=512, E=8,
+             k=2, BM=16, layout=0, out=P)
+    a.update(kw)
+    return B.load().moe_forward_static_workspace(
+        a["x"], a["q13"], a["s13"], a["q2"], a["s2"], a["wts"], a["srt"], a["tiles"], a["nt"],
+        a["T"], a["H"], a["I"], a["E"], a["k"], a["BM"], a["layout"], a["out"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(x=None), NULL), (dict(q13=None), NULL), (dict(out=None), NULL), (dict(nt=None), NULL),
+    (dict(H=100), SHAPE), (dict(BM=24), SHAPE), (dict(layout=2), SHAPE), (dict(s2=PMIS), ALIGN),
+    (dict(T=0, x=None), OK),
+    # h bf16 + y fp32 of every slot must fit the library's 16 MiB array:
+    # 970 slots of 2880 x 2880 fit, 971 do not
+    (dict(T=971, k=1, E=1, H=2880, I=2880, BM=128), WORKSPACE),
+    (dict(T=4096, k=4, E=128, H=2880, I=2880, BM=128), WORKSPACE),
+])
+def test_forward_static_workspace_validation(kw, want):
+    assert _forward_static(**kw) == want
+
+
+def test_static_workspace_limit_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define MOE_STATIC_WORKSPACE_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == moe.STATIC_WORKSPACE_BYTES
+    assert moe.forward_workspace_bytes(970, 2880, 2880, 1) <= moe.STATIC_WORKSPACE_BYTES
+    assert moe.forward_workspace_bytes(971, 2880, 2880, 1) > moe.STATIC_WORKSPACE_BYTES
+
+
 def _route_tiles(**kw):
     a = dict(x=P, w=P, bias=None, T=4, H=256, E=8, k=2, gating=0, BM=16, ids=P, wts=P,
              logits=None, off=P, srt=P, tiles=P, nt=P, ws=P, wsb=1 << 20)
