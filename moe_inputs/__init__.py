@@ -130,6 +130,28 @@ def make_random(T: int, H: int, E: int, k: int, I: int, seed: int,
     return out
 
 
+def with_gptoss_experts(inp: dict, seed: int, bias_std: float = 0.5) -> dict:
+    """The same layer read in the gpt-oss expert form (w13 rows taken as
+    interleaved gate/up pairs) with expert biases: b13 fp32 [E, 2I] (in the
+    interleaved row order) and b2 fp32 [E, H], drawn N(0, bias_std) and
+    rounded to bf16 values (the released checkpoints store bf16 biases),
+    alpha 1.702 and limit 7.0.  Drawn from ``default_rng([seed, 3])``."""
+    E, H, I = inp["w13_q"].shape[0], inp["H"], inp["I"]
+    rng = np.random.default_rng([seed, 3])
+    b13 = _bf16_values(rng.normal(0.0, bias_std, size=(E, 2 * I)))
+    b2 = _bf16_values(rng.normal(0.0, bias_std, size=(E, H)))
+    out = dict(inp)
+    out.update(activation="gptoss", b13=b13, b2=b2, alpha=1.702, limit=7.0,
+               name=inp.get("name", "?") + "_gptoss")
+    return out
+
+
+def _bf16_values(a: np.ndarray) -> np.ndarray:
+    """float32 array of the bf16 values nearest to a (RNE)."""
+    bits = f64_to_bf16_bits(a).astype(np.uint32) << 16
+    return bits.view(np.float32).reshape(a.shape)
+
+
 def identical_experts(inp: dict) -> dict:
     """Copy expert 0's packed weights into every expert (same bytes everywhere)."""
     out = dict(inp)
@@ -140,4 +162,5 @@ def identical_experts(inp: dict) -> dict:
 
 
 __all__ = ["Workload", "WORKLOADS", "f64_to_bf16_bits", "make_weights",
-           "make_activations", "make_workload", "make_random", "identical_experts"]
+           "make_activations", "make_workload", "make_random", "identical_experts",
+           "with_gptoss_experts"]

@@ -44,6 +44,15 @@ section "Correctness"):
   * Two codes per byte, the even element in the low nibble.
   * w13 rows [0, I) are the gate projection, rows [I, 2I) the up projection.
   * The router bias, when present, is added before both top-k and softmax.
+  * The gpt-oss expert form (an opt-in variant, not on the pages, which only
+    say that the official MXFP4 checkpoints are loaded unchanged): w13 rows
+    interleaved (row 2i the gate projection of output i, row 2i + 1 its up
+    projection), a bias on each w13 row and on each w2 row, and a clamped
+    SwiGLU, h = min(g, limit) * sigmoid(alpha * min(g, limit)) *
+    (clip(u, -limit, limit) + 1), with alpha = 1.702 and limit = 7 for the
+    released models.  This is the published model's own definition, taken
+    as given; nothing on the pages confirms it, so parity against a real
+    checkpoint is unpinned.
   * Sigmoid gating: the pages name it (the README's router; the DeepSeek-V3
     report cited there) but give no formula.  Read here as: experts chosen
     by the same top-k of the logits (sigmoid is increasing, so this is the
@@ -231,6 +240,46 @@ def expert_ffn(X: np.ndarray, w13_q_e, w13_s_e, w2_q_e, w2_s_e) -> np.ndarray:
     return h @ W2.T
 
 
+# ---------------------------------------- gpt-oss expert form (opt-in) --
+
+GPTOSS_ALPHA = 1.702
+GPTOSS_LIMIT = 7.0
+
+
+def concatenated_from_interleaved(a: np.ndarray, axis: int) -> np.ndarray:
+    """Rows interleaved along `axis` (entry 2i: gate of output i, 2i + 1: its
+    up) -> gate entries first, then up entries: out[i] = a[2i],
+    out[I + i] = a[2i + 1] along that axis."""
+    a = np.asarray(a)
+    n = a.shape[axis]
+    if n % 2:
+        raise ValueError("need an even extent along axis")
+    gate = np.take(a, np.arange(0, n, 2), axis=axis)
+    up = np.take(a, np.arange(1, n, 2), axis=axis)
+    return np.ascontiguousarray(np.concatenate([gate, up], axis=axis))
+
+
+def swiglu_clamped(g: np.ndarray, u: np.ndarray, alpha: float, limit: float) -> np.ndarray:
+    """gpt-oss SwiGLU: the gate clamped from above, the up projection on both
+    sides, h = g * sigmoid(alpha * g) * (u + 1)."""
+    g = np.minimum(g, limit)
+    u = np.clip(u, -limit, limit)
+    with np.errstate(over="ignore"):
+        return g / (1.0 + np.exp(-alpha * g)) * (u + 1.0)
+
+
+def expert_ffn_gptoss(X: np.ndarray, w13_q_e, w13_s_e, w2_q_e, w2_s_e, b13_e, b2_e,
+                      alpha: float = GPTOSS_ALPHA, limit: float = GPTOSS_LIMIT) -> np.ndarray:
+    """Steps 5-6 for one expert in the gpt-oss form: w13 rows interleaved
+    (gate = even rows, up = odd rows), b13_e [2I] in the same order, b2_e [H];
+    X float64 [M, H] -> y float64 [M, H]."""
+    W13 = dequant_mxfp4(w13_q_e, w13_s_e)            # [2I, H], interleaved rows
+    z = X @ W13.T + np.asarray(b13_e, dtype=np.float64)[None, :]
+    h = swiglu_clamped(z[:, 0::2], z[:, 1::2], alpha, limit)
+    W2 = dequant_mxfp4(w2_q_e, w2_s_e)               # [H, I]
+    return h @ W2.T + np.asarray(b2_e, dtype=np.float64)[None, :]
+
+
 def combine(y: np.ndarray, w: np.ndarray) -> np.ndarray:
     """Step 7: out[t] = sum_j w[t, j] * y[t*k + j] (float64, no rounding)."""
     T, k = w.shape
@@ -241,7 +290,9 @@ def moe_layer(inp: dict, BM: int = 16, tokens=None, progress=None) -> dict:
     """The whole layer in float64.
 
     inp holds x, w_router, bias, w13_q, w13_s, w2_q, w2_s and k (and
-    optionally gating, "softmax" when absent).  With
+    optionally gating, "softmax" when absent; and activation: "swiglu" when
+    absent, or "gptoss" with b13, b2 and optionally alpha and limit, which
+    runs expert_ffn_gptoss on the weights as given).  With
     ``tokens`` (an index array) only those tokens' outputs are evaluated
     (routing and the tile table still cover every token); experts are
     decoded one at a time so the largest layer stays within memory.
@@ -266,8 +317,14 @@ def moe_layer(inp: dict, BM: int = 16, tokens=None, progress=None) -> dict:
         slots = slots[need_slot[slots]]
         if slots.size == 0:
             continue
-        y[slots] = expert_ffn(x64[slots // k], inp["w13_q"][e], inp["w13_s"][e],
-                              inp["w2_q"][e], inp["w2_s"][e])
+        if inp.get("activation", "swiglu") == "gptoss":
+            y[slots] = expert_ffn_gptoss(x64[slots // k], inp["w13_q"][e], inp["w13_s"][e],
+                                         inp["w2_q"][e], inp["w2_s"][e], inp["b13"][e],
+                                         inp["b2"][e], inp.get("alpha", GPTOSS_ALPHA),
+                                         inp.get("limit", GPTOSS_LIMIT))
+        else:
+            y[slots] = expert_ffn(x64[slots // k], inp["w13_q"][e], inp["w13_s"][e],
+                                  inp["w2_q"][e], inp["w2_s"][e])
         if progress is not None:
             progress(e, E)
     out = combine(y, w)

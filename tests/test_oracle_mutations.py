@@ -12,6 +12,7 @@ from oracle import moe_oracle as mo
 
 import test_oracle_decode as tdec
 import test_oracle_ffn as tffn
+import test_oracle_gptoss as tgpt
 import test_oracle_routing as trout
 
 
@@ -88,6 +89,31 @@ def _blocked_whole_matrix(q):
     return np.ascontiguousarray(np.swapaxes(t, -3, -2)).reshape(q.shape)
 
 
+def _gptoss(gate_first_half=False, no_plus_one=False, gate_clamp_both=False, up_unclamped=False,
+            no_down_bias=False, alpha_one=False, bias_halves=False):
+    """expert_ffn_gptoss with one plausible mistake."""
+    def f(X, q13, s13, q2, s2, b13, b2, alpha=mo.GPTOSS_ALPHA, limit=mo.GPTOSS_LIMIT):
+        W13 = mo.dequant_mxfp4(q13, s13)
+        I = W13.shape[0] // 2
+        b = np.asarray(b13, dtype=np.float64)
+        if bias_halves:  # bias taken as [gate; up] while the rows interleave
+            b = np.stack([b[:I], b[I:]], axis=1).reshape(-1)
+        z = X @ W13.T + b[None, :]
+        g, u = (z[:, :I], z[:, I:]) if gate_first_half else (z[:, 0::2], z[:, 1::2])
+        g = np.clip(g, -limit, limit) if gate_clamp_both else np.minimum(g, limit)
+        if not up_unclamped:
+            u = np.clip(u, -limit, limit)
+        a = 1.0 if alpha_one else alpha
+        h = g / (1.0 + np.exp(-a * g)) * (u if no_plus_one else u + 1.0)
+        y = h @ mo.dequant_mxfp4(q2, s2).T
+        return y if no_down_bias else y + np.asarray(b2, dtype=np.float64)[None, :]
+    return f
+
+
+def _deinterleave_identity(a, axis):
+    return np.ascontiguousarray(np.asarray(a))
+
+
 _orig_build_tiles = mo.build_tiles
 
 PINS = [
@@ -103,6 +129,11 @@ PINS = [
     tffn.test_permutation_weights_closed_form,
     tffn.test_single_expert_equals_textbook_swiglu_mlp,
     lambda: tffn.test_routed_equals_dense_then_select(4, 64, 8, 2, 64, False),
+    tgpt.test_deinterleave_matches_index_loop_and_inverts,
+    tgpt.test_single_expert_equals_textbook_torch_mlp,
+    tgpt.test_clamp_boundaries_worked_example,
+    tgpt.test_bias_only_experts,
+    tgpt.test_reduces_to_plain_swiglu_plus_silu_term,
 ]
 
 MUTATIONS = {
@@ -119,6 +150,14 @@ MUTATIONS = {
     "unstable_scatter": ("build_tiles", _tiles_unstable),
     "blocked_layout_unchanged": ("blocked_from_canonical", _blocked_unchanged),
     "blocked_over_whole_matrix": ("blocked_from_canonical", _blocked_whole_matrix),
+    "gptoss_gate_first_half": ("expert_ffn_gptoss", _gptoss(gate_first_half=True)),
+    "gptoss_no_plus_one": ("expert_ffn_gptoss", _gptoss(no_plus_one=True)),
+    "gptoss_gate_clamped_both_sides": ("expert_ffn_gptoss", _gptoss(gate_clamp_both=True)),
+    "gptoss_up_unclamped": ("expert_ffn_gptoss", _gptoss(up_unclamped=True)),
+    "gptoss_no_down_bias": ("expert_ffn_gptoss", _gptoss(no_down_bias=True)),
+    "gptoss_alpha_one": ("expert_ffn_gptoss", _gptoss(alpha_one=True)),
+    "gptoss_bias_in_halves": ("expert_ffn_gptoss", _gptoss(bias_halves=True)),
+    "deinterleave_identity": ("concatenated_from_interleaved", _deinterleave_identity),
 }
 
 
