@@ -249,6 +249,51 @@ moe_status moe_forward(const uint16_t* x,
                        void* workspace, size_t workspace_bytes,
                        uint16_t* out, struct ihipStream_t* stream);
 
+/* ---------------------------------------------------- moe_forward_gptoss
+ * moe_forward with the expert form of the released gpt-oss models, which
+ * the SimpleLLM write-up runs from "the official MXFP4 checkpoints"
+ * ("Correctness") but does not spell out; its definition here is the
+ * released model's own (not on the pages):
+ *   z = x[t] W13_e^T + b13[e]
+ *   g = min(z_gate, limit), u = clip(z_up, -limit, limit)
+ *   h = g * sigmoid(alpha * g) * (u + 1)                    (rounded to bf16)
+ *   y[p] = h W2_e^T + b2[e]
+ * then the same combine.  The released models use alpha = 1.702, limit = 7.
+ *
+ *   arguments as for moe_forward, plus
+ *   w13_q, w13_s  gate rows [0, I) and up rows [I, 2I) of each expert: a
+ *                 checkpoint's interleaved rows (gate of output i at row 2i,
+ *                 up at 2i + 1) go through moe_deinterleave_rows first (and
+ *                 then moe_repack_weights for the blocked layout)
+ *   b13           [E][2I] fp32 in the same row order as w13 (so also
+ *                 de-interleaved), or NULL for zero biases
+ *   b2            [E][H] fp32, or NULL
+ *   alpha         finite;  limit > 0 (INFINITY: no clamp), else MOE_ERR_SHAPE
+ * Only the separate-launch path has this form (moe_layer_one_token keeps the
+ * plain SwiGLU). */
+moe_status moe_forward_gptoss(const uint16_t* x,
+                              const uint8_t* w13_q, const uint8_t* w13_s,
+                              const uint8_t* w2_q, const uint8_t* w2_s,
+                              const float* b13, const float* b2, float alpha, float limit,
+                              const float* topk_weights, const int32_t* sorted_ids,
+                              const int32_t* tiles, const int32_t* num_tiles,
+                              int T, int H, int I, int E, int k, int BM, int layout,
+                              void* workspace, size_t workspace_bytes,
+                              uint16_t* out, struct ihipStream_t* stream);
+
+/* ------------------------------------------------- moe_deinterleave_rows
+ * Load-time row permutation for checkpoints that keep each output's gate and
+ * up rows adjacent: within each of E blocks of 2I rows, destination row i
+ * takes source row 2i and destination row I + i takes source row 2i + 1.
+ * Bytes move unchanged ("Correctness": nothing is re-quantised).
+ *   src, dst   device, E * 2I rows of row_bytes bytes each (w13_q: row_bytes
+ *              = H/2; w13_s: H/32; b13 as fp32: 4); must not overlap
+ *              (MOE_ERR_OVERLAP)
+ *   E >= 1, I >= 1, row_bytes >= 1, total bytes < 2^40, else MOE_ERR_SHAPE
+ */
+moe_status moe_deinterleave_rows(const void* src, int E, int I, int row_bytes, void* dst,
+                                 struct ihipStream_t* stream);
+
 /* ------------------------------------------ moe_forward_static_workspace
  * moe_forward for callers that cannot allocate device memory: code being
  * captured into a HIP graph, tight serving loops, harnesses that forbid

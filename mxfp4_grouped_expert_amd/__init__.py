@@ -12,7 +12,8 @@ from .binding import (MoeError, LIB_PATH, load, version, status_string, pick_bm,
                       zeroed_route_tiles_workspace, moe_layer_one_token,
                       layer_one_token_workspace_bytes, layer_one_token_sync_bytes,
                       zeroed_layer_one_token_workspace, moe_repack_weights, LAYOUTS,
-                      GATINGS, moe_forward_static_workspace, STATIC_WORKSPACE_BYTES)
+                      GATINGS, moe_forward_static_workspace, STATIC_WORKSPACE_BYTES,
+                      moe_forward_gptoss, moe_deinterleave_rows, GPTOSS_ALPHA, GPTOSS_LIMIT)
 from .layer import MoeLayer
 
 __all__ = ["MoeError", "LIB_PATH", "load", "version", "status_string", "pick_bm", "tiles_max",
@@ -21,4 +22,5 @@ __all__ = ["MoeError", "LIB_PATH", "load", "version", "status_string", "pick_bm"
            "route_tiles_ok", "route_tiles_workspace_bytes", "zeroed_route_tiles_workspace",
            "moe_layer_one_token", "layer_one_token_workspace_bytes", "layer_one_token_sync_bytes",
            "zeroed_layer_one_token_workspace", "moe_repack_weights", "LAYOUTS", "GATINGS",
-           "moe_forward_static_workspace", "STATIC_WORKSPACE_BYTES", "MoeLayer"]
+           "moe_forward_static_workspace", "STATIC_WORKSPACE_BYTES", "moe_forward_gptoss",
+           "moe_deinterleave_rows", "GPTOSS_ALPHA", "GPTOSS_LIMIT", "MoeLayer"]

@@ -81,6 +81,12 @@ def load() -> ctypes.CDLL:
     lib.moe_forward_static_workspace.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _p,
                                                  _i, _i, _i, _i, _i, _i, _i, _p, _p]
     lib.moe_forward_static_workspace.restype = _i
+    lib.moe_forward_gptoss.argtypes = [_p, _p, _p, _p, _p, _p, _p, ctypes.c_float,
+                                       ctypes.c_float, _p, _p, _p, _p,
+                                       _i, _i, _i, _i, _i, _i, _i, _p, _sz, _p, _p]
+    lib.moe_forward_gptoss.restype = _i
+    lib.moe_deinterleave_rows.argtypes = [_p, _i, _i, _i, _p, _p]
+    lib.moe_deinterleave_rows.restype = _i
     lib.moe_repack_weights.argtypes = [_p, ctypes.c_int64, _i, _p, _p]
     lib.moe_repack_weights.restype = _i
     _lib = lib
@@ -366,6 +372,80 @@ def moe_forward(x: torch.Tensor, w13_q: torch.Tensor, w13_s: torch.Tensor, w2_q:
                               T, H, I, E, k, BM, layout_code(layout), _ptr(workspace),
                               workspace.numel(), _ptr(out),
                               _stream(dev)), "moe_forward")
+    return out
+
+
+def moe_deinterleave_rows(src: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Rows interleaved in gate/up pairs -> gate rows first, then up rows, per
+    expert: src [E, 2I, ...] (w13_q, w13_s, or b13 as fp32 [E, 2I]).  Returns
+    a new tensor of the same shape (bytes moved, nothing converted)."""
+    _need(src, "src", None)
+    if src.dim() < 2 or src.shape[1] % 2:
+        raise ValueError("src must be [E, 2I, ...]")
+    E, I2 = src.shape[0], src.shape[1]
+    row_bytes = src[0, 0].numel() * src.element_size()
+    if out is None:
+        out = torch.empty_like(src)
+    _need(out, "out", (src.dtype,), src.device)
+    if out.shape != src.shape:
+        raise ValueError("out must have the shape of src")
+    _check(load().moe_deinterleave_rows(_ptr(src), E, I2 // 2, row_bytes, _ptr(out),
+                                        _stream(src.device)), "moe_deinterleave_rows")
+    return out
+
+
+GPTOSS_ALPHA, GPTOSS_LIMIT = 1.702, 7.0
+
+
+def moe_forward_gptoss(x: torch.Tensor, w13_q: torch.Tensor, w13_s: torch.Tensor,
+                       w2_q: torch.Tensor, w2_s: torch.Tensor, b13: Optional[torch.Tensor],
+                       b2: Optional[torch.Tensor], topk_weights: torch.Tensor,
+                       sorted_ids: torch.Tensor, tiles: torch.Tensor, num_tiles: torch.Tensor,
+                       BM: int, alpha: float = GPTOSS_ALPHA, limit: float = GPTOSS_LIMIT,
+                       out: Optional[torch.Tensor] = None,
+                       workspace: Optional[torch.Tensor] = None,
+                       layout: str = "canonical") -> torch.Tensor:
+    """moe_forward with the gpt-oss expert form.  w13_q/w13_s and b13 are in
+    the kernels' row order (gate rows, then up rows: moe_deinterleave_rows of
+    a checkpoint's interleaved rows).  Returns out bf16 [T, H]."""
+    _need(x, "x", _BF16)
+    dev = x.device
+    for name, t in (("w13_q", w13_q), ("w13_s", w13_s), ("w2_q", w2_q), ("w2_s", w2_s)):
+        _need(t, name, _U8, dev)
+    _need(topk_weights, "topk_weights", (torch.float32,), dev)
+    _need(sorted_ids, "sorted_ids", (torch.int32,), dev)
+    _need(tiles, "tiles", (torch.int32,), dev)
+    _need(num_tiles, "num_tiles", (torch.int32,), dev)
+    T, H = x.shape
+    E, I2, Hh = w13_q.shape
+    I = I2 // 2
+    k = topk_weights.shape[1]
+    if (Hh * 2 != H or tuple(w13_s.shape) != (E, 2 * I, H // 32)
+            or tuple(w2_q.shape) != (E, H, I // 2) or tuple(w2_s.shape) != (E, H, I // 32)):
+        raise ValueError("weight shapes do not match x")
+    if b13 is not None:
+        _need(b13, "b13", (torch.float32,), dev)
+        if tuple(b13.shape) != (E, 2 * I):
+            raise ValueError("b13 must be fp32 [E, 2I]")
+    if b2 is not None:
+        _need(b2, "b2", (torch.float32,), dev)
+        if tuple(b2.shape) != (E, H):
+            raise ValueError("b2 must be fp32 [E, H]")
+    if topk_weights.shape[0] != T or sorted_ids.numel() != T * k:
+        raise ValueError("routing tensors do not match x")
+    if tiles.shape[0] < tiles_max(T, k, E, BM):
+        raise ValueError("tiles has fewer rows than moe_tiles_max")
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    _need(out, "out", _BF16, dev)
+    if workspace is None:
+        workspace = _workspace(forward_workspace_bytes(T, H, I, k), dev)
+    _check(load().moe_forward_gptoss(_ptr(x), _ptr(w13_q), _ptr(w13_s), _ptr(w2_q), _ptr(w2_s),
+                                     _ptr(b13), _ptr(b2), float(alpha), float(limit),
+                                     _ptr(topk_weights), _ptr(sorted_ids), _ptr(tiles),
+                                     _ptr(num_tiles), T, H, I, E, k, BM, layout_code(layout),
+                                     _ptr(workspace), workspace.numel(), _ptr(out),
+                                     _stream(dev)), "moe_forward_gptoss")
     return out
 
 

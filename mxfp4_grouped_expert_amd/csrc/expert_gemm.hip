@@ -58,7 +58,7 @@ __global__ __launch_bounds__(256 * NBW) void expert_gemm_kernel(
     const uint16_t* __restrict__ act, const uint8_t* __restrict__ wq,
     const uint8_t* __restrict__ ws, const int32_t* sorted_ids,  // not restrict: see below
     const int32_t* __restrict__ tiles, const int32_t* __restrict__ num_tiles, int T, int H,
-    int I, int E, int k, void* __restrict__ out) {
+    int I, int E, int k, void* __restrict__ out, ExpertAct fn) {
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int NW = GATEUP ? 2 : 1;  // weight rows per lane per step (gate + up)
 
@@ -390,11 +390,19 @@ __global__ __launch_bounds__(256 * NBW) void expert_gemm_kernel(
         if (tm < prow && on < N) {
           const int r = r0 + p0 + tm;
           if (GATEUP) {
-            reinterpret_cast<uint16_t*>(out)[(size_t)r * I + on] =
-                float_to_bf16(silu(v[0]) * v[NW - 1]);
+            float hv;
+            if (fn.kind == 0) {
+              hv = silu(v[0]) * v[NW - 1];
+            } else {
+              const float bg = fn.b13 ? fn.b13[(size_t)e * 2 * I + on] : 0.f;
+              const float bu = fn.b13 ? fn.b13[(size_t)e * 2 * I + I + on] : 0.f;
+              hv = act_gptoss(v[0] + bg, v[NW - 1] + bu, fn.alpha, fn.limit);
+            }
+            reinterpret_cast<uint16_t*>(out)[(size_t)r * I + on] = float_to_bf16(hv);
           } else {
             const long long p = s_slot[p0 + tm];
-            if (p >= 0 && p < nslots) reinterpret_cast<float*>(out)[(size_t)p * H + on] = v[0];
+            const float yv = fn.kind != 0 && fn.b2 ? v[0] + fn.b2[(size_t)e * H + on] : v[0];
+            if (p >= 0 && p < nslots) reinterpret_cast<float*>(out)[(size_t)p * H + on] = yv;
           }
         }
       }
@@ -420,7 +428,7 @@ __global__ __launch_bounds__(256 * kFuseMaxK) void down_combine_one_token_kernel
     const uint8_t* __restrict__ ws, const int32_t* sorted_ids,
     const int32_t* __restrict__ tiles, const int32_t* __restrict__ num_tiles,
     const float* __restrict__ topk_weights, int H, int I, int E, int k, bool blocked,
-    uint16_t* __restrict__ out) {
+    uint16_t* __restrict__ out, ExpertAct fn) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -451,6 +459,7 @@ __global__ __launch_bounds__(256 * kFuseMaxK) void down_combine_one_token_kernel
   unsigned char* s_sc = smem + kFuseMaxK * region + g * kScaleRunMax;
   float* red = reinterpret_cast<float*>(smem + kFuseMaxK * (region + kScaleRunMax));
   __shared__ int s_slot[kFuseMaxK];
+  __shared__ int s_exp[kFuseMaxK];
 
   uint4 wreg[kChunk];
   uint32_t sreg[kChunk];
@@ -483,7 +492,10 @@ __global__ __launch_bounds__(256 * kFuseMaxK) void down_combine_one_token_kernel
   }
   if (tid < kFuseMaxK) s_slot[tid] = -1;
   lds_barrier();
-  if (live && kq == 0 && lane == 0) s_slot[g] = slot;
+  if (live && kq == 0 && lane == 0) {
+    s_slot[g] = slot;
+    s_exp[g] = e;
+  }
 
   floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
   if (live) {
@@ -516,6 +528,8 @@ __global__ __launch_bounds__(256 * kFuseMaxK) void down_combine_one_token_kernel
       float v = red[(gg * 4 + 0) * 16 + tid];
 #pragma unroll
       for (int q = 1; q < 4; ++q) v += red[(gg * 4 + q) * 16 + tid];
+      if (fn.kind != 0 && fn.b2 && s_slot[gg] >= 0)
+        v += fn.b2[(size_t)s_exp[gg] * H + blockIdx.x * kRowsPerBlock + tid];
       y[gg] = v;
     }
     float a = 0.f;
@@ -555,7 +569,7 @@ template <bool GATEUP, bool BLK>
 void launch_expert_gemm(const uint16_t* act, const uint8_t* wq, const uint8_t* ws,
                         const int32_t* sorted_ids, const int32_t* tiles,
                         const int32_t* num_tiles, int tiles_max, int T, int H, int I, int E,
-                        int k, int BM, void* out, hipStream_t stream) {
+                        int k, int BM, void* out, const ExpertAct& fn, hipStream_t stream) {
   const int K = GATEUP ? H : I;
   const int N = GATEUP ? I : H;
   const int xr = pick_xr(T, BM, K, E, k);
@@ -574,15 +588,15 @@ void launch_expert_gemm(const uint16_t* act, const uint8_t* wq, const uint8_t* w
     if (one_chunk)                                                                              \
       hipLaunchKernelGGL((expert_gemm_kernel<GATEUP, NBW_, XR_, true, BLK>), grid, dim3(256 * (NBW_)), \
                          lds, stream, act, wq, ws, sorted_ids, tiles, num_tiles, T, H, I, E, k,  \
-                         out);                                                                  \
+                         out, fn);                                                              \
     else if (group2)                                                                            \
       hipLaunchKernelGGL((expert_gemm_kernel<GATEUP, NBW_, XR_, false, BLK, 2>), grid,          \
                          dim3(256 * (NBW_)), lds, stream, act, wq, ws, sorted_ids, tiles,       \
-                         num_tiles, T, H, I, E, k, out);                                        \
+                         num_tiles, T, H, I, E, k, out, fn);                                    \
     else                                                                                        \
       hipLaunchKernelGGL((expert_gemm_kernel<GATEUP, NBW_, XR_, false, BLK, 1>), grid,          \
                          dim3(256 * (NBW_)), lds, stream, act, wq, ws, sorted_ids, tiles,       \
-                         num_tiles, T, H, I, E, k, out);                                        \
+                         num_tiles, T, H, I, E, k, out, fn);                                    \
   } while (0)
   switch (xr) {
     case 1: MOE_LAUNCH(1, 1); break;
@@ -599,18 +613,19 @@ void launch_expert_gemm(const uint16_t* act, const uint8_t* wq, const uint8_t* w
 void launch_gateup_swiglu(const uint16_t* x, const uint8_t* w13_q, const uint8_t* w13_s,
                           const int32_t* sorted_ids, const int32_t* tiles,
                           const int32_t* num_tiles, int tiles_max, int T, int H, int I, int E,
-                          int k, int BM, bool blocked, uint16_t* h, hipStream_t stream) {
+                          int k, int BM, bool blocked, uint16_t* h, const ExpertAct& fn,
+                          hipStream_t stream) {
   if (expert_mma_ok(T, H, I, E, k, BM)) {
     launch_expert_mma(true, x, w13_q, w13_s, sorted_ids, tiles, num_tiles, tiles_max, T, H, I, E,
-                      k, blocked, h, stream);
+                      k, blocked, h, fn, stream);
     return;
   }
   if (blocked)
     launch_expert_gemm<true, true>(x, w13_q, w13_s, sorted_ids, tiles, num_tiles, tiles_max, T,
-                                   H, I, E, k, BM, h, stream);
+                                   H, I, E, k, BM, h, fn, stream);
   else
     launch_expert_gemm<true, false>(x, w13_q, w13_s, sorted_ids, tiles, num_tiles, tiles_max, T,
-                                    H, I, E, k, BM, h, stream);
+                                    H, I, E, k, BM, h, fn, stream);
 }
 
 bool down_combine_one_token_ok(int T, int H, int I, int k) {
@@ -621,29 +636,29 @@ void launch_down_combine_one_token(const uint16_t* h, const uint8_t* w2_q, const
                                    const int32_t* sorted_ids, const int32_t* tiles,
                                    const int32_t* num_tiles, const float* topk_weights, int H,
                                    int I, int E, int k, bool blocked, uint16_t* out,
-                                   hipStream_t stream) {
+                                   const ExpertAct& fn, hipStream_t stream) {
   const size_t red_bytes = (size_t)kFuseMaxK * 4 * 16 * sizeof(float);
   const size_t lds = (size_t)kFuseMaxK * (fuse_row_region(I) + kScaleRunMax) + red_bytes;
   hipLaunchKernelGGL(down_combine_one_token_kernel, dim3(H / kRowsPerBlock),
                      dim3(256 * kFuseMaxK), lds, stream, h, w2_q, w2_s, sorted_ids, tiles,
-                     num_tiles, topk_weights, H, I, E, k, blocked, out);
+                     num_tiles, topk_weights, H, I, E, k, blocked, out, fn);
 }
 
 void launch_down(const uint16_t* h, const uint8_t* w2_q, const uint8_t* w2_s,
                  const int32_t* sorted_ids, const int32_t* tiles, const int32_t* num_tiles,
                  int tiles_max, int T, int H, int I, int E, int k, int BM, bool blocked,
-                 float* y, hipStream_t stream) {
+                 float* y, const ExpertAct& fn, hipStream_t stream) {
   if (expert_mma_ok(T, H, I, E, k, BM)) {
     launch_expert_mma(false, h, w2_q, w2_s, sorted_ids, tiles, num_tiles, tiles_max, T, H, I, E,
-                      k, blocked, y, stream);
+                      k, blocked, y, fn, stream);
     return;
   }
   if (blocked)
     launch_expert_gemm<false, true>(h, w2_q, w2_s, sorted_ids, tiles, num_tiles, tiles_max, T, H,
-                                    I, E, k, BM, y, stream);
+                                    I, E, k, BM, y, fn, stream);
   else
     launch_expert_gemm<false, false>(h, w2_q, w2_s, sorted_ids, tiles, num_tiles, tiles_max, T,
-                                     H, I, E, k, BM, y, stream);
+                                     H, I, E, k, BM, y, fn, stream);
 }
 
 }  // namespace moe

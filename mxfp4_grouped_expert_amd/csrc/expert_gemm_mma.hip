@@ -137,9 +137,10 @@ struct UnitCtx {
   int w_swz[2];             // the MX block (0/1) of the stage it fetches
   int w_dst[2];             // its 1 KB slot within the stage's weight area
   int soff[kNFW];           // slab offset of this lane's row, per fragment
-  int K, KB, niters, wave, lane, mg, wn, n0, N, H, I, r0, rows;
+  int K, KB, niters, wave, lane, mg, wn, n0, N, H, I, r0, rows, e;
   long long nslots;
   void* out;
+  ExpertAct fn;
 };
 
 // Weight direct loads of stage `it` into buffer st: slice loads 0, 1 go to
@@ -349,8 +350,18 @@ __device__ __forceinline__ void unit_main(const UnitCtx& c, int mrow0) {
         const int col = col0 + 8 * f;
         uint16_t* o = reinterpret_cast<uint16_t*>(c.out) + (size_t)(c.r0 + row) * c.I + col;
         if (col < c.N) {
-          if (row < c.rows) o[0] = float_to_bf16(silu_fast(g0) * u0);
-          if (row + 1 < c.rows) o[c.I] = float_to_bf16(silu_fast(g1) * u1);
+          float h0, h1;
+          if (c.fn.kind == 0) {
+            h0 = silu_fast(g0) * u0;
+            h1 = silu_fast(g1) * u1;
+          } else {
+            const float bg = c.fn.b13 ? c.fn.b13[(size_t)c.e * 2 * c.I + col] : 0.f;
+            const float bu = c.fn.b13 ? c.fn.b13[(size_t)c.e * 2 * c.I + c.I + col] : 0.f;
+            h0 = act_gptoss_fast(g0 + bg, u0 + bu, c.fn.alpha, c.fn.limit);
+            h1 = act_gptoss_fast(g1 + bg, u1 + bu, c.fn.alpha, c.fn.limit);
+          }
+          if (row < c.rows) o[0] = float_to_bf16(h0);
+          if (row + 1 < c.rows) o[c.I] = float_to_bf16(h1);
         }
       }
     }
@@ -366,7 +377,12 @@ __device__ __forceinline__ void unit_main(const UnitCtx& c, int mrow0) {
 #pragma unroll
         for (int f = 0; f < NF; ++f) {
           const int col = cbase + 16 * f + li;
-          if (col < c.N) reinterpret_cast<float*>(c.out)[(size_t)p * c.H + col] = acc[i][f][r];
+          if (col < c.N) {
+            const float bias =
+                c.fn.kind != 0 && c.fn.b2 ? c.fn.b2[(size_t)c.e * c.H + col] : 0.f;
+            reinterpret_cast<float*>(c.out)[(size_t)p * c.H + col] =
+                c.fn.kind != 0 ? acc[i][f][r] + bias : acc[i][f][r];
+          }
         }
       }
     }
@@ -378,7 +394,7 @@ __global__ __launch_bounds__(kThreads, 1) void expert_mma_kernel(
     const uint16_t* __restrict__ act, const uint8_t* __restrict__ wq,
     const uint8_t* __restrict__ ws, const int32_t* sorted_ids,
     const int32_t* __restrict__ tiles, const int32_t* __restrict__ num_tiles, int T, int H,
-    int I, int E, int k, int ncb, bool blocked, void* __restrict__ out) {
+    int I, int E, int k, int ncb, bool blocked, void* __restrict__ out, ExpertAct fn) {
   constexpr int kCols = GATEUP ? kColsGateUp : kColsDown;  // output columns per slice
   constexpr int kRunRows = 4 * kCols;                        // rows per scale run
   constexpr int kRuns = GATEUP ? 2 : 1;                      // gate + up, or w2
@@ -407,6 +423,8 @@ __global__ __launch_bounds__(kThreads, 1) void expert_mma_kernel(
   c.niters = (c.KB + 1) / 2;
   c.n0 = cb * 4 * kCols;
   c.H = H; c.I = I; c.r0 = r0; c.rows = rows; c.nslots = nslots; c.out = out;
+  c.e = e;
+  c.fn = fn;
   const int tid = threadIdx.x;
   c.wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, so branches on
   c.lane = tid & 63;                                   // it stay scalar
@@ -554,17 +572,17 @@ bool expert_mma_ok(int T, int H, int I, int E, int k, int BM) {
 void launch_expert_mma(bool gateup, const uint16_t* act, const uint8_t* wq, const uint8_t* ws,
                        const int32_t* sorted_ids, const int32_t* tiles, const int32_t* num_tiles,
                        int tiles_max, int T, int H, int I, int E, int k, bool blocked,
-                       void* out, hipStream_t stream) {
+                       void* out, const ExpertAct& fn, hipStream_t stream) {
   const int N = gateup ? I : H;
   const int ncol = 4 * (gateup ? kColsGateUp : kColsDown);
   const int ncb = (N + ncol - 1) / ncol;
   const dim3 grid((unsigned)tiles_max * (unsigned)ncb);
   if (gateup)
     hipLaunchKernelGGL(expert_mma_kernel<true>, grid, dim3(kThreads), kLdsBytes, stream, act, wq, ws,
-                       sorted_ids, tiles, num_tiles, T, H, I, E, k, ncb, blocked, out);
+                       sorted_ids, tiles, num_tiles, T, H, I, E, k, ncb, blocked, out, fn);
   else
     hipLaunchKernelGGL(expert_mma_kernel<false>, grid, dim3(kThreads), kLdsBytes, stream, act, wq, ws,
-                       sorted_ids, tiles, num_tiles, T, H, I, E, k, ncb, blocked, out);
+                       sorted_ids, tiles, num_tiles, T, H, I, E, k, ncb, blocked, out, fn);
 }
 
 }  // namespace moe

@@ -210,7 +210,8 @@ moe_status moe_gateup_swiglu(const uint16_t* x, const uint8_t* w13_q, const uint
   (void)hipGetLastError();
   moe::launch_gateup_swiglu(x, w13_q, w13_s, sorted_ids, tiles, num_tiles,
                             (int)moe_tiles_max(T, k, E, BM), T, H, I, E, k, BM,
-                            layout == MOE_LAYOUT_BLOCKED, h, as_stream(stream));
+                            layout == MOE_LAYOUT_BLOCKED, h, moe::plain_swiglu(),
+                            as_stream(stream));
   return finish_launches();
 }
 
@@ -226,7 +227,8 @@ moe_status moe_down(const uint16_t* h, const uint8_t* w2_q, const uint8_t* w2_s,
   if (st != MOE_OK) return st;
   (void)hipGetLastError();
   moe::launch_down(h, w2_q, w2_s, sorted_ids, tiles, num_tiles, (int)moe_tiles_max(T, k, E, BM),
-                   T, H, I, E, k, BM, layout == MOE_LAYOUT_BLOCKED, y, as_stream(stream));
+                   T, H, I, E, k, BM, layout == MOE_LAYOUT_BLOCKED, y, moe::plain_swiglu(),
+                   as_stream(stream));
   return finish_launches();
 }
 
@@ -273,22 +275,23 @@ moe_status forward_launch(const uint16_t* x, const uint8_t* w13_q, const uint8_t
                           const uint8_t* w2_q, const uint8_t* w2_s, const float* topk_weights,
                           const int32_t* sorted_ids, const int32_t* tiles,
                           const int32_t* num_tiles, int T, int H, int I, int E, int k, int BM,
-                          int layout, void* workspace, uint16_t* out, hipStream_t s) {
+                          int layout, void* workspace, uint16_t* out, const moe::ExpertAct& fn,
+                          hipStream_t s) {
   const int64_t tmax = moe_tiles_max(T, k, E, BM);
   const size_t nslots = (size_t)T * (size_t)k;
   uint16_t* h = static_cast<uint16_t*>(workspace);
   float* y = reinterpret_cast<float*>(static_cast<char*>(workspace) + round256(nslots * I * 2));
   const bool blocked = layout == MOE_LAYOUT_BLOCKED;
   moe::launch_gateup_swiglu(x, w13_q, w13_s, sorted_ids, tiles, num_tiles, (int)tmax, T, H, I, E,
-                            k, BM, blocked, h, s);
+                            k, BM, blocked, h, fn, s);
   if (moe::down_combine_one_token_ok(T, H, I, k)) {
     // one token: down GEMM and combine in one launch, bit-identical to the two
     moe::launch_down_combine_one_token(h, w2_q, w2_s, sorted_ids, tiles, num_tiles, topk_weights,
-                                       H, I, E, k, blocked, out, s);
+                                       H, I, E, k, blocked, out, fn, s);
     return finish_launches();
   }
   moe::launch_down(h, w2_q, w2_s, sorted_ids, tiles, num_tiles, (int)tmax, T, H, I, E, k, BM,
-                   blocked, y, s);
+                   blocked, y, fn, s);
   moe::launch_combine(y, topk_weights, T, H, k, out, s);
   return finish_launches();
 }
@@ -343,7 +346,50 @@ moe_status moe_forward(const uint16_t* x, const uint8_t* w13_q, const uint8_t* w
   if (st != MOE_OK) return st;
   (void)hipGetLastError();
   return forward_launch(x, w13_q, w13_s, w2_q, w2_s, topk_weights, sorted_ids, tiles, num_tiles,
-                        T, H, I, E, k, BM, layout, workspace, out, as_stream(stream));
+                        T, H, I, E, k, BM, layout, workspace, out, moe::plain_swiglu(),
+                        as_stream(stream));
+}
+
+moe_status moe_forward_gptoss(const uint16_t* x, const uint8_t* w13_q, const uint8_t* w13_s,
+                              const uint8_t* w2_q, const uint8_t* w2_s, const float* b13,
+                              const float* b2, float alpha, float limit,
+                              const float* topk_weights, const int32_t* sorted_ids,
+                              const int32_t* tiles, const int32_t* num_tiles, int T, int H, int I,
+                              int E, int k, int BM, int layout, void* workspace,
+                              size_t workspace_bytes, uint16_t* out,
+                              struct ihipStream_t* stream) {
+  // alpha finite; limit > 0 (+inf: no clamp); NaN fails both
+  if (!(alpha == alpha && alpha - alpha == 0.0f) || !(limit > 0.0f)) return MOE_ERR_SHAPE;
+  moe_status st = forward_validate(x, w13_q, w13_s, w2_q, w2_s, topk_weights, sorted_ids, tiles,
+                                   num_tiles, T, H, I, E, k, BM, layout, out);
+  if (st != MOE_OK || T == 0) return st;
+  if (!workspace) return MOE_ERR_NULL;
+  if (!aligned16(workspace)) return MOE_ERR_ALIGN;
+  if (workspace_bytes < moe_forward_workspace_bytes(T, H, I, k)) return MOE_ERR_WORKSPACE;
+  st = check_device();
+  if (st != MOE_OK) return st;
+  (void)hipGetLastError();
+  const moe::ExpertAct fn{b13, b2, alpha, limit, 1};
+  return forward_launch(x, w13_q, w13_s, w2_q, w2_s, topk_weights, sorted_ids, tiles, num_tiles,
+                        T, H, I, E, k, BM, layout, workspace, out, fn, as_stream(stream));
+}
+
+moe_status moe_deinterleave_rows(const void* src, int E, int I, int row_bytes, void* dst,
+                                 struct ihipStream_t* stream) {
+  if (E < 1 || I < 1 || row_bytes < 1 || (int64_t)E * 2 * I * row_bytes >= (int64_t(1) << 40))
+    return MOE_ERR_SHAPE;
+  if (!src || !dst) return MOE_ERR_NULL;
+  {
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(src), b0 = reinterpret_cast<uintptr_t>(dst);
+    const uintptr_t n = (uintptr_t)E * 2 * I * (uintptr_t)row_bytes;
+    if (a0 < b0 + n && b0 < a0 + n) return MOE_ERR_OVERLAP;
+  }
+  moe_status st = check_device();
+  if (st != MOE_OK) return st;
+  (void)hipGetLastError();
+  moe::launch_deinterleave_rows(static_cast<const uint8_t*>(src), E, I, row_bytes,
+                                static_cast<uint8_t*>(dst), as_stream(stream));
+  return finish_launches();
 }
 
 moe_status moe_forward_static_workspace(const uint16_t* x, const uint8_t* w13_q,
@@ -365,7 +411,8 @@ moe_status moe_forward_static_workspace(const uint16_t* x, const uint8_t* w13_q,
   if (st != MOE_OK) return st;
   (void)hipGetLastError();
   return forward_launch(x, w13_q, w13_s, w2_q, w2_s, topk_weights, sorted_ids, tiles, num_tiles,
-                        T, H, I, E, k, BM, layout, ws, out, as_stream(stream));
+                        T, H, I, E, k, BM, layout, ws, out, moe::plain_swiglu(),
+                        as_stream(stream));
 }
 
 size_t moe_layer_one_token_workspace_bytes(int H, int I, int E, int k) {

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "moe_launch.h"
+
 namespace moe {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -68,6 +70,22 @@ __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 // negative z gives 1 / inf = 0, large positive z gives z.
 __device__ __forceinline__ float silu_fast(float z) {
   return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * 1.4426950408889634f));
+}
+
+// The gpt-oss activation of a (gate, up) pair with their biases already
+// added (ExpertAct kind 1, moe_launch.h).
+__device__ __forceinline__ float act_gptoss(float g, float u, float alpha, float limit) {
+  g = fminf(g, limit);
+  u = fminf(fmaxf(u, -limit), limit);
+  return g / (1.0f + expf(-alpha * g)) * (u + 1.0f);
+}
+
+// The same with the hardware exp2 and reciprocal (as silu_fast).
+__device__ __forceinline__ float act_gptoss_fast(float g, float u, float alpha, float limit) {
+  g = fminf(g, limit);
+  u = fminf(fmaxf(u, -limit), limit);
+  return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-alpha * g * 1.4426950408889634f)) *
+         (u + 1.0f);
 }
 
 // Value of the other lane of an even/odd lane pair (quad permutation 1,0,3,2

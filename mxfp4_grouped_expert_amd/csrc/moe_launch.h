@@ -8,6 +8,22 @@
 
 namespace moe {
 
+// The expert activation of the gate/up epilogue, and the expert biases.
+// kind 0: the SwiGLU of the pages, h = silu(g) * u, no biases (b13 and b2
+// ignored).  kind 1: the gpt-oss form: g and u get their w13 row's bias
+// (b13 [E][2I] in the kernels' row order: gate n at [e][n], up n at
+// [e][I + n]), then h = min(g, limit) * sigmoid(alpha * min(g, limit)) *
+// (clip(u, -limit, limit) + 1); the down output gets its w2 row's bias (b2
+// [E][H]).  Null bias pointers mean zero biases.
+struct ExpertAct {
+  const float* b13;
+  const float* b2;
+  float alpha;
+  float limit;
+  int kind;
+};
+inline ExpertAct plain_swiglu() { return ExpertAct{nullptr, nullptr, 1.0f, 0.0f, 0}; }
+
 // Router: fp64 partial logits over `splits` K-ranges, then top-k + softmax.
 struct RouterPlan {
   int splits;      // number of K-ranges
@@ -43,11 +59,12 @@ void launch_build_tiles(const int32_t* topk_ids, int N, int E, int BM, int32_t* 
 void launch_gateup_swiglu(const uint16_t* x, const uint8_t* w13_q, const uint8_t* w13_s,
                           const int32_t* sorted_ids, const int32_t* tiles,
                           const int32_t* num_tiles, int tiles_max, int T, int H, int I, int E,
-                          int k, int BM, bool blocked, uint16_t* h, hipStream_t stream);
+                          int k, int BM, bool blocked, uint16_t* h, const ExpertAct& act,
+                          hipStream_t stream);
 void launch_down(const uint16_t* h, const uint8_t* w2_q, const uint8_t* w2_s,
                  const int32_t* sorted_ids, const int32_t* tiles, const int32_t* num_tiles,
                  int tiles_max, int T, int H, int I, int E, int k, int BM, bool blocked,
-                 float* y, hipStream_t stream);
+                 float* y, const ExpertAct& act, hipStream_t stream);
 
 // Down GEMM and combine of a single token in one launch (no y buffer).
 bool down_combine_one_token_ok(int T, int H, int I, int k);
@@ -55,7 +72,7 @@ void launch_down_combine_one_token(const uint16_t* h, const uint8_t* w2_q, const
                                    const int32_t* sorted_ids, const int32_t* tiles,
                                    const int32_t* num_tiles, const float* topk_weights, int H,
                                    int I, int E, int k, bool blocked, uint16_t* out,
-                                   hipStream_t stream);
+                                   const ExpertAct& act, hipStream_t stream);
 
 // Large-tile (prefill) form of the grouped GEMMs: 128-row tiles, LDS-staged
 // operands.  expert_mma_ok says when the launchers above use it.
@@ -63,7 +80,13 @@ bool expert_mma_ok(int T, int H, int I, int E, int k, int BM);
 void launch_expert_mma(bool gateup, const uint16_t* act, const uint8_t* wq, const uint8_t* ws,
                        const int32_t* sorted_ids, const int32_t* tiles, const int32_t* num_tiles,
                        int tiles_max, int T, int H, int I, int E, int k, bool blocked,
-                       void* out, hipStream_t stream);
+                       void* out, const ExpertAct& fn, hipStream_t stream);
+
+// Rows interleaved in pairs within each of E blocks of 2I rows -> the two
+// halves: dst row [e][i] = src row [e][2i], dst row [e][I + i] =
+// src row [e][2i + 1]; rows of row_bytes bytes.
+void launch_deinterleave_rows(const uint8_t* src, int E, int I, int row_bytes, uint8_t* dst,
+                              hipStream_t stream);
 
 // The whole layer for one token in one launch (routing, gate/up, down and
 // combine; bit-identical to the separate launches).  The workspace starts

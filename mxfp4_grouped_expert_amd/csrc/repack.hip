@@ -36,7 +36,44 @@ __global__ __launch_bounds__(256) void repack_blocked_kernel(const uint4* __rest
   }
 }
 
+// Row de-interleave of a [E][2I] stack of rows (the gpt-oss checkpoints
+// keep each output's gate and up rows adjacent; the kernels read the two
+// halves): destination row (e, i) <- source row (e, 2i), destination row
+// (e, I + i) <- source row (e, 2i + 1).  One thread per CH-byte piece, in
+// destination order (CH = 16 when rows are whole 16-byte pieces, else 1).
+template <typename Piece>
+__global__ __launch_bounds__(256) void deinterleave_rows_kernel(const Piece* __restrict__ src,
+                                                                long long npieces,
+                                                                long long per_row, int I,
+                                                                Piece* __restrict__ dst) {
+  for (long long d = (long long)blockIdx.x * 256 + threadIdx.x; d < npieces;
+       d += (long long)gridDim.x * 256) {
+    const long long row = d / per_row, off = d - row * per_row;
+    const long long e = row / (2LL * I), r = row - e * 2LL * I;
+    const long long sr = r < I ? 2 * r : 2 * (r - I) + 1;
+    dst[d] = src[(e * 2LL * I + sr) * per_row + off];
+  }
+}
+
 }  // namespace
+
+void launch_deinterleave_rows(const uint8_t* src, int E, int I, int row_bytes, uint8_t* dst,
+                              hipStream_t stream) {
+  const long long rows = 2LL * E * I;
+  const bool wide = row_bytes % 16 == 0 && (reinterpret_cast<uintptr_t>(src) & 15) == 0 &&
+                    (reinterpret_cast<uintptr_t>(dst) & 15) == 0;
+  const long long per_row = wide ? row_bytes / 16 : row_bytes;
+  const long long npieces = rows * per_row;
+  long long blocks = (npieces + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  if (wide)
+    hipLaunchKernelGGL(deinterleave_rows_kernel<uint4>, dim3((unsigned)blocks), dim3(256), 0,
+                       stream, reinterpret_cast<const uint4*>(src), npieces, per_row, I,
+                       reinterpret_cast<uint4*>(dst));
+  else
+    hipLaunchKernelGGL(deinterleave_rows_kernel<uint8_t>, dim3((unsigned)blocks), dim3(256), 0,
+                       stream, src, npieces, per_row, I, dst);
+}
 
 void launch_repack_blocked(const uint8_t* q, long long rows, int K, uint8_t* qb,
                            hipStream_t stream) {

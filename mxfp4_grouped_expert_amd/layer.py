@@ -9,6 +9,13 @@ library's canonical layout (see include/moe_mxfp4.h).  By default
 (layout="blocked") the layer repacks the packed codes once, at construction,
 into a copy its kernels read in the blocked layout (one contiguous kilobyte
 per wave load); layout="canonical" reads the given codes as they are.
+
+activation="gptoss" selects the released gpt-oss expert form
+(moe_forward_gptoss: biases b13 [E, 2I] and b2 [E, H], clamped SwiGLU with
+alpha and limit).  Its w13 rows (and b13 entries) are taken as a checkpoint
+stores them, gate and up of each output adjacent, and are de-interleaved
+once at construction (w13_interleaved=False when they already come as the
+two halves).  That form runs as separate launches at every batch size.
 """
 from __future__ import annotations
 
@@ -43,7 +50,16 @@ class MoeLayer:
     def __init__(self, w_router: torch.Tensor, bias: Optional[torch.Tensor],
                  w13_q: torch.Tensor, w13_s: torch.Tensor, w2_q: torch.Tensor,
                  w2_s: torch.Tensor, k: int, gating: str = "softmax",
-                 layout: str = "blocked"):
+                 layout: str = "blocked", activation: str = "swiglu",
+                 b13: Optional[torch.Tensor] = None, b2: Optional[torch.Tensor] = None,
+                 alpha: float = B.GPTOSS_ALPHA, limit: float = B.GPTOSS_LIMIT,
+                 w13_interleaved: bool = True):
+        if activation not in ("swiglu", "gptoss"):
+            raise ValueError("activation must be 'swiglu' or 'gptoss'")
+        self.gptoss = activation == "gptoss"
+        if not self.gptoss and (b13 is not None or b2 is not None):
+            raise ValueError("expert biases need activation='gptoss'")
+        self.alpha, self.limit = float(alpha), float(limit)
         self.gating = B.gating_code(gating)
         self.layout = B.layout_code(layout)
         if not isinstance(w13_q, torch.Tensor) or w13_q.dim() != 3:
@@ -59,6 +75,18 @@ class MoeLayer:
         if bias is not None:
             _expect(bias, "bias", (torch.float32,), (self.E,), self.device)
         self.w_router, self.bias = w_router, bias
+        if b13 is not None:
+            _expect(b13, "b13", (torch.float32,), (self.E, 2 * self.I), self.device)
+        if b2 is not None:
+            _expect(b2, "b2", (torch.float32,), (self.E, self.H), self.device)
+        if self.gptoss and w13_interleaved:
+            _expect(w13_q, "w13_q", (torch.uint8,), (self.E, 2 * self.I, self.H // 2), self.device)
+            _expect(w13_s, "w13_s", (torch.uint8,), (self.E, 2 * self.I, self.H // 32),
+                    self.device)
+            w13_q, w13_s = B.moe_deinterleave_rows(w13_q), B.moe_deinterleave_rows(w13_s)
+            if b13 is not None:
+                b13 = B.moe_deinterleave_rows(b13)
+        self.b13, self.b2 = b13, b2
         self.set_weights(w13_q, w13_s, w2_q, w2_s, repack=True)
         self.T = None
 
@@ -98,7 +126,7 @@ class MoeLayer:
                                   dtype=torch.uint8, device=dev)
         self.out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
         one_ws = B.layer_one_token_workspace_bytes(H, I, E, k) if T == 1 else 0
-        self.one_launch = bool(one_launch and one_ws > 0)
+        self.one_launch = bool(one_launch and one_ws > 0 and not self.gptoss)
         # its counters must start zeroed; every call leaves them that way
         self.one_ws = (torch.zeros(one_ws, dtype=torch.uint8, device=dev)
                        if self.one_launch else None)
@@ -208,6 +236,14 @@ class MoeLayer:
             return self.out
         self.route_only(x)
         self.tiles_only()
+        if self.gptoss:
+            B._check(lib.moe_forward_gptoss(p(x), p(self.w13_q), p(self.w13_s), p(self.w2_q),
+                                            p(self.w2_s), p(self.b13), p(self.b2), self.alpha,
+                                            self.limit, p(self.topk_weights), p(self.sorted_ids),
+                                            p(self.tiles), p(self.num_tiles), T, H, I, E, k, BM,
+                                            self.layout, p(self.fwd_ws), self.fwd_ws.numel(),
+                                            p(self.out), s), "moe_forward_gptoss")
+            return self.out
         B._check(lib.moe_forward(p(x), p(self.w13_q), p(self.w13_s), p(self.w2_q), p(self.w2_s),
                                  p(self.topk_weights), p(self.sorted_ids), p(self.tiles),
                                  p(self.num_tiles), T, H, I, E, k, BM, self.layout, p(self.fwd_ws),

@@ -160,6 +160,36 @@ def test_static_workspace_limit_matches_header():
     assert moe.forward_workspace_bytes(971, 2880, 2880, 1) > moe.STATIC_WORKSPACE_BYTES
 
 
+def _forward_gptoss(**kw):
+    a = dict(x=P, q13=P, s13=P, q2=P, s2=P, b13=P, b2=None, alpha=1.702, limit=7.0, wts=P, srt=P,
+             tiles=P, nt=P, T=4, H=256, I=512, E=8, k=2, BM=16, layout=0, ws=P, wsb=1 << 30, out=P)
+    a.update(kw)
+    return B.load().moe_forward_gptoss(
+        a["x"], a["q13"], a["s13"], a["q2"], a["s2"], a["b13"], a["b2"], a["alpha"], a["limit"],
+        a["wts"], a["srt"], a["tiles"], a["nt"], a["T"], a["H"], a["I"], a["E"], a["k"], a["BM"],
+        a["layout"], a["ws"], a["wsb"], a["out"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(x=None), NULL), (dict(ws=None), NULL), (dict(out=None), NULL),
+    (dict(H=100), SHAPE), (dict(BM=24), SHAPE), (dict(layout=2), SHAPE),
+    (dict(alpha=float("nan")), SHAPE), (dict(alpha=float("inf")), SHAPE),
+    (dict(limit=0.0), SHAPE), (dict(limit=-1.0), SHAPE), (dict(limit=float("nan")), SHAPE),
+    (dict(q13=PMIS), ALIGN), (dict(wsb=1000), WORKSPACE), (dict(T=0, x=None), OK),
+])
+def test_forward_gptoss_validation(kw, want):
+    assert _forward_gptoss(**kw) == want
+
+
+@pytest.mark.parametrize("args,want", [
+    ((P, 0, 4, 16, P + (1 << 20)), SHAPE), ((P, 2, 0, 16, P + (1 << 20)), SHAPE),
+    ((P, 2, 4, 0, P + (1 << 20)), SHAPE), ((None, 2, 4, 16, P), NULL),
+    ((P, 2, 4, 16, None), NULL), ((P, 2, 4, 16, P + 64), OVERLAP),
+])
+def test_deinterleave_rows_validation(args, want):
+    assert B.load().moe_deinterleave_rows(*args, None) == want
+
+
 def _route_tiles(**kw):
     a = dict(x=P, w=P, bias=None, T=4, H=256, E=8, k=2, gating=0, BM=16, ids=P, wts=P,
              logits=None, off=P, srt=P, tiles=P, nt=P, ws=P, wsb=1 << 20)
