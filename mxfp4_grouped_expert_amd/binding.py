@@ -220,13 +220,18 @@ def route_tiles_workspace_bytes(T: int, H: int, E: int) -> int:
     return int(load().moe_route_tiles_workspace_bytes(T, H, E))
 
 
+# largest batch that moe_route_tiles routes and tiles in one workgroup
+ROUTE_TILES_ONE_WG_MAX_T = 16
+
+
 def route_tiles_ok(T: int, E: int, k: int) -> bool:
     """Whether the fused decode routing entry point accepts this batch."""
-    return T <= 16
+    return T <= 64
 
 
 def zeroed_route_tiles_workspace(T: int, H: int, E: int, device) -> torch.Tensor:
-    """A workspace for moe_route_tiles whose ticket counter starts at zero."""
+    """A zeroed workspace for moe_route_tiles (it must start zero; every call
+    leaves its sync block and hand-off words zero)."""
     return torch.zeros(max(route_tiles_workspace_bytes(T, H, E), 256), dtype=torch.uint8,
                        device=device)
 

@@ -295,6 +295,101 @@ __global__ __launch_bounds__(kFusedThreads) void router_decode_fused(
   if (threadIdx.x == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// --------------------------------------------- fused routing, 17..64 tokens
+// moe_route_tiles for batches the single tail above serves slowly (one
+// workgroup running every token's top-k and the table): the work after the
+// partial logits is spread over the token blocks.
+//   routing  tb x ceil(eb/2) x splits workgroups of 512 threads (two
+//            16-expert blocks each) compute the partial logits of
+//            router_logits_partial and take a ticket of their 4-token block;
+//   top-k    the last routing workgroup of a token block sums that block's
+//            partials in split order and adds the bias (as
+//            router_topk_softmax does) and runs the same wave top-k and
+//            gating, one wave per token; it publishes the selected ids and
+//            takes a ticket of the call;
+//   tiles    the last token block reads every selected id and builds the
+//            table with the per-wave builder of tiles_block.h.
+// Partials and ids are written with agent-scope atomic stores, which are
+// coherent across the XCDs' L2 caches; each workgroup waits for their
+// completion before it takes a ticket, so a ticket's last holder sees all of
+// them (the single-tail kernel's ordering argument).  The tickets (ints 16..
+// of the workspace) are reset by their last holders, so they must be zero
+// before the first call and are zero after each.
+constexpr int kRelayThreads = 512;
+constexpr int kRelayMaxT = 64;
+constexpr int kRelayTicket0 = 16;  // first ticket int of the sync block
+
+__global__ __launch_bounds__(kRelayThreads) void route_tiles_relay(
+    const uint16_t* __restrict__ x, const float* __restrict__ w_router,
+    const float* __restrict__ bias, int T, int H, int E, int k, int gating, int BM,
+    int split_len, int splits, int* __restrict__ tickets, double* __restrict__ partial,
+    int* __restrict__ idw, int32_t* __restrict__ topk_ids, float* __restrict__ topk_weights,
+    double* __restrict__ logits, int32_t* __restrict__ expert_offsets,
+    int32_t* __restrict__ sorted_ids, int32_t* __restrict__ tiles,
+    int32_t* __restrict__ num_tiles) {
+  __shared__ __align__(16) long long s_rank[kWavesPerBlock][kRankScratch];
+  __shared__ int s_ids[kRelayMaxT * kMaxTopk];
+  __shared__ TilesScratch<kRelayThreads> S;
+  __shared__ int s_last;
+  const int tb = (T + kTokPerWave - 1) / kTokPerWave;
+  const int eb = (E + kExpPerBlock - 1) / kExpPerBlock;
+  const int ebp = (eb + 1) / 2;
+  const int wg = blockIdx.x;
+  const int bz = wg / (tb * ebp), rem = wg - bz * tb * ebp;
+  const int by = (rem / tb) * 2 + (threadIdx.x >> 8), bx = rem % tb;
+  if (by < eb)  // uniform per 256-thread half
+    logits_partial_body<true>(x, w_router, T, H, E, split_len, partial, bx, by, bz);
+  __builtin_amdgcn_s_waitcnt(0);  // this workgroup's partials are stored
+  __syncthreads();
+  if (threadIdx.x == 0) s_last = atomicAdd(&tickets[bx], 1) == ebp * splits - 1;
+  __syncthreads();
+  if (!s_last) return;  // uniform
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = bx * kTokPerWave + wave;
+  if (wave < kTokPerWave && t < T) {  // wave-uniform
+    double val[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = lane + kWave * i;
+      double v = 0.0;
+      if (e < E) {
+        double p[kFusedMaxSplits];
+#pragma unroll
+        for (int c = 0; c < kFusedMaxSplits; ++c)
+          p[c] = __hip_atomic_load(&partial[((size_t)min(c, splits - 1) * T + t) * E + e],
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int c = 0; c < kFusedMaxSplits; ++c)
+          if (c < splits) v += p[c];
+        if (bias) v += (double)bias[e];
+        if (logits) logits[(size_t)t * E + e] = v;
+      }
+      val[i] = v;
+    }
+    topk_softmax_wave(val, E, k, gating, t, topk_ids, topk_weights, s_ids, nullptr,
+                      s_rank[wave]);
+    wave_lds_sync();
+    if (lane < k)
+      __hip_atomic_store(&idw[t * k + lane], s_ids[t * k + lane], __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // this block's ids are stored
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    tickets[bx] = 0;  // the block's last holder resets its ticket
+    s_last = atomicAdd(&tickets[tb], 1) == tb - 1;
+  }
+  __syncthreads();
+  if (!s_last) return;  // uniform
+  const int N = T * k;
+  for (int p = threadIdx.x; p < N; p += kRelayThreads)
+    s_ids[p] = __hip_atomic_load(&idw[p], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  lds_barrier();
+  build_tiles_block<kRelayThreads>(static_cast<const int*>(s_ids), N, E, BM, S, expert_offsets,
+                                   sorted_ids, tiles, num_tiles);
+  if (threadIdx.x == 0) tickets[tb] = 0;
+}
+
 }  // namespace
 
 // Many tokens (enough 16-token workgroups to fill the chip), at most
@@ -341,12 +436,17 @@ void launch_router_logits(const uint16_t* x, const float* w_router, int T, int H
 bool router_fused_ok(int T, int E, int k) {
   (void)E;
   (void)k;
-  return T <= kFusedMaxT;
+  return T <= kRelayMaxT;
 }
 
+namespace {
+size_t round256(size_t n) { return (n + 255) & ~size_t(255); }
+}  // namespace
+
 size_t router_fused_bytes(int T, int H, int E) {
-  // 256-byte counter block, then the K-range partials
-  return 256 + router_partial_bytes(T, H, E);
+  // 256-byte block of ticket counters (int 0: the single tail's; ints 16..:
+  // the relay's), the K-range partials, the relay's selected ids
+  return 256 + round256(router_partial_bytes(T, H, E)) + round256((size_t)T * kMaxTopk * 4);
 }
 
 void launch_router_fused(const uint16_t* x, const float* w_router, const float* bias, int T,
@@ -359,6 +459,17 @@ void launch_router_fused(const uint16_t* x, const float* w_router, const float* 
   int* counter = static_cast<int*>(workspace);
   double* partial = reinterpret_cast<double*>(static_cast<char*>(workspace) + 256);
   const int eb = (E + kExpPerBlock - 1) / kExpPerBlock;
+  if (T > kFusedMaxT) {
+    const size_t pb = round256(router_partial_bytes(T, H, E));
+    int* idw = reinterpret_cast<int*>(static_cast<char*>(workspace) + 256 + pb);
+    const int tb = (T + kTokPerWave - 1) / kTokPerWave;
+    const int n_route = tb * ((eb + 1) / 2) * plan.splits;
+    hipLaunchKernelGGL(route_tiles_relay, dim3(n_route), dim3(kRelayThreads), 0, stream, x,
+                       w_router, bias, T, H, E, k, gating, BM, plan.split_len, plan.splits,
+                       counter + kRelayTicket0, partial, idw, topk_ids, topk_weights, logits,
+                       expert_offsets, sorted_ids, tiles, num_tiles);
+    return;
+  }
   dim3 grid((T + kTokPerWave - 1) / kTokPerWave, (eb + 3) / 4, plan.splits);
   hipLaunchKernelGGL(router_decode_fused, grid, dim3(kFusedThreads), 0, stream, x, w_router, bias,
                      T, H, E, k, gating, BM, plan.split_len, plan.splits, counter, partial,

@@ -112,9 +112,13 @@ class MoeLayer:
         self.BM = B.pick_bm(T, k, E) if BM is None else BM
         self.topk_ids = torch.empty((T, k), dtype=torch.int32, device=dev)
         self.topk_weights = torch.empty((T, k), dtype=torch.float32, device=dev)
-        # small batches route and tile in one launch (moe_route_tiles); its
-        # workspace must start zeroed, and every call leaves it that way
-        self.fused = B.route_tiles_ok(T, E, k)
+        # up to 16 tokens route and tile in one launch (moe_route_tiles: one
+        # workgroup); from 17 to 64 tokens that entry point relays between
+        # workgroups through tickets, which measured slower than the two
+        # separate launches (13.5 vs 11.5 us at 64 tokens), so the layer
+        # launches those.  The fused workspace must start zeroed, and every
+        # call leaves it that way.
+        self.fused = B.route_tiles_ok(T, E, k) and T <= B.ROUTE_TILES_ONE_WG_MAX_T
         ws = B.route_tiles_workspace_bytes(T, H, E) if self.fused else B.route_workspace_bytes(T, H, E)
         self.route_ws = torch.zeros(max(ws, 256), dtype=torch.uint8, device=dev)
         self.offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)

@@ -202,7 +202,7 @@ def _route_tiles(**kw):
 
 @pytest.mark.parametrize("kw,want", [
     (dict(x=None), NULL), (dict(tiles=None), NULL), (dict(ws=None), NULL), (dict(nt=None), NULL),
-    (dict(T=17, E=128), SHAPE), (dict(T=64, k=4, E=8), SHAPE), (dict(BM=8), SHAPE),
+    (dict(T=65, E=128), SHAPE), (dict(T=1000, k=4, E=8), SHAPE), (dict(BM=8), SHAPE),
     (dict(H=48), SHAPE), (dict(x=PMIS), ALIGN), (dict(wsb=16), WORKSPACE), (dict(T=0, x=None), OK),
     (dict(gating=7), SHAPE),
 ])
@@ -211,7 +211,7 @@ def test_route_tiles_validation(kw, want):
 
 
 def test_route_tiles_limits_and_workspace():
-    assert moe.route_tiles_ok(16, 256, 8) and not moe.route_tiles_ok(17, 8, 1)
+    assert moe.route_tiles_ok(64, 256, 8) and not moe.route_tiles_ok(65, 8, 1)
     assert moe.route_tiles_workspace_bytes(1, 2880, 32) >= 256 + moe.route_workspace_bytes(1, 2880, 32) - 256
 
 

@@ -1,9 +1,10 @@
 """GPU: the fused decode routing entry point (moe_route_tiles).
 
 Its outputs must be bit-identical to moe_route + moe_build_tiles and match
-the oracle (bit-exact ids and tables, weights within 1e-6); its ticket
-counter must return to zero after every call, so one workspace serves calls
-of different sizes in a row and under graph replay.
+the oracle (bit-exact ids and tables, weights within 1e-6) on both of its
+kernels (one tail workgroup up to 16 tokens; the token relay from 17 to 64);
+its sync block must return to zero after every call, so one workspace
+serves calls of different sizes in a row and under graph replay.
 """
 import numpy as np
 import pytest
@@ -36,9 +37,9 @@ def _workload(wid):
     return make_workload(wid, weights=False)
 
 
-def _random(T, H, E, k, bias, std, seed):
+def _random(T, H, E, k, bias, std, seed, gating="softmax"):
     from moe_inputs import make_activations
-    inp = dict(T=T, H=H, E=E, k=k, name=f"rand_T{T}_H{H}_E{E}_k{k}")
+    inp = dict(T=T, H=H, E=E, k=k, name=f"rand_T{T}_H{H}_E{E}_k{k}", gating=gating)
     inp.update(make_activations(T, H, E, [2000 + seed, 2], bias, std))
     return inp
 
@@ -51,6 +52,15 @@ CASES = {
     "T16_E8_k8": lambda: _random(16, 96, 8, 8, False, 0.5, 3),
     "T3_E256_k8": lambda: _random(3, 2880, 256, 8, True, 0.02, 4),
     "T16_E128_k4_H2880": lambda: _random(16, 2880, 128, 4, False, 0.02, 7),
+    # the token relay (17..64 tokens)
+    "T17_E32_k4": lambda: _random(17, 2880, 32, 4, False, 0.02, 9),
+    "20b_T64_biased": lambda: _workload(2),
+    "120b_T64": lambda: _workload(3),
+    "T33_E33_k3_bias": lambda: _random(33, 160, 33, 3, True, 0.3, 10),
+    "T64_E256_k8": lambda: _random(64, 2880, 256, 8, True, 0.02, 11),
+    "T40_E100_k4": lambda: _random(40, 512, 100, 4, False, 0.3, 12),
+    "T48_E24_k4_sigmoid": lambda: _random(48, 256, 24, 4, True, 0.3, 13, "sigmoid"),
+    "T64_E1_k1": lambda: _random(64, 64, 1, 1, False, 0.02, 14),
 }
 
 
@@ -59,11 +69,12 @@ def test_fused_equals_separate_and_oracle(name):
     inp = CASES[name]()
     T, E, k = inp["T"], inp["E"], inp["k"]
     BM = moe.pick_bm(T, k, E)
+    gating = inp.get("gating", "softmax")
     x, wr, b = _router_inputs(inp)
     log(f"route_tiles {name}: fused")
-    f = moe.moe_route_tiles(x, wr, b, k, BM, want_logits=True)
+    f = moe.moe_route_tiles(x, wr, b, k, BM, want_logits=True, gating=gating)
     log(f"route_tiles {name}: separate")
-    ids, wts, logits = moe.moe_route(x, wr, b, k, want_logits=True)
+    ids, wts, logits = moe.moe_route(x, wr, b, k, want_logits=True, gating=gating)
     off, srt, tiles, nt = moe.moe_build_tiles(ids, E, BM)
     torch.cuda.synchronize()
     n = int(nt.item())
@@ -71,7 +82,7 @@ def test_fused_equals_separate_and_oracle(name):
     for a, c in ((f[0], ids), (f[1], wts), (f[2], logits), (f[3], off), (f[4], srt),
                  (f[5][:n], tiles[:n])):
         assert torch.equal(a, c)
-    ref_ids, ref_w, _ = oracle.route(inp["x"], inp["w_router"], inp.get("bias"), k)
+    ref_ids, ref_w, _ = oracle.route(inp["x"], inp["w_router"], inp.get("bias"), k, gating)
     np.testing.assert_array_equal(f[0].cpu().numpy(), ref_ids)
     np.testing.assert_allclose(f[1].cpu().numpy(), ref_w, rtol=0, atol=1e-6)
     r_off, r_srt, r_tiles, r_n = oracle.build_tiles(ref_ids, E, BM)
@@ -82,10 +93,10 @@ def test_fused_equals_separate_and_oracle(name):
 
 
 def test_counter_returns_to_zero_across_sizes():
-    inp = _random(16, 256, 32, 4, True, 0.3, 5)
+    inp = _random(64, 256, 32, 4, True, 0.3, 5)
     x, wr, b = _router_inputs(inp)
-    ws = moe.zeroed_route_tiles_workspace(16, 256, 32, x.device)
-    for T in (1, 16, 3, 1, 11, 16):
+    ws = moe.zeroed_route_tiles_workspace(64, 256, 32, x.device)
+    for T in (1, 16, 3, 64, 1, 11, 17, 40, 16, 64, 33):
         log(f"counter reuse T={T}")
         xs = x[:T].contiguous()
         BM = moe.pick_bm(T, 4, 32)
@@ -167,7 +178,7 @@ def test_ties_on_every_routing_path(E, k):
         ids, wts, _ = moe.moe_route(x, wrd, None, k)
         np.testing.assert_array_equal(ids.cpu().numpy(), ref_ids)
         np.testing.assert_allclose(wts.cpu().numpy(), ref_w, rtol=0, atol=1e-6)
-        for T in (1, 5):
+        for T in (1, 5, 20):
             log(f"ties E={E} k={k} zero={zero}: moe_route_tiles at T={T}")
             f = moe.moe_route_tiles(x[:T].contiguous(), wrd, None, k, moe.pick_bm(T, k, E))
             np.testing.assert_array_equal(f[0].cpu().numpy(), ref_ids[:T])
