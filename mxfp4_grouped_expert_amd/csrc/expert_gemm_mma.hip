@@ -9,7 +9,8 @@
 // around the matrix cores and LDS.
 //
 // Unit of work: one workgroup of 8 waves takes a tile of up to 128 token
-// rows of one expert and 384 weight rows (4 slices of 96).  Waves w and w+4
+// rows of one expert (160 when it takes over the expert's remainder tile,
+// see the kernel) and 384 weight rows (4 slices of 96).  Waves w and w+4
 // (the two waves of one SIMD) share slice w & 3: each decodes all six 16-row
 // weight fragments of the slice and multiplies them against its own half of
 // the tile's token fragments (16 rows each; the first ceil(n/2) of the n
@@ -22,14 +23,14 @@
 //     neighbour hold the two halves of SwiGLU; 192 output columns per unit.
 //   down: a fragment is 16 rows of w2; 384 output columns per unit.
 //
-// K loop: 64 K per stage (two MX blocks), four stage buffers in LDS: the
+// K loop: 64 K per stage (two MX blocks), three stage buffers in LDS: the
 // stage being read and two in flight.  MFMA 16x16x32: lane group g supplies
 // K elements 32*(g>>1) + 16*(g&1) + 8j .. +8 of the stage for step j = 0, 1
 // (any K order works as long as both operands use it), so a lane's weight
 // operand is one 8-byte half of one MX block and its scale is one byte.  All loads in the
 // loop are direct global->LDS 16-byte loads (global_load_lds_dwordx4), a
 // fixed number per wave and stage, so a stage wait is an exact vmcnt:
-//   * activations: 64 or 128 rows x 128 B (as many as the tile needs),
+//   * activations: 64, 128 or 192 rows x 128 B (as many as the unit needs),
 //     gathered by a row table, row r's eight 16-byte chunks stored at
 //     chunk ^ ((r >> 1) & 7): a 128-bit read is served 16 lanes (one 256-byte
 //     bank row) at a time, and the 16 rows a fragment read touches then cover
@@ -52,11 +53,13 @@ namespace moe {
 
 namespace {
 
-constexpr int kMT = 128;                           // token rows per tile (largest BM)
+constexpr int kMT = 128;                           // token rows per tile (the tile table's BM)
+constexpr int kUnitRows = 160;                     // token rows per unit (a tile + remainder)
+constexpr int kXRows = 192;                        // activation rows staged (3 loads of 64)
 constexpr int kThreads = 512;                      // 8 waves, two per SIMD
 constexpr int kBK = 64;                            // K per stage: two MX blocks
-constexpr int kStages = 4;
-constexpr int kXStage = kMT * kBK * 2;             // 16 KB of bf16 activations
+constexpr int kStages = 3;
+constexpr int kXStage = kXRows * kBK * 2;          // 24 KB of bf16 activations
 constexpr int kWRowsSlice = 96;                    // weight rows staged per slice
 constexpr int kWSlice = kWRowsSlice * kBK / 2;     // 3 KB of e2m1 codes per slice
 constexpr int kWStage = 4 * kWSlice;
@@ -65,7 +68,7 @@ constexpr int kWLoadsSlice = kWSlice / 1024;       // direct loads per slice and
 constexpr int kMaxKB = 96;                         // K <= 3072
 constexpr int kSlabUnits = 5;                      // of kThreads pieces of 16 B
 constexpr int kSlabBytes = kSlabUnits * kThreads * 16;  // 40 KB of raw scale bytes
-constexpr int kLdsBytes = kStages * kStage + kSlabBytes + kMT * 8 + kMT * 4;
+constexpr int kLdsBytes = kStages * kStage + kSlabBytes + kXRows * 8 + kXRows * 4;
 constexpr int kNFW = 6;                            // weight fragments per wave
 constexpr int kColsGateUp = 48;                    // output columns per slice
 constexpr int kColsDown = 96;
@@ -160,9 +163,10 @@ __device__ __forceinline__ void lds_wait_all() { asm volatile("s_waitcnt lgkmcnt
 
 // K loop and epilogue of one wave: all kNFW weight fragments of slice wn
 // against NMW token fragments starting at tile row mrow0, with XCW
-// activation loads per wave and stage (1: rows 0..63 of the tile, 2: rows
-// 0..127).  NMW (0..4) and XCW are compile-time constants so the loop body
-// is straight-line code; a wave with NMW = 0 only loads and syncs.
+// activation loads per wave and stage (1: rows 0..63 of the unit, 2: rows
+// 0..127, 3: rows 0..191).  NMW (0..5) and XCW are compile-time constants so
+// the loop body is straight-line code; a wave with NMW = 0 only loads and
+// syncs.
 template <bool GATEUP, int NMW, int XCW>
 __device__ __forceinline__ void unit_main(const UnitCtx& c, int mrow0) {
   constexpr int NF = kNFW;
@@ -174,7 +178,7 @@ __device__ __forceinline__ void unit_main(const UnitCtx& c, int mrow0) {
   const int ww = 2 - c.mg;    // weight loads of this wave per stage
   const int niters = c.niters;
   // loads per stage of this wave: stages 0 and 1 are issued before the loop
-  // (their weights, and those of stages 2 and 3, came with the prologue);
+  // (their weights, and those of stage 2, came with the prologue);
   // stage s >= 2 is issued in iteration s - 2 with its weights.  Stages past
   // the last one are loaded too (clamped, in-bounds addresses, into a buffer
   // that is not read again), so the loop issues a fixed number of loads per
@@ -257,7 +261,7 @@ __device__ __forceinline__ void unit_main(const UnitCtx& c, int mrow0) {
   // load phase: all operands of stage `it`, decoded, in registers
   auto load_phase = [&](int it) {
     if (NMW > 0) {
-      const unsigned char* xs = c.smem + (it & (kStages - 1)) * kStage;
+      const unsigned char* xs = c.smem + (it % kStages) * kStage;
       uint2 wr[NF];
       uint32_t sr[NF];
       float sc[NF];
@@ -277,10 +281,10 @@ __device__ __forceinline__ void unit_main(const UnitCtx& c, int mrow0) {
     __builtin_amdgcn_sched_barrier(0);
   };
   // MFMA phase: stage `it`; this wave also issues its share of stage it+2,
-  // into the buffer of stage it-2 (read by both groups before the previous
-  // barrier)
+  // into the buffer of stage it-1 (group 0 read it two phases earlier, group
+  // 1 in the phase that ended at the previous barrier)
   auto mfma_phase = [&](int it) {
-    const int st = (it + 2) & (kStages - 1);
+    const int st = (it + 2) % kStages;
     issue_x(it + 2, st);
     issue_w(c, it + 2, st);
     if (NMW > 0) {
@@ -410,9 +414,27 @@ __global__ __launch_bounds__(kThreads, 1) void expert_mma_kernel(
 
   const int e = tiles[3 * tile + 0];
   const int r0 = tiles[3 * tile + 1];
-  const int rows = tiles[3 * tile + 2];
+  const int trows = tiles[3 * tile + 2];
   const long long nslots = (long long)T * k;
-  if (!tile_ok(e, r0, rows, E, nslots)) return;  // uniform
+  if (!tile_ok(e, r0, trows, E, nslots)) return;  // uniform
+  // An expert's rows past its last full tile (a remainder tile of at most
+  // kUnitRows - kMT rows) are computed by the unit of that full tile, so the
+  // expert's weights are staged and decoded once for all its rows: tile b is
+  // absorbed by tile a = b - 1 when both hold rows of one expert, b's rows
+  // continue a's, a is full and the two fit one unit.  (A full tile cannot
+  // itself be absorbed, so no chains form; both units test the same rows.)
+  auto absorbs = [&](int ea, int ra, int na, int eb, int rb, int nb) {
+    return ea == eb && ra + na == rb && na == kMT && na + nb <= kUnitRows &&
+           tile_ok(ea, ra, na, E, nslots) && tile_ok(eb, rb, nb, E, nslots);
+  };
+  const int ntl = units / ncb;  // whole tiles of the table (tile < ntl)
+  if (tile > 0 && absorbs(tiles[3 * tile - 3], tiles[3 * tile - 2], tiles[3 * tile - 1], e, r0,
+                          trows))
+    return;  // uniform: computed by the previous tile's unit
+  int rows = trows;
+  if (tile + 1 < ntl && absorbs(e, r0, trows, tiles[3 * tile + 3], tiles[3 * tile + 4],
+                                tiles[3 * tile + 5]))
+    rows += tiles[3 * tile + 5];
 
   UnitCtx c;
   c.smem = smem;
@@ -435,7 +457,7 @@ __global__ __launch_bounds__(kThreads, 1) void expert_mma_kernel(
 
   unsigned char* slab = smem + kStages * kStage;
   long long* s_rowoff = reinterpret_cast<long long*>(slab + kSlabBytes);
-  int* s_slot = reinterpret_cast<int*>(s_rowoff + kMT);
+  int* s_slot = reinterpret_cast<int*>(s_rowoff + kXRows);
   c.slab = slab;
   c.s_rowoff = s_rowoff;
   c.s_slot = s_slot;
@@ -502,10 +524,10 @@ __global__ __launch_bounds__(kThreads, 1) void expert_mma_kernel(
     c.w_dst[t] = c.wn * kWSlice + q * 1024;
   }
   c.w_pstride = wq_piece_stride(blocked);
-  for (int s = 0; s < 4 && s < c.niters; ++s) issue_w(c, s, s);
+  for (int s = 0; s < kStages && s < c.niters; ++s) issue_w(c, s, s);
 
   // ---- prologue 3: the row table
-  if (tid < kMT) {
+  if (tid < kXRows) {
     const int rr = min(tid, rows - 1);
     const int slot = sorted_ids[r0 + rr];
     s_rowoff[tid] = GATEUP ? (long long)min(max(slot / k, 0), T - 1) * H
@@ -545,7 +567,12 @@ __global__ __launch_bounds__(kThreads, 1) void expert_mma_kernel(
   const int nm0 = (nm + 1) >> 1;
   const int mine = c.mg ? nm - nm0 : nm0;  // wave-uniform
   const int mrow0 = c.mg ? 16 * nm0 : 0;
-  if (nm > 4) {
+  if (nm > 8) {
+    switch (mine) {
+      case 5: unit_main<GATEUP, 5, 3>(c, mrow0); break;
+      default: unit_main<GATEUP, 4, 3>(c, mrow0); break;
+    }
+  } else if (nm > 4) {
     switch (mine) {
       case 4: unit_main<GATEUP, 4, 2>(c, mrow0); break;
       case 3: unit_main<GATEUP, 3, 2>(c, mrow0); break;
