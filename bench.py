@@ -272,11 +272,14 @@ def measure(args) -> dict:
 
     mode = "hip_graph"
     graphs = []
+    # calls per graph: a multiple of the R weight copies and at least 8, so
+    # that one replay's fixed cost is spread over several calls
+    G = R * max(1, math.ceil(8 / R))
     if not args.no_graph:
         try:
-            graphs.append(capture(step, R))
-            if steps % R:
-                graphs.append(capture(step, steps % R))
+            graphs.append(capture(lambda r: step(r % R), G))
+            if steps % G:
+                graphs.append(capture(lambda r: step(r % R), steps % G))
         except Exception as exc:  # graph capture unavailable: time eagerly
             print(f"graph capture failed ({exc}); timing eager calls", file=sys.stderr)
             graphs = []
@@ -286,13 +289,13 @@ def measure(args) -> dict:
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     with torch.cuda.stream(stream):
         if graphs:
-            for _ in range(max(1, warmup // R)):
+            for _ in range(max(1, warmup // G)):
                 graphs[0].replay()
             torch.cuda.synchronize()
             start.record(stream)
-            for _ in range(steps // R):
+            for _ in range(steps // G):
                 graphs[0].replay()
-            if steps % R:
+            if steps % G:
                 graphs[1].replay()
             end.record(stream)
         else:
@@ -414,6 +417,7 @@ def measure(args) -> dict:
         "data": "synthetic (seeded MXFP4 layer of the workload's shape, no checkpoint)",
         "config": {"workload": inp["name"], "T": T, "H": H, "E": E, "k": k, "I": I, "BM": BM,
                    "experts_touched": n_touched, "weight_rotations": R, "timing": mode,
+                   "calls_per_graph": G if graphs else None,
                    "gating": inp["gating"], "weight_layout": args.layout,
                    "routing": ("moe_layer_one_token" if layer.one_launch else
                                "moe_route_tiles" if layer.fused else
