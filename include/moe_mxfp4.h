@@ -250,9 +250,9 @@ moe_status moe_forward(const uint16_t* x,
                        uint16_t* out, struct ihipStream_t* stream);
 
 /* ---------------------------------------------------- moe_forward_gptoss
- * moe_forward with the expert form of the released gpt-oss models, which
- * the SimpleLLM write-up runs from "the official MXFP4 checkpoints"
- * ("Correctness") but does not spell out; its definition here is the
+ * moe_forward with the expert form of the released gpt-oss models, whose
+ * MXFP4 checkpoints the SimpleLLM write-up runs unchanged ("Correctness")
+ * without spelling out their expert arithmetic; its definition here is the
  * released model's own (not on the pages):
  *   z = x[t] W13_e^T + b13[e]
  *   g = min(z_gate, limit), u = clip(z_up, -limit, limit)
