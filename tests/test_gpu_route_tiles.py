@@ -14,7 +14,7 @@ import mxfp4_grouped_expert_amd as moe
 import oracle
 from moe_inputs import make_random, make_workload
 
-from gpu_helpers import log
+from gpu_helpers import assert_out_close, log, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -51,6 +51,8 @@ CASES = {
     "T16_E33_k3_bias": lambda: _random(16, 160, 33, 3, True, 0.3, 2),
     "T16_E8_k8": lambda: _random(16, 96, 8, 8, False, 0.5, 3),
     "T3_E256_k8": lambda: _random(3, 2880, 256, 8, True, 0.02, 4),
+    "T2_E32_k4": lambda: _random(2, 2880, 32, 4, False, 0.02, 15),
+    "T5_E32_k4_bias": lambda: _random(5, 2880, 32, 4, True, 0.3, 16),
     "T16_E128_k4_H2880": lambda: _random(16, 2880, 128, 4, False, 0.02, 7),
     # the token relay (17..64 tokens)
     "T17_E32_k4": lambda: _random(17, 2880, 32, 4, False, 0.02, 9),
@@ -192,3 +194,30 @@ def test_ties_on_every_routing_path(E, k):
         torch.cuda.synchronize()
         np.testing.assert_array_equal(o[1].cpu().numpy(), ref_ids[:1])
         np.testing.assert_allclose(o[2].cpu().numpy(), ref_w[:1], rtol=0, atol=1e-6)
+
+
+@pytest.mark.parametrize("T", [2, 5, 16, 64])
+def test_layer_output_with_one_launch_routing(T):
+    """The whole layer with routing and tiles in one launch (moe_route_tiles:
+    one tail workgroup up to 16 tokens, the relay at 64) gives the same
+    output, bit for bit, as with moe_route + moe_build_tiles, and meets the
+    oracle bar."""
+    inp = make_random(T=T, H=512, E=32, k=4, I=512, seed=50 + T, router_bias=True,
+                      router_std=0.3)
+    d = to_device(inp)
+    k, E = inp["k"], inp["E"]
+    BM = moe.pick_bm(T, k, E)
+    log(f"layer with one-launch routing T={T}")
+    f = moe.moe_route_tiles(d["x"], d["w_router"], d["bias"], k, BM)
+    out_f = moe.moe_forward(d["x"], d["w13_q"], d["w13_s"], d["w2_q"], d["w2_s"], f[1], f[4],
+                            f[5], f[6], BM)
+    log(f"layer with separate routing launches T={T}")
+    ids, wts, _ = moe.moe_route(d["x"], d["w_router"], d["bias"], k)
+    off, srt, tiles, nt = moe.moe_build_tiles(ids, E, BM)
+    out_s = moe.moe_forward(d["x"], d["w13_q"], d["w13_s"], d["w2_q"], d["w2_s"], wts, srt,
+                            tiles, nt, BM)
+    torch.cuda.synchronize()
+    assert torch.equal(out_f.view(torch.int16), out_s.view(torch.int16))
+    log(f"layer with one-launch routing T={T}: oracle")
+    r = oracle.moe_layer(inp, BM=BM)
+    assert_out_close(out_f.float().cpu().numpy().astype(np.float64)[r["tokens"]], r["out"])
