@@ -17,7 +17,9 @@ in a process of its own, the median reported):
     T=4096) it starts `--runs` fresh child processes (`bench.py --child`),
     each of which measures the workload once and prints one JSON record; the
     record with the median µs/call is kept, with every run's value beside
-    it.  The headline child times exactly K steps after W warmup steps.
+    it.  The headline child times exactly K steps after W warmup steps (and,
+    before those, 0.1 s of untimed replays that bring the GPU's clocks to
+    their steady state).
   * within a child: HIP graphs, each holding one call per rotating weight
     copy, replayed back to back; exactly K steps between two events on the
     replay stream, synchronised on both sides.  R copies of the expert
@@ -56,6 +58,7 @@ BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 INFINITY_CACHE = 256 << 20
 GPTOSS_WORKLOADS = (1, 2, 3, 4)
 CHILD_TIMEOUT_S = 300
+BURN_IN_S = 0.1              # untimed replays before the warmup steps (see measure)
 
 
 def parse_args(argv=None):
@@ -285,6 +288,24 @@ def measure(args) -> dict:
             graphs = []
     if not graphs:
         mode = "eager"
+
+    # Burn-in: after idling, the GPU runs at lower clocks for the first few
+    # tens of milliseconds of sustained work (µs per call over consecutive
+    # 16-call windows from a cold start: 1,154, 1,035, then 1,000-1,007 at
+    # the 4k-token prefill; 18.6, then 18.15 at one token), so every run
+    # replays its workload for BURN_IN_S of wall time, untimed, before the W
+    # warmup steps, and the K timed steps measure the steady state that a
+    # serving loop runs in.
+    with torch.cuda.stream(stream):
+        t_burn = time.perf_counter()
+        i = 0
+        while time.perf_counter() - t_burn < BURN_IN_S:
+            if graphs:
+                graphs[0].replay()
+            else:
+                step(i % R)
+                i += 1
+            torch.cuda.synchronize()
 
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     with torch.cuda.stream(stream):
