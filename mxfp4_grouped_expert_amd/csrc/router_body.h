@@ -227,8 +227,13 @@ __device__ __forceinline__ double gate_term(double v, double m, int gating) {
 // argmax rounds' picks in selection order.  Every key is compared at once
 // (the keys are read from LDS in 16-byte pairs, branch-free), where the
 // rounds are k dependent chains of cross-lane steps: at E = 32, k = 4 the
-// selection measured about 2,700 cycles as rounds.  The softmax below it is
-// the same formula in the same order, so the weights are identical.
+// selection measured about 2,700 cycles as rounds.  With at most 32 experts
+// lanes l and l + 32 both rank expert l, each against half of the keys, and
+// add their counts (one cross-lane swap): the count is a serial chain of
+// 64-bit compares whose vector and scalar steps wait on each other (0.8 us
+// for 32 keys inside the one-token layer), and halving it halves that.
+// The softmax below it is the same formula in the same order, so the
+// weights are identical.
 constexpr int kRankScratch = kWave + 2 * kMaxTopk;  // keys, then (expert, value) by slot
 
 __device__ __forceinline__ void wave_lds_order() {
@@ -250,19 +255,39 @@ __device__ void topk_softmax_rank(double v0, int E, int k, int gating, int t,
   s_key[lane] = key;
   wave_lds_order();
   int rank = 0;
+  if (E <= kWave / 2) {  // uniform: two lanes per expert, 16 keys each
+    const int ex = lane & (kWave / 2 - 1);  // the expert this lane ranks
+    const int j0 = lane & (kWave / 2);      // its half of the keys: 0..15 or 16..31
+    const long long kx = s_key[ex];
+    int r = 0;
 #pragma unroll
-  for (int b = 0; b < kWave; b += 8) {
-    if (b >= E) break;  // uniform
-    long long o[8];
+    for (int b = 0; b < kWave / 4; b += 8) {
+      long long o[8];
 #pragma unroll
-    for (int q = 0; q < 8; q += 2) {
-      const longlong2 pr = *reinterpret_cast<const longlong2*>(s_key + b + q);
-      o[q] = pr.x;
-      o[q + 1] = pr.y;
+      for (int q = 0; q < 8; q += 2) {
+        const longlong2 pr = *reinterpret_cast<const longlong2*>(s_key + j0 / 2 + b + q);
+        o[q] = pr.x;
+        o[q + 1] = pr.y;
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) r += (o[q] > kx) | ((o[q] == kx) & (j0 / 2 + b + q < ex));
     }
+    rank = r + __shfl_xor(r, kWave / 2);
+  } else {
 #pragma unroll
-    for (int q = 0; q < 8; ++q)
-      rank += (o[q] > key) | ((o[q] == key) & (b + q < lane));
+    for (int b = 0; b < kWave; b += 8) {
+      if (b >= E) break;  // uniform
+      long long o[8];
+#pragma unroll
+      for (int q = 0; q < 8; q += 2) {
+        const longlong2 pr = *reinterpret_cast<const longlong2*>(s_key + b + q);
+        o[q] = pr.x;
+        o[q + 1] = pr.y;
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        rank += (o[q] > key) | ((o[q] == key) & (b + q < lane));
+    }
   }
   wave_lds_order();  // every key read before the slot table overwrites nothing of it
   if (lane < E && rank < k) {
