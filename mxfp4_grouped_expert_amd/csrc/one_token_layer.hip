@@ -250,18 +250,26 @@ __device__ __forceinline__ CallState read_call_state(const Sync* S) {
 
 // LDS of a workgroup's own routing: logits, the rank scratch of the wave
 // top-k, and the selected experts and weights in slot order.
+constexpr int kRankAllMaxE = 32;  // experts whose ranks the whole workgroup counts
+constexpr int kRankParts = kThreads / kRankAllMaxE;
 struct RouteLds {
   double logit[kMaxExperts];
   long long scratch[kRankScratch];
   int ids[kMaxTopk];
   float w[kMaxTopk];
+  int cnt[kRankAllMaxE][kRankParts];
 };
 
 // The token's logits from the published partials, by the whole workgroup
 // (barriers inside): wave w sums the partials of experts w*64 + lane in
 // split order and adds the bias, exactly as one_token_logits does, into
 // r->logit; then wave 0 runs the wave top-k, as moe_route_tiles does, and
-// the selected ids end in r->ids (slot order).
+// the selected ids end in r->ids (slot order).  With at most 32 experts the
+// whole workgroup counts the ranks instead (thread t: expert t % 32 against
+// keys 4*(t/32) .. +3; the eight counts of an expert are then added): the
+// same ranks as the wave top-k's rank count (the number of experts with a
+// larger order key, or an equal key and a lower index), so the same ids in
+// the same slots, with a serial compare chain of 4 instead of 16.
 __device__ void route_ids(const Args& a, const CallState& cs, RouteLds* r) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int e = lane + kWave * wave;
@@ -273,7 +281,26 @@ __device__ void route_ids(const Args& a, const CallState& cs, RouteLds* r) {
     r->logit[e] = sum;
   }
   __syncthreads();
-  if (wave == 0) {
+  if (a.E <= kRankAllMaxE) {  // uniform
+    const int t = threadIdx.x;
+    const int ex = t % kRankAllMaxE, part = t / kRankAllMaxE;
+    const long long kx = ex < a.E ? order_key(r->logit[ex]) : LLONG_MIN;
+    int c = 0;
+#pragma unroll
+    for (int q = 0; q < kRankAllMaxE / kRankParts; ++q) {
+      const int j = (kRankAllMaxE / kRankParts) * part + q;
+      const long long o = j < a.E ? order_key(r->logit[j]) : LLONG_MIN;
+      c += (o > kx) | ((o == kx) & (j < ex));
+    }
+    r->cnt[ex][part] = c;
+    __syncthreads();
+    if (t < a.E) {
+      int rank = 0;
+#pragma unroll
+      for (int p = 0; p < kRankParts; ++p) rank += r->cnt[t][p];
+      if (rank < a.k) r->ids[rank] = t;
+    }
+  } else if (wave == 0) {
     double val[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) val[i] = lane + kWave * i < a.E ? r->logit[lane + kWave * i] : 0.0;
