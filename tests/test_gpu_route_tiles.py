@@ -153,13 +153,15 @@ def test_fused_graph_replays():
         assert int(layer_ws[:256].count_nonzero().item()) == 0
 
 
-@pytest.mark.parametrize("E,k", [(40, 4), (64, 8), (100, 4)])
+@pytest.mark.parametrize("E,k", [(8, 2), (32, 4), (40, 4), (64, 8), (100, 4)])
 def test_ties_on_every_routing_path(E, k):
     """Equal logits go to the lower expert on every path that selects: the
     unfused top-k (T > 16), the fused launch (one and several tokens) and the
-    one-launch layer; at 40 and 64 experts the rank count runs, at 100 the
-    argmax rounds.  Rows of the router are duplicated in pairs, so every
-    logit has a twin, and an all-zero router ties everything."""
+    one-launch layer; up to 32 experts the rank count with two lanes per
+    expert runs (and the one-launch layer's publishers count with the whole
+    workgroup), at 40 and 64 experts the rank count with one lane per expert,
+    at 100 the argmax rounds.  Rows of the router are duplicated in pairs, so
+    every logit has a twin, and an all-zero router ties everything."""
     for zero in (False, True):
         inp = make_random(T=20, H=128, E=E, k=k, I=64, seed=E + k, router_std=0.5)
         wr = inp["w_router"]
