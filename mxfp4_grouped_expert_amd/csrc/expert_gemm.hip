@@ -546,7 +546,8 @@ __global__ __launch_bounds__(256 * kFuseMaxK) void down_combine_one_token_kernel
 
 // Rows of activations staged per pass, by the mean rows per expert
 // m = T*k/E: 4 below m = 2, 8 below m = 8, else 16 (with 16-row blocks per
-// workgroup: 1, 2 and 4 respectively, see the launcher); bounded by the
+// workgroup: 1, 2 and 4 respectively; the one-chunk down kernel takes 12
+// rows and 3 blocks in place of 16 and 4, see the launcher); bounded by the
 // tile's row bound (an expert gets at most one slot per token, so rows <=
 // min(BM, T), rounded up to a power of two) and small enough that the
 // staged rows fit in 96 KB (whole-K rows) or 100 KB (one chunk's K-range per
@@ -612,7 +613,19 @@ void launch_expert_gemm(const uint16_t* act, const uint8_t* wq, const uint8_t* w
     case 2: MOE_LAUNCH(1, 2); break;
     case 4: MOE_LAUNCH(1, 4); break;
     case 8: MOE_LAUNCH(2, 8); break;
-    default: MOE_LAUNCH(4, 16); break;
+    default:
+      // down with one K chunk: three blocks and 12-row passes, so that two
+      // 768-thread workgroups fit on a CU (registers and LDS) and one's
+      // weight stream overlaps the other's compute; bit-identical, and at
+      // 20b T = 64 under its biased router down 36.9 -> 35.2 us (gpt-oss-120b
+      // T = 512: layer 497 -> 490 us), where 4 x 8 (registers spill at 64),
+      // 2 x 8, 2 x 12, 2 x 16, 3 x 8, 3 x 10, 3 x 16 and 4 x 12 measured
+      // slower; gate/up (124 registers) keeps 4 x 16
+      if (!GATEUP && one_chunk)
+        MOE_LAUNCH(3, 12);
+      else
+        MOE_LAUNCH(4, 16);
+      break;
   }
 #undef MOE_LAUNCH
 }
