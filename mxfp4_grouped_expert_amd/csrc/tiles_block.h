@@ -17,6 +17,11 @@
 //      the wave's own running position in that expert;
 //   4. each tile index finds its expert by binary search over the tile
 //      offsets and writes (expert, row_start, rows).
+// Many slots (a prefill) split over several workgroups, each scattering one
+// contiguous range of slots: a workgroup also counts the slots before and
+// after its range per expert (order-free LDS adds over the ids, read from
+// L2), so it knows every expert's offset and its own first position in each
+// expert without hearing from the others, and the result is the same table.
 #pragma once
 
 #include "moe_device.h"
@@ -61,6 +66,17 @@ __device__ inline void wave_exclusive_scan(const int* in, int* out, int n, int l
   if (lane == kWave - 1) out[n] = incl;
 }
 
+// The part of the slots [0, N) one workgroup scatters: [q0, q1).  With
+// q0 > 0 or q1 < N, `before` and `after` are LDS arrays of kBuckets ints
+// for the counts outside the range; only the workgroup with `writer` set
+// stores expert_offsets, the tiles and num_tiles (identical in every one).
+struct TilesRange {
+  int q0, q1;
+  int* before;
+  int* after;
+  bool writer;
+};
+
 // Builds the table from ids[0..N) (any address space).  Every thread of the
 // NT-thread workgroup must call it; it ends with a barrier.  Phases exchange
 // data through LDS only, so the barriers do not wait for global stores.
@@ -76,35 +92,48 @@ template <int NT, typename IdPtr>
 __device__ void build_tiles_block(IdPtr ids, int N, int E, int BM, TilesScratch<NT>& S,
                                   int32_t* __restrict__ expert_offsets,
                                   int32_t* __restrict__ sorted_ids, int32_t* __restrict__ tiles,
-                                  int32_t* __restrict__ num_tiles) {
+                                  int32_t* __restrict__ num_tiles,
+                                  TilesRange R = TilesRange{0, -1, nullptr, nullptr, true}) {
   constexpr int kW = NT / kWave;
   static_assert(kW >= 2, "needs two waves for the scans");
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int NB = E + 1;  // buckets in use
-  const int L = ((N + kW - 1) / kW + kWave - 1) / kWave * kWave;  // slots per wave
-  const int p0 = wave * L;
-  const int p1 = min(N, p0 + L);
+  const int q0 = R.q0, q1 = R.q1 < 0 ? N : R.q1;
+  const bool split = q0 > 0 || q1 < N;  // uniform
+  const int L = ((q1 - q0 + kW - 1) / kW + kWave - 1) / kWave * kWave;  // slots per wave
+  const int p0 = q0 + wave * L;
+  const int p1 = min(q1, p0 + L);
   auto bucket = [&](int p) {
     const int e = ids[p];
     return (e < 0 || e >= E) ? E : e;
   };
 
   for (int i = tid; i < kW * NB; i += NT) S.wcnt[i / NB][i % NB] = 0;
+  if (split)
+    for (int i = tid; i < NB; i += NT) R.before[i] = R.after[i] = 0;
   lds_barrier();
 #pragma unroll 8
   for (int p = p0 + lane; p < p1; p += kWave) atomicAdd(&S.wcnt[wave][bucket(p)], 1);
+  if (split) {
+#pragma unroll 8
+    for (int p = tid; p < q0; p += NT) atomicAdd(&R.before[bucket(p)], 1);
+#pragma unroll 8
+    for (int p = q1 + tid; p < N; p += NT) atomicAdd(&R.after[bucket(p)], 1);
+  }
   lds_barrier();
   // per bucket: total, and each wave's first position relative to the
-  // bucket (exclusive scan over waves, in wave order)
+  // bucket (the slots before the range, then an exclusive scan over the
+  // waves, in wave order)
   for (int i = tid; i < NB; i += NT) {
-    int run = 0;
+    int run = split ? R.before[i] : 0;
     for (int w = 0; w < kW; ++w) {
       const int c = S.wcnt[w][i];
       S.wcnt[w][i] = run;
       run += c;
     }
+    if (split) run += R.after[i];
     S.cnt[i] = run;
     S.ntile[i] = (i < E) ? (run + BM - 1) / BM : 0;
   }
@@ -112,7 +141,8 @@ __device__ void build_tiles_block(IdPtr ids, int N, int E, int BM, TilesScratch<
   if (wave == 0) wave_exclusive_scan(S.cnt, S.off, NB, lane);
   if (wave == 1) wave_exclusive_scan(S.ntile, S.toff, NB, lane);
   lds_barrier();
-  for (int i = tid; i <= E; i += NT) expert_offsets[i] = S.off[i];
+  if (R.writer)
+    for (int i = tid; i <= E; i += NT) expert_offsets[i] = S.off[i];
 
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   constexpr int kBatch = 8;  // rounds whose ids are loaded together
@@ -149,7 +179,7 @@ __device__ void build_tiles_block(IdPtr ids, int N, int E, int BM, TilesScratch<
     }
   }
 
-  const int total = S.toff[E];
+  const int total = R.writer ? S.toff[E] : 0;
   for (int i = tid; i < total; i += NT) {
     int lo = 0, hi = E - 1;
     while (lo < hi) {
@@ -161,7 +191,7 @@ __device__ void build_tiles_block(IdPtr ids, int N, int E, int BM, TilesScratch<
     tiles[3 * i + 1] = S.off[lo] + j * BM;
     tiles[3 * i + 2] = min(BM, S.cnt[lo] - j * BM);
   }
-  if (tid == 0) num_tiles[0] = total;
+  if (tid == 0 && R.writer) num_tiles[0] = total;
   lds_barrier();
 }
 

@@ -190,6 +190,30 @@ def test_tile_table_all_bm_at_prefill(w120b, BM):
     np.testing.assert_array_equal(tiles[:n].cpu().numpy(), ref[2])
 
 
+# Many slots: the table is built by several workgroups, each scattering one
+# range of the slots (the 16,384-slot prefill above takes 8 of them).  A
+# slot count whose last range is short (100,008 slots, 49 ranges), one whose
+# last workgroup gets no slots at all (160,000 slots over 64 workgroups of
+# 2,560), the smallest split (4,097 slots, 3 ranges), skewed expert loads,
+# and the largest expert count and top-k.
+@pytest.mark.parametrize("T,k,E,BM", [(12_501, 8, 256, 128), (40_000, 4, 128, 64),
+                                      (4_097, 1, 3, 16)])
+def test_tile_table_many_slots(T, k, E, BM):
+    rng = np.random.default_rng(T + E)
+    keys = rng.random((T, E)) + np.linspace(0.0, 0.6, E)[None, :]  # skewed toward high ids
+    ids_np = np.argsort(-keys, axis=1, kind="stable")[:, :k].astype(np.int32)
+    log(f"tile table T={T} k={k} E={E} BM={BM} ({T * k} slots)")
+    ids = torch.from_numpy(ids_np).cuda()
+    off, srt, tiles, nt = moe.moe_build_tiles(ids, E, BM)
+    torch.cuda.synchronize()
+    ref = oracle.build_tiles(ids_np, E, BM)
+    n = int(nt.item())
+    assert n == ref[3]
+    np.testing.assert_array_equal(off.cpu().numpy(), ref[0])
+    np.testing.assert_array_equal(srt.cpu().numpy(), ref[1])
+    np.testing.assert_array_equal(tiles[:n].cpu().numpy(), ref[2])
+
+
 # ------------------------------------------------------ random / ragged --
 
 RANDOM_CASES = [
