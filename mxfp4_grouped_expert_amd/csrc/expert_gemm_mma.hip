@@ -161,15 +161,16 @@ __device__ __forceinline__ void issue_w(const UnitCtx& c, int it, int st) {
 
 __device__ __forceinline__ void lds_wait_all() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-// K loop and epilogue of one wave: all kNFW weight fragments of slice wn
-// against NMW token fragments starting at tile row mrow0, with XCW
-// activation loads per wave and stage (1: rows 0..63 of the unit, 2: rows
-// 0..127, 3: rows 0..191).  NMW (0..5) and XCW are compile-time constants so
-// the loop body is straight-line code; a wave with NMW = 0 only loads and
-// syncs.
-template <bool GATEUP, int NMW, int XCW>
+// K loop and epilogue of one wave: the first NF weight fragments of slice
+// wn (all kNFW, or 3 in a down unit whose columns end within the first three
+// fragments of every slice) against NMW token fragments starting at tile row
+// mrow0, with XCW activation loads per wave and stage (1: rows 0..63 of the
+// unit, 2: rows 0..127, 3: rows 0..191).  NMW (0..5), XCW and NF are
+// compile-time constants so the loop body is straight-line code; a wave with
+// NMW = 0 only loads and syncs.
+template <bool GATEUP, int NMW, int XCW, int NF = kNFW>
 __device__ __forceinline__ void unit_main(const UnitCtx& c, int mrow0) {
-  constexpr int NF = kNFW;
+  static_assert(NF == kNFW || (!GATEUP && NF == 3), "short units: down only");
   constexpr int NA = NMW > 0 ? NMW : 1;  // array extent
   const int li = c.lane & 15;
   const int grp = c.lane >> 4;
@@ -331,7 +332,7 @@ __device__ __forceinline__ void unit_main(const UnitCtx& c, int mrow0) {
 
   // epilogue straight from the accumulators: the lane holds D[4*grp + r][li]
   // of each (token fragment, weight fragment)
-  const int cbase = c.n0 + (GATEUP ? kColsGateUp : kColsDown) * c.wn;
+  const int cbase = c.n0 + kColsGateUp * c.wn;  // gate/up: the slice's 48 columns
   if (GATEUP) {
     // A lane pair (even: gate, odd: up, of column cbase + 8*f + li/2) swaps
     // half of its rows, so that the even lane finishes rows 0, 1 of its four
@@ -380,7 +381,7 @@ __device__ __forceinline__ void unit_main(const UnitCtx& c, int mrow0) {
         if (p < 0 || p >= c.nslots) continue;
 #pragma unroll
         for (int f = 0; f < NF; ++f) {
-          const int col = cbase + 16 * f + li;
+          const int col = c.n0 + 16 * (4 * f + c.wn) + li;  // fragment f of slice wn
           if (col < c.N) {
             const float bias =
                 c.fn.kind != 0 && c.fn.b2 ? c.fn.b2[(size_t)c.e * c.H + col] : 0.f;
@@ -463,7 +464,10 @@ __global__ __launch_bounds__(kThreads, 1) void expert_mma_kernel(
   c.s_slot = s_slot;
 
   // rows of one expert's weight matrix (2I for gate/up, H for down), and the
-  // rows of one run's half (I or H)
+  // rows of one run's half (I or H).  Down: fragment f of slice wn is the
+  // unit's 16-column group 4f + wn, so that a unit whose columns end early
+  // (the last of 2880 = 7.5 x 384) spreads its valid groups over all four
+  // SIMDs and runs short (NF = 3) instead of leaving two SIMDs idle.
   const int mrows = GATEUP ? 2 * I : H;
   const int nvalid = GATEUP ? I : H;
   // slice row rl (0..95) of slice wn -> run (0: gate or w2, 1: up) and run row
@@ -474,7 +478,7 @@ __global__ __launch_bounds__(kThreads, 1) void expert_mma_kernel(
       rr = kCols * wn + 8 * f + (l >> 1);
     } else {
       ch = 0;
-      rr = kCols * wn + 16 * f + l;
+      rr = 16 * (4 * f + wn) + l;
     }
   };
 
@@ -567,6 +571,29 @@ __global__ __launch_bounds__(kThreads, 1) void expert_mma_kernel(
   const int nm0 = (nm + 1) >> 1;
   const int mine = c.mg ? nm - nm0 : nm0;  // wave-uniform
   const int mrow0 = c.mg ? 16 * nm0 : 0;
+  if constexpr (!GATEUP) {
+    if (c.N - c.n0 <= 3 * 4 * 16) {  // uniform: every slice's valid fragments are its first 3
+      if (nm > 8) {
+        switch (mine) {
+          case 5: unit_main<false, 5, 3, 3>(c, mrow0); break;
+          default: unit_main<false, 4, 3, 3>(c, mrow0); break;
+        }
+      } else if (nm > 4) {
+        switch (mine) {
+          case 4: unit_main<false, 4, 2, 3>(c, mrow0); break;
+          case 3: unit_main<false, 3, 2, 3>(c, mrow0); break;
+          default: unit_main<false, 2, 2, 3>(c, mrow0); break;
+        }
+      } else {
+        switch (mine) {
+          case 2: unit_main<false, 2, 1, 3>(c, mrow0); break;
+          case 1: unit_main<false, 1, 1, 3>(c, mrow0); break;
+          default: unit_main<false, 0, 1, 3>(c, mrow0); break;
+        }
+      }
+      return;
+    }
+  }
   if (nm > 8) {
     switch (mine) {
       case 5: unit_main<GATEUP, 5, 3>(c, mrow0); break;
