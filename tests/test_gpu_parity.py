@@ -214,6 +214,35 @@ def test_tile_table_many_slots(T, k, E, BM):
     np.testing.assert_array_equal(tiles[:n].cpu().numpy(), ref[2])
 
 
+# Ids outside [0, E) are dropped from the counts and tiles and their slots
+# placed after expert_offsets[E] (the library's contract for a corrupted
+# routing; the method itself never produces them).  One case per builder:
+# all-pairs (<= 128 slots), one workgroup, and the scatter split over
+# workgroups.  Expected values: counts of the valid ids, a stable argsort of
+# the bucket (invalid ids last), and the oracle's tiles of the valid ids.
+@pytest.mark.parametrize("T,k,E,BM", [(50, 2, 8, 16), (300, 4, 32, 64), (2_500, 4, 128, 128)])
+def test_tile_table_drops_out_of_range_ids(T, k, E, BM):
+    rng = np.random.default_rng(7 * T + E)
+    ids_np = rng.integers(0, E, (T, k)).astype(np.int32)
+    bad = rng.random((T, k)) < 0.05
+    ids_np[bad] = rng.choice(np.array([-1, E, E + 7, -1000], dtype=np.int32), int(bad.sum()))
+    log(f"tile table with {int(bad.sum())} out-of-range ids, {T * k} slots")
+    ids = torch.from_numpy(ids_np).cuda()
+    off, srt, tiles, nt = moe.moe_build_tiles(ids, E, BM)
+    torch.cuda.synchronize()
+    flat = ids_np.ravel()
+    valid = (flat >= 0) & (flat < E)
+    nv = int(valid.sum())
+    want_off = np.concatenate([[0], np.cumsum(np.bincount(flat[valid], minlength=E))])
+    np.testing.assert_array_equal(off.cpu().numpy(), want_off)
+    bucket = np.where(valid, flat, E)
+    np.testing.assert_array_equal(srt.cpu().numpy(), np.argsort(bucket, kind="stable"))
+    ref = oracle.build_tiles(flat[valid], E, BM)
+    n = int(nt.item())
+    assert n == ref[3] and want_off[E] == nv
+    np.testing.assert_array_equal(tiles[:n].cpu().numpy(), ref[2])
+
+
 # ------------------------------------------------------ random / ragged --
 
 RANDOM_CASES = [
