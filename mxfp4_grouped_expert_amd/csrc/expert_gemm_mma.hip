@@ -21,7 +21,9 @@
 //   gate/up: a fragment holds 8 output columns, gate and up rows interleaved
 //     (even row: gate, odd row: up, of the same column), so a lane and its
 //     neighbour hold the two halves of SwiGLU; 192 output columns per unit.
-//   down: a fragment is 16 rows of w2; 384 output columns per unit.
+//   down: a fragment is 16 rows of w2, fragment f of slice s being the
+//     unit's 16-row group 4f + s; 384 output columns per unit (a unit whose
+//     columns end within the first 192 runs three fragments per wave).
 //
 // K loop: 64 K per stage (two MX blocks), three stage buffers in LDS: the
 // stage being read and two in flight.  MFMA 16x16x32: lane group g supplies
