@@ -102,6 +102,13 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Waits until this wave's LDS writes have completed, so its later reads (of
+// other lanes' entries) see them; the memory clobber keeps the compiler from
+// moving LDS accesses across.
+__device__ __forceinline__ void wave_lds_sync() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
 // Layouts of a packed MXFP4 code matrix (K/2 bytes per weight row, one
 // 16-byte piece per 32-element MX block).  Canonical: row-major.  Blocked:
 // within each group of 16 consecutive rows the pieces are stored block by

@@ -262,7 +262,7 @@ struct RouteLds {
 
 // The token's logits from the published partials, by the whole workgroup
 // (barriers inside): wave w sums the partials of experts w*64 + lane in
-// split order and adds the bias, exactly as one_token_logits does, into
+// split order and adds the bias, exactly as token_logits does, into
 // r->logit; then wave 0 runs the wave top-k, as moe_route_tiles does, and
 // the selected ids end in r->ids (slot order).  With at most 32 experts the
 // whole workgroup counts the ranks instead (thread t: expert t % 32 against

@@ -172,7 +172,6 @@ __global__ __launch_bounds__(256) void router_topk_softmax(
 // resets it to zero, so the counter must be zero before the first call.
 constexpr int kFusedThreads = 1024;  // 16 waves: one token per wave in the tail
 constexpr int kFusedMaxT = 16;
-constexpr int kFusedMaxTE = kFusedMaxT * kMaxExperts;  // logits staged in LDS as fp64
 constexpr int kFusedMaxSlots = kFusedMaxT * kMaxTopk;
 
 __global__ __launch_bounds__(kFusedThreads) void router_decode_fused(
@@ -183,13 +182,9 @@ __global__ __launch_bounds__(kFusedThreads) void router_decode_fused(
     double* __restrict__ logits, int32_t* __restrict__ expert_offsets,
     int32_t* __restrict__ sorted_ids, int32_t* __restrict__ tiles,
     int32_t* __restrict__ num_tiles) {
-  __shared__ double s_logits[kFusedMaxTE];
+  __shared__ __align__(16) long long s_rank[kFusedThreads / kWave][kRankScratch];
   __shared__ int s_ids[kFusedMaxSlots];
-  __shared__ __align__(16) long long s_key[kFusedMaxTE];
-  __shared__ int s_sel_e[kFusedMaxSlots];
-  __shared__ double s_sel_v[kFusedMaxSlots];
-  __shared__ double s_z[kFusedMaxSlots];
-  __shared__ TilesScratch<kFusedThreads> S;
+  __shared__ int s_tab[kWaveTablesScratch];
   __shared__ int s_last;
 
   // Partials are written with agent-scope atomic stores, which are coherent
@@ -210,88 +205,36 @@ __global__ __launch_bounds__(kFusedThreads) void router_decode_fused(
   if (threadIdx.x == 0) s_last = (atomicAdd(counter, 1) == nwg - 1);
   __syncthreads();
   if (!s_last) return;  // uniform over the workgroup
+  // The tail: wave t sums token t's partials and runs its top-k and gating
+  // with the unfused path's wave code (router_topk_softmax), so ids and
+  // weights are identical to moe_route's; then one wave builds the table.
+  const int wave = threadIdx.x >> 6;
   if (T == 1) {  // uniform: one wave finishes a single token, no barriers
-    if (threadIdx.x < kWave) {
+    if (wave == 0) {
       double val[4];
-      one_token_logits(partial, bias, E, splits, val);
+      token_logits(partial, bias, 1, 0, E, splits, val);
       tail_one_token(val, E, k, gating, topk_ids, topk_weights, logits, s_ids, expert_offsets,
-                     sorted_ids, tiles, num_tiles, nullptr, s_key);
+                     sorted_ids, tiles, num_tiles, nullptr, s_rank[0]);
       if (threadIdx.x == 0)
         __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     return;
   }
-
-  // fixed-order sum of the K-range partials (+ bias); all loads independent
-  const int TE = T * E;
-  for (int i = threadIdx.x; i < TE; i += kFusedThreads) {
-    const int t = i / E;
-    const int e = i - t * E;
-    // every K-range partial of the entry in flight at once, summed in order
-    double p[kFusedMaxSplits];
+  if (wave < T) {  // wave-uniform
+    double val[4];
+    token_logits(partial, bias, T, wave, E, splits, val);
+    if (logits)
 #pragma unroll
-    for (int c = 0; c < kFusedMaxSplits; ++c) {
-      const int sc = min(c, splits - 1);  // in bounds; surplus terms dropped below
-      p[c] = __hip_atomic_load(&partial[((size_t)sc * T + t) * E + e], __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-    }
-    double v = 0.0;
-#pragma unroll
-    for (int c = 0; c < kFusedMaxSplits; ++c)
-      if (c < splits) v += p[c];
-    if (bias) v += (double)bias[e];
-    s_logits[i] = v;
-    if (logits) logits[i] = v;
-  }
-  // top-k by rank: an entry's rank is the number of its token's experts
-  // with a larger order key, or an equal one and a lower index (the order of
-  // the k argmax rounds of the unfused path), so ranks < k are the picks in
-  // selection order
-  for (int i = threadIdx.x; i < TE; i += kFusedThreads) s_key[i] = order_key(s_logits[i]);
-  lds_barrier();
-  for (int i = threadIdx.x; i < TE; i += kFusedThreads) {
-    const int t = i / E;
-    const int e = i - t * E;
-    const long long ki = s_key[i];
-    const long long* kt = s_key + t * E;
-    int rank = 0;
-#pragma unroll 8
-    for (int j = 0; j < E; ++j) {
-      const long long kj = kt[j];
-      rank += (kj > ki) | ((kj == ki) & (j < e));
-    }
-    if (rank < k) {
-      s_sel_e[t * kMaxTopk + rank] = e;
-      s_sel_v[t * kMaxTopk + rank] = s_logits[i];
-    }
+      for (int i = 0; i < 4; ++i) {
+        const int e = (threadIdx.x & (kWave - 1)) + kWave * i;
+        if (e < E) logits[(size_t)wave * E + e] = val[i];
+      }
+    topk_softmax_wave(val, E, k, gating, wave, topk_ids, topk_weights, s_ids, nullptr,
+                      s_rank[wave]);
   }
   lds_barrier();
-  // softmax: the k exponentials of a token in parallel, then each of its
-  // threads sums them in ascending j, the order of topk_softmax_wave, so the
-  // weights are bit-identical to the unfused path
-  for (int i = threadIdx.x; i < T * k; i += kFusedThreads) {
-    const int t = i / k;
-    const int j = i - t * k;
-    const double* v = s_sel_v + t * kMaxTopk;
-    double m = v[0];
-    for (int q = 1; q < k; ++q) m = fmax(m, v[q]);
-    s_z[t * kMaxTopk + j] = gate_term(v[j], m, gating);
-  }
-  lds_barrier();
-  for (int i = threadIdx.x; i < T * k; i += kFusedThreads) {
-    const int t = i / k;
-    const int j = i - t * k;
-    const double* z = s_z + t * kMaxTopk;
-    double sum = 0.0;
-    for (int q = 0; q < k; ++q) sum += z[q];
-    const int e = s_sel_e[t * kMaxTopk + j];
-    topk_ids[(size_t)t * k + j] = e;
-    topk_weights[(size_t)t * k + j] = (float)(z[j] / sum);
-    s_ids[t * k + j] = e;
-  }
-  lds_barrier();
-  build_tiles_small<kFusedThreads>(static_cast<const int*>(s_ids), T * k, E, BM, S,
-                                   expert_offsets, sorted_ids, tiles, num_tiles);
+  if (wave != 0) return;
+  build_tiles_wave(s_ids, T * k, E, BM, s_tab, expert_offsets, sorted_ids, tiles, num_tiles);
   if (threadIdx.x == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 

@@ -164,13 +164,6 @@ __device__ __forceinline__ long long readlane_i64(long long v, int l) {
   return ((long long)hi << 32) | (unsigned int)lo;
 }
 
-// Waits until this wave's LDS writes have completed, so its later reads (of
-// other lanes' entries) see them; the memory clobber keeps the compiler from
-// moving LDS accesses across.
-__device__ __forceinline__ void wave_lds_sync() {
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-}
-
 // max(v, v of the lane DPP control CTRL selects); lanes without a source
 // keep v
 template <int CTRL>
@@ -410,12 +403,13 @@ __device__ void topk_softmax_wave(const double (&val)[4], int E, int k, int gati
 // Most K-ranges a one-token logit is summed over.
 constexpr int kFusedMaxSplits = 32;
 
-// The logits of a single token, lane l holding experts l, l+64, ...: the
-// K-range partials (agent-scope atomic loads, all in flight at once) summed
-// in order plus the bias, as router_topk_softmax sums them.
-[[maybe_unused]] __device__ void one_token_logits(const double* __restrict__ partial,
-                                 const float* __restrict__ bias, int E, int splits,
-                                 double (&val)[4]) {
+// The logits of token t of T, lane l holding experts l, l+64, ...: the
+// K-range partials ([split][token][expert], agent-scope atomic loads, all in
+// flight at once) summed in order plus the bias, as router_topk_softmax sums
+// them.
+[[maybe_unused]] __device__ void token_logits(const double* __restrict__ partial,
+                                              const float* __restrict__ bias, int T, int t,
+                                              int E, int splits, double (&val)[4]) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -424,10 +418,10 @@ constexpr int kFusedMaxSplits = 32;
     if (e < E) {
       double p[kFusedMaxSplits];
 #pragma unroll
-      for (int c = 0; c < kFusedMaxSplits; ++c) {
-        p[c] = __hip_atomic_load(&partial[(size_t)min(c, splits - 1) * E + e], __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_AGENT);
-      }
+      for (int c = 0; c < kFusedMaxSplits; ++c)
+        if (c < splits)  // uniform
+          p[c] = __hip_atomic_load(&partial[((size_t)c * T + t) * E + e], __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
       for (int c = 0; c < kFusedMaxSplits; ++c)
         if (c < splits) v += p[c];

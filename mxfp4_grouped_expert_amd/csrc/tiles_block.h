@@ -260,4 +260,87 @@ __device__ void build_tiles_small(const int* ids, int N, int E, int BM, TilesScr
   lds_barrier();
 }
 
+// The same table for at most 128 slots, built by one wave with no barrier
+// (the fused decode router's tail): lane l owns slots l and l + 64.  Slots
+// of one bucket find each other with nine ballots (one per bucket bit) per
+// half; the first slot of a bucket stores the bucket's count, and two
+// exclusive scans over the E + 1 buckets give the row offsets and the tile
+// offsets.  Every quantity is a count over the ids, so the table equals
+// build_tiles_small's.  scratch: >= kWaveTablesScratch ints of LDS private
+// to the wave.
+constexpr int kWaveTablesScratch = 4 * (kBuckets + 1);
+__device__ inline void build_tiles_wave(const int* ids, int N, int E, int BM, int* scratch,
+                                        int32_t* __restrict__ expert_offsets,
+                                        int32_t* __restrict__ sorted_ids,
+                                        int32_t* __restrict__ tiles,
+                                        int32_t* __restrict__ num_tiles) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int* cnt = scratch;                 // [E + 1] slots per bucket
+  int* off = cnt + kBuckets;          // [E + 2] exclusive scan of cnt
+  int* nt = off + kBuckets + 1;       // [E + 1] tiles per bucket
+  int* toff = nt + kBuckets;          // [E + 2] exclusive scan of nt
+  for (int e = lane; e <= E; e += kWave) cnt[e] = 0;
+  const int halves = N > kWave ? 2 : 1;  // uniform
+  int b[2];
+  uint64_t valid[2], bal[2][9];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int p = lane + kWave * s;
+    const bool v = p < N;
+    b[s] = 0;
+    if (v) {
+      const int e = ids[p];
+      b[s] = (e < 0 || e >= E) ? E : e;
+    }
+    valid[s] = __ballot(v);
+#pragma unroll
+    for (int i = 0; i < 9; ++i) bal[s][i] = __ballot(v && ((b[s] >> i) & 1));
+  }
+  // same-bucket masks of slot (s, lane) within half h
+  int before[2], same[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    uint64_t m[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      m[h] = valid[h];
+#pragma unroll
+      for (int i = 0; i < 9; ++i) m[h] &= ((b[s] >> i) & 1) ? bal[h][i] : ~bal[h][i];
+    }
+    same[s] = __popcll(m[0]) + __popcll(m[1]);
+    before[s] = s == 0 ? lanes_below(m[0]) : __popcll(m[0]) + lanes_below(m[1]);
+    if (s + 1 >= halves) {  // uniform: no second half
+      if (s == 0) { same[1] = 0; before[1] = 1; }
+      break;
+    }
+  }
+  wave_lds_sync();  // the zeroed counts before the first slots' stores
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+    if (((valid[s] >> lane) & 1) && before[s] == 0) cnt[b[s]] = same[s];
+  wave_lds_sync();
+  wave_exclusive_scan(cnt, off, E + 1, lane);
+  for (int e = lane; e <= E; e += kWave) nt[e] = e < E ? (cnt[e] + BM - 1) / BM : 0;
+  wave_lds_sync();
+  wave_exclusive_scan(nt, toff, E + 1, lane);
+  wave_lds_sync();
+  for (int e = lane; e <= E; e += kWave) expert_offsets[e] = off[e];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    if (!((valid[s] >> lane) & 1)) continue;
+    const int o = off[b[s]];
+    sorted_ids[o + before[s]] = lane + kWave * s;
+    if (before[s] == 0 && b[s] < E) {
+      const int t0 = toff[b[s]];
+      const int n = (same[s] + BM - 1) / BM;
+      for (int j = 0; j < n; ++j) {
+        tiles[3 * (t0 + j) + 0] = b[s];
+        tiles[3 * (t0 + j) + 1] = o + j * BM;
+        tiles[3 * (t0 + j) + 2] = min(BM, same[s] - j * BM);
+      }
+    }
+  }
+  if (lane == 0) num_tiles[0] = toff[E];
+}
+
 }  // namespace moe
