@@ -212,7 +212,7 @@ __global__ __launch_bounds__(kFusedThreads) void router_decode_fused(
   if (T == 1) {  // uniform: one wave finishes a single token, no barriers
     if (wave == 0) {
       double val[4];
-      token_logits(partial, bias, 1, 0, E, splits, val);
+      token_logits<true>(partial, bias, 1, 0, E, splits, val);
       tail_one_token(val, E, k, gating, topk_ids, topk_weights, logits, s_ids, expert_offsets,
                      sorted_ids, tiles, num_tiles, nullptr, s_rank[0]);
       if (threadIdx.x == 0)
@@ -222,7 +222,7 @@ __global__ __launch_bounds__(kFusedThreads) void router_decode_fused(
   }
   if (wave < T) {  // wave-uniform
     double val[4];
-    token_logits(partial, bias, T, wave, E, splits, val);
+    token_logits<false>(partial, bias, T, wave, E, splits, val);
     if (logits)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {

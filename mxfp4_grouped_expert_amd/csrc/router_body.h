@@ -406,10 +406,13 @@ constexpr int kFusedMaxSplits = 32;
 // The logits of token t of T, lane l holding experts l, l+64, ...: the
 // K-range partials ([split][token][expert], agent-scope atomic loads, all in
 // flight at once) summed in order plus the bias, as router_topk_softmax sums
-// them.
-[[maybe_unused]] __device__ void token_logits(const double* __restrict__ partial,
-                                              const float* __restrict__ bias, int T, int t,
-                                              int E, int splits, double (&val)[4]) {
+// them.  ALL_LOADS issues kFusedMaxSplits loads branch-free (the surplus ones
+// at the last K-range's address, unused), which measured faster for a single
+// token; otherwise only the K-ranges that exist are loaded, which halves a
+// multi-token tail's load count.
+template <bool ALL_LOADS>
+__device__ void token_logits(const double* __restrict__ partial, const float* __restrict__ bias,
+                             int T, int t, int E, int splits, double (&val)[4]) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -419,9 +422,9 @@ constexpr int kFusedMaxSplits = 32;
       double p[kFusedMaxSplits];
 #pragma unroll
       for (int c = 0; c < kFusedMaxSplits; ++c)
-        if (c < splits)  // uniform
-          p[c] = __hip_atomic_load(&partial[((size_t)c * T + t) * E + e], __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
+        if (ALL_LOADS || c < splits)  // uniform
+          p[c] = __hip_atomic_load(&partial[((size_t)min(c, splits - 1) * T + t) * E + e],
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
       for (int c = 0; c < kFusedMaxSplits; ++c)
         if (c < splits) v += p[c];
