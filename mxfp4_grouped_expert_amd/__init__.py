@@ -11,7 +11,9 @@ from .binding import (MoeError, LIB_PATH, load, version, status_string, pick_bm,
                       moe_route_tiles, route_tiles_ok, route_tiles_workspace_bytes,
                       zeroed_route_tiles_workspace, moe_layer_one_token,
                       layer_one_token_workspace_bytes, layer_one_token_sync_bytes,
-                      zeroed_layer_one_token_workspace, moe_repack_weights, LAYOUTS,
+                      zeroed_layer_one_token_workspace, moe_layer_small_batch,
+                      layer_small_batch_workspace_bytes, layer_small_batch_sync_bytes,
+                      zeroed_layer_small_batch_workspace, moe_repack_weights, LAYOUTS,
                       GATINGS, moe_forward_static_workspace, STATIC_WORKSPACE_BYTES,
                       moe_forward_gptoss, moe_deinterleave_rows, GPTOSS_ALPHA, GPTOSS_LIMIT)
 from .layer import MoeLayer
@@ -21,6 +23,8 @@ __all__ = ["MoeError", "LIB_PATH", "load", "version", "status_string", "pick_bm"
            "moe_forward", "moe_gateup_swiglu", "moe_down", "moe_combine", "moe_route_tiles",
            "route_tiles_ok", "route_tiles_workspace_bytes", "zeroed_route_tiles_workspace",
            "moe_layer_one_token", "layer_one_token_workspace_bytes", "layer_one_token_sync_bytes",
-           "zeroed_layer_one_token_workspace", "moe_repack_weights", "LAYOUTS", "GATINGS",
+           "zeroed_layer_one_token_workspace", "moe_layer_small_batch",
+           "layer_small_batch_workspace_bytes", "layer_small_batch_sync_bytes",
+           "zeroed_layer_small_batch_workspace", "moe_repack_weights", "LAYOUTS", "GATINGS",
            "moe_forward_static_workspace", "STATIC_WORKSPACE_BYTES", "moe_forward_gptoss",
            "moe_deinterleave_rows", "GPTOSS_ALPHA", "GPTOSS_LIMIT", "MoeLayer"]

@@ -78,6 +78,13 @@ def load() -> ctypes.CDLL:
     lib.moe_layer_one_token.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i,
                                         _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p, _p]
     lib.moe_layer_one_token.restype = _i
+    lib.moe_layer_small_batch_workspace_bytes.argtypes = [_i, _i, _i, _i, _i]
+    lib.moe_layer_small_batch_workspace_bytes.restype = _sz
+    lib.moe_layer_small_batch_sync_bytes.argtypes = []
+    lib.moe_layer_small_batch_sync_bytes.restype = _sz
+    lib.moe_layer_small_batch.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i,
+                                          _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p, _p]
+    lib.moe_layer_small_batch.restype = _i
     lib.moe_forward_static_workspace.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _p,
                                                  _i, _i, _i, _i, _i, _i, _i, _p, _p]
     lib.moe_forward_static_workspace.restype = _i
@@ -321,6 +328,64 @@ def moe_layer_one_token(x: torch.Tensor, w_router: torch.Tensor, bias: Optional[
                                       _ptr(tiles), _ptr(num_tiles), _ptr(workspace),
                                       workspace.numel(), _ptr(out), _stream(dev)),
            "moe_layer_one_token")
+    return out, ids, wts, logits, offsets, sorted_ids, tiles, num_tiles
+
+
+def layer_small_batch_workspace_bytes(T: int, H: int, I: int, E: int, k: int) -> int:
+    """Workspace bytes of moe_layer_small_batch; 0 if the shape is not accepted."""
+    return int(load().moe_layer_small_batch_workspace_bytes(T, H, I, E, k))
+
+
+def layer_small_batch_sync_bytes() -> int:
+    """Bytes at the start of that workspace that must be zero before first use."""
+    return int(load().moe_layer_small_batch_sync_bytes())
+
+
+def zeroed_layer_small_batch_workspace(T: int, H: int, I: int, E: int, k: int,
+                                       device) -> torch.Tensor:
+    """A workspace for moe_layer_small_batch whose sync block starts at zero."""
+    return torch.zeros(max(layer_small_batch_workspace_bytes(T, H, I, E, k), 256),
+                       dtype=torch.uint8, device=device)
+
+
+def moe_layer_small_batch(x: torch.Tensor, w_router: torch.Tensor, bias: Optional[torch.Tensor],
+                          w13_q: torch.Tensor, w13_s: torch.Tensor, w2_q: torch.Tensor,
+                          w2_s: torch.Tensor, k: int, BM: int, want_logits: bool = False,
+                          workspace: Optional[torch.Tensor] = None,
+                          out: Optional[torch.Tensor] = None, gating: str = "softmax"):
+    """The whole layer for 2..4 tokens in one launch (codes in the blocked
+    layout).  Returns (out bf16 [T, H], topk_ids, topk_weights, logits or
+    None, expert_offsets, sorted_ids, tiles, num_tiles), each equal to what
+    moe_route_tiles + moe_forward produce."""
+    _need(x, "x", _BF16)
+    dev = x.device
+    _need(w_router, "w_router", (torch.float32,), dev)
+    if bias is not None:
+        _need(bias, "bias", (torch.float32,), dev)
+    for name, t in (("w13_q", w13_q), ("w13_s", w13_s), ("w2_q", w2_q), ("w2_s", w2_s)):
+        _need(t, name, _U8, dev)
+    T, H = x.shape
+    E, I2, _ = w13_q.shape
+    I = I2 // 2
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    wts = torch.empty((T, k), dtype=torch.float32, device=dev)
+    logits = torch.empty((T, E), dtype=torch.float64, device=dev) if want_logits else None
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    sorted_ids = torch.empty(T * k, dtype=torch.int32, device=dev)
+    tiles = torch.empty((max(tiles_max(T, k, E, BM), 1), 3), dtype=torch.int32, device=dev)
+    num_tiles = torch.zeros(1, dtype=torch.int32, device=dev)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    _need(out, "out", _BF16, dev)
+    if workspace is None:
+        workspace = zeroed_layer_small_batch_workspace(T, H, I, E, k, dev)
+    _check(load().moe_layer_small_batch(_ptr(x), _ptr(w_router), _ptr(bias), _ptr(w13_q),
+                                        _ptr(w13_s), _ptr(w2_q), _ptr(w2_s), T, H, I, E, k,
+                                        gating_code(gating), LAYOUTS["blocked"], _ptr(ids),
+                                        _ptr(wts), _ptr(logits), _ptr(offsets), _ptr(sorted_ids),
+                                        _ptr(tiles), _ptr(num_tiles), _ptr(workspace),
+                                        workspace.numel(), _ptr(out), _stream(dev)),
+           "moe_layer_small_batch")
     return out, ids, wts, logits, offsets, sorted_ids, tiles, num_tiles
 
 

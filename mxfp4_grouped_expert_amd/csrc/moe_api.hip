@@ -415,6 +415,42 @@ moe_status moe_forward_static_workspace(const uint16_t* x, const uint8_t* w13_q,
                         as_stream(stream));
 }
 
+size_t moe_layer_small_batch_workspace_bytes(int T, int H, int I, int E, int k) {
+  if (H > MOE_MAX_DIM || I > MOE_MAX_DIM || !moe::layer_small_batch_ok(T, H, I, E, k)) return 0;
+  return moe::layer_small_batch_bytes(H, I);
+}
+
+size_t moe_layer_small_batch_sync_bytes(void) { return moe::layer_small_batch_sync_bytes(); }
+
+moe_status moe_layer_small_batch(const uint16_t* x, const float* w_router, const float* bias,
+                                 const uint8_t* w13_q, const uint8_t* w13_s, const uint8_t* w2_q,
+                                 const uint8_t* w2_s, int T, int H, int I, int E, int k,
+                                 int gating, int layout, int32_t* topk_ids, float* topk_weights,
+                                 double* logits, int32_t* expert_offsets, int32_t* sorted_ids,
+                                 int32_t* tiles, int32_t* num_tiles, void* workspace,
+                                 size_t workspace_bytes, uint16_t* out,
+                                 struct ihipStream_t* stream) {
+  if (H <= 0 || I <= 0 || H > MOE_MAX_DIM || I > MOE_MAX_DIM || E < 1 ||
+      E > MOE_MAX_EXPERTS || k < 1 || k > MOE_MAX_TOPK || k > E ||
+      (int64_t)E * 2 * I >= (int64_t(1) << 31) || !moe::layer_small_batch_ok(T, H, I, E, k) ||
+      !gating_ok(gating) || layout != MOE_LAYOUT_BLOCKED)
+    return MOE_ERR_SHAPE;
+  if (!x || !w_router || !w13_q || !w13_s || !w2_q || !w2_s || !topk_ids || !topk_weights ||
+      !expert_offsets || !sorted_ids || !tiles || !num_tiles || !workspace || !out)
+    return MOE_ERR_NULL;
+  if (!aligned16(x) || !aligned16(w_router) || !aligned16(w13_q) || !aligned16(w13_s) ||
+      !aligned16(w2_q) || !aligned16(w2_s) || !aligned16(workspace))
+    return MOE_ERR_ALIGN;
+  if (workspace_bytes < moe::layer_small_batch_bytes(H, I)) return MOE_ERR_WORKSPACE;
+  moe_status st = check_device();
+  if (st != MOE_OK) return st;
+  (void)hipGetLastError();
+  moe::launch_layer_small_batch(x, w_router, bias, w13_q, w13_s, w2_q, w2_s, T, H, I, E, k,
+                                gating, topk_ids, topk_weights, logits, expert_offsets,
+                                sorted_ids, tiles, num_tiles, workspace, out, as_stream(stream));
+  return finish_launches();
+}
+
 size_t moe_layer_one_token_workspace_bytes(int H, int I, int E, int k) {
   if (!moe::layer_one_token_ok(H, I, E, k) || H > MOE_MAX_DIM) return 0;
   return moe::layer_one_token_bytes(H, I, E, k);

@@ -103,6 +103,21 @@ void launch_layer_one_token(const uint16_t* x, const float* w_router, const floa
                             int32_t* sorted_ids, int32_t* tiles, int32_t* num_tiles,
                             void* workspace, uint16_t* out, hipStream_t stream);
 
+// The whole layer for 2..4 tokens in one launch (blocked codes; T * k <=
+// 16), the same scheme with tiles of several rows.  The workspace starts
+// with a sync block of layer_small_batch_sync_bytes() bytes that must be zero
+// before first use and is left consistent by every call.
+bool layer_small_batch_ok(int T, int H, int I, int E, int k);
+size_t layer_small_batch_sync_bytes();
+size_t layer_small_batch_bytes(int H, int I);
+void launch_layer_small_batch(const uint16_t* x, const float* w_router, const float* bias,
+                              const uint8_t* w13_q, const uint8_t* w13_s, const uint8_t* w2_q,
+                              const uint8_t* w2_s, int T, int H, int I, int E, int k,
+                              int gating, int32_t* topk_ids, float* topk_weights, double* logits,
+                              int32_t* expert_offsets, int32_t* sorted_ids, int32_t* tiles,
+                              int32_t* num_tiles, void* workspace, uint16_t* out,
+                              hipStream_t stream);
+
 // Code matrix [rows][K/2] (canonical) -> blocked layout, out of place.
 void launch_repack_blocked(const uint8_t* q, long long rows, int K, uint8_t* qb,
                            hipStream_t stream);

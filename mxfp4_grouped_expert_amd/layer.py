@@ -2,7 +2,8 @@
 
 A call enqueues the library's entry points (moe_route, moe_build_tiles,
 moe_forward; for small batches moe_route_tiles + moe_forward; for one token
-the single-launch moe_layer_one_token) on the current stream with
+the single-launch moe_layer_one_token, and on request for 2..4 tokens the
+single-launch moe_layer_small_batch) on the current stream with
 preallocated outputs and workspaces, so it allocates nothing per call and
 can be captured in a HIP graph.  Weights are given as device tensors in the
 library's canonical layout (see include/moe_mxfp4.h).  By default
@@ -103,10 +104,13 @@ class MoeLayer:
             w13_q, w2_q = B.moe_repack_weights(w13_q), B.moe_repack_weights(w2_q)
         self.w13_q, self.w13_s, self.w2_q, self.w2_s = w13_q, w13_s, w2_q, w2_s
 
-    def plan(self, T: int, BM: Optional[int] = None, one_launch: bool = True):
+    def plan(self, T: int, BM: Optional[int] = None, one_launch: bool = True,
+             small_batch: bool = False):
         """Allocate every buffer for batches of T tokens.  With one token the
         layer runs as one launch (moe_layer_one_token) unless one_launch is
-        False or the shape is outside that entry point's range."""
+        False or the shape is outside that entry point's range; with 2..4
+        tokens and small_batch set it runs as one launch too
+        (moe_layer_small_batch, blocked codes)."""
         dev, E, H, I, k = self.device, self.E, self.H, self.I, self.k
         self.T = T
         self.BM = B.pick_bm(T, k, E) if BM is None else BM
@@ -134,6 +138,16 @@ class MoeLayer:
         # its counters must start zeroed; every call leaves them that way
         self.one_ws = (torch.zeros(one_ws, dtype=torch.uint8, device=dev)
                        if self.one_launch else None)
+        # 2..4 tokens (T * k <= 16, blocked codes): the small-batch one launch,
+        # only on request: on MI355X it measured slower than the separate
+        # launches (20b shape: 37.0 against 35.3 us at 2 tokens, 61.4 against
+        # 52.4 at 4), so it serves callers bound by the host's enqueue rate
+        small_ws = (B.layer_small_batch_workspace_bytes(T, H, I, E, k)
+                    if 2 <= T and self.layout == B.LAYOUTS["blocked"] else 0)
+        self.small_launch = bool(one_launch and small_batch and small_ws > 0 and not self.gptoss)
+        self._launch_opts = dict(one_launch=one_launch, small_batch=small_batch)
+        self.small_ws = (torch.zeros(small_ws, dtype=torch.uint8, device=dev)
+                         if self.small_launch else None)
         return self
 
     def _args(self):
@@ -224,7 +238,7 @@ class MoeLayer:
         self.check_input(x)
         T = x.shape[0]
         if self.T != T:
-            self.plan(T)
+            self.plan(T, **getattr(self, "_launch_opts", {}))
         lib, s = self._args()
         p = self._p
         E, H, I, k, BM = self.E, self.H, self.I, self.k, self.BM
@@ -237,6 +251,17 @@ class MoeLayer:
                                              p(self.num_tiles), p(self.one_ws),
                                              self.one_ws.numel(), p(self.out), s),
                      "moe_layer_one_token")
+            return self.out
+        if self.small_launch:
+            B._check(lib.moe_layer_small_batch(p(x), p(self.w_router), p(self.bias),
+                                               p(self.w13_q), p(self.w13_s), p(self.w2_q),
+                                               p(self.w2_s), T, H, I, E, k, self.gating,
+                                               self.layout, p(self.topk_ids),
+                                               p(self.topk_weights), None, p(self.offsets),
+                                               p(self.sorted_ids), p(self.tiles),
+                                               p(self.num_tiles), p(self.small_ws),
+                                               self.small_ws.numel(), p(self.out), s),
+                     "moe_layer_small_batch")
             return self.out
         self.route_only(x)
         self.tiles_only()
