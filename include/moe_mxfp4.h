@@ -413,9 +413,10 @@ moe_status moe_layer_one_token(const uint16_t* x, const float* w_router, const f
  * 16-column block combines every token of the block.  Every output is
  * bit-identical to moe_route_tiles + moe_forward with the same arguments
  * (BM any valid value: at most T <= 4 rows per expert give one tile each).
- * (On MI355X it measured slower than the separate launches at the
- * gpt-oss-20b shape: 37.0 against 35.3 us at 2 tokens, 61.4 against 52.4 at
- * 4; it saves the host three enqueues per call.)
+ * (On MI355X it does not beat the separate launches at the gpt-oss-20b
+ * shape: 35.4 against 35.3 us at 2 tokens (32.6 against 34.4 under a skewed
+ * router), 59.4 against 52.7 at 4; it saves the host three enqueues per
+ * call.)
  *
  *   arguments as for moe_route_tiles and moe_forward; logits may be NULL;
  *   bias may be NULL.  Also requires layout == MOE_LAYOUT_BLOCKED, H <= 3072

@@ -19,15 +19,14 @@
 //             position and the slots of its rows; per slot its routing
 //             weight.  Publisher 0 also writes the routing outputs and the
 //             table for the caller.
-//   GEMM      workgroup j stages every token's x row at its start (they do
-//             not depend on the routing), reads its plan words, runs gate/up
-//             job j (tile g = j / (I/16), block j % (I/16)) for the tile's
-//             rows with the arithmetic of expert_gemm_kernel<gate/up, 1, XR>,
-//             then the down job(s) of the tile t with (t+1) * I/16 <= j <
-//             (t+1) * I/16 + H/16 with that of expert_gemm_kernel<down, 1,
-//             XR>.  The last tile's down job of each 16-column block also
-//             combines the block for every token, in ascending slot order,
-//             as combine_kernel does.
+//   GEMM      workgroups run one job each: first every gate/up job (tile g,
+//             16-row block), whose workgroups stage every token's x row at
+//             their start (they do not depend on the routing), for the
+//             tile's rows with the arithmetic of expert_gemm_kernel<gate/up,
+//             1, XR>; then every down job, with that of
+//             expert_gemm_kernel<down, 1, XR>.  The last tile's down job of
+//             each 16-column block also combines the block for every token,
+//             in ascending slot order, as combine_kernel does.
 // Every value is bit-identical to moe_route_tiles + moe_forward: the router
 // partials and their sums, the top-k and gating, the table, the GEMMs' lane
 // mapping, MFMA order and split-K order, and the combine are the same
@@ -469,79 +468,55 @@ __device__ __forceinline__ void down_finish(const Args& a, const TileInfo& t, in
 }
 
 // ------------------------------------------------------- GEMM workgroups
-// Workgroup j (after the routing ones) runs gate/up job j when j < G * I/16,
-// then the down jobs of every tile t with (t+1) * I/16 <= j <
-// (t+1) * I/16 + H/16 (block j - (t+1) * I/16): a tile's down jobs sit above
-// all of its gate/up jobs, and the last tile's down job of a block above
-// the other tiles' jobs of that block.  Jobs of tiles past the table's end
-// are skipped.
+// Workgroup j (after the routing ones) runs one job: gate/up job j (tile
+// j / (I/16), block j % (I/16)) when j < G * I/16, else down job d = j -
+// G * I/16 (tile d / (H/16), block d % (H/16)).  Every down job sits above
+// every gate/up job, and the last tile's down job of a block above the other
+// tiles' jobs of that block.  (With one token, where all workgroups fit on
+// the GPU at once, a workgroup pairs a gate/up job with a down job; here
+// the grid is several times what fits, and down jobs that wait for their
+// tile's h would hold their CU while gate/up jobs of later tiles wait to be
+// dispatched.)  Jobs of tiles past the table's end return at once.
 __device__ void gemm_role(const Args& a, int j, unsigned char* lds, CallState* s_call,
                           unsigned* s_plan) {
   const int ncbI = a.I / kRowsPerBlock, ncbH = a.H / kRowsPerBlock;
-  const bool has_gu = j < a.G * ncbI;
-  const int g_gu = min(j / ncbI, a.G - 1);
-  int t0 = a.G;  // first tile with a down job here
-  for (int t = a.G - 1; t >= 0; --t)
-    if (j >= (t + 1) * ncbI && j < (t + 1) * ncbI + ncbH) t0 = t;
+  const bool gu = j < a.G * ncbI;
+  const int d = j - a.G * ncbI;
+  const int tile = gu ? j / ncbI : min(d / ncbH, a.G - 1);
+  const int cb = gu ? j - tile * ncbI : d - tile * ncbH;
 
-  if (has_gu) stage_x(a, lds);
+  if (gu) stage_x(a, lds);
   const PlanBlock* P = &a.plans[blockIdx.x % a.n_pub];
   if (threadIdx.x == 0) {
     const CallState cs = read_call_state(a.sync);
     *s_call = cs;
-    // the gate/up tile, the first down tile and the one after it (whether
-    // the down tile is the table's last)
-    const int td = min(t0, a.G - 1);
-    const u64* src[3] = {&P->tile[g_gu], &P->tile[td], &P->tile[min(td + 1, a.G - 1)]};
-    const bool use[3] = {true, true, td + 1 < a.G};
-    u64 v[3];
+    // the job's tile and, for a down job, the next one (whether the tile
+    // is the table's last)
+    const u64* src[2] = {&P->tile[tile], &P->tile[min(tile + 1, a.G - 1)]};
+    const bool use[2] = {true, !gu && tile + 1 < a.G};
+    u64 v[2];
     settle(src, use, v, (unsigned)cs.epoch + 1u, &a.sync->error, cs.spin_limit);
     s_plan[0] = (unsigned)v[0];
-    s_plan[1] = (unsigned)v[1];
-    s_plan[2] = use[2] ? (unsigned)v[2] : kNoTile;
+    s_plan[1] = use[1] ? (unsigned)v[1] : kNoTile;
   }
   __syncthreads();
   const CallState cs = *s_call;
   const unsigned stamp = (unsigned)cs.epoch + 1u;
-  const int spin_limit = cs.spin_limit;
-
-  if (has_gu) {
-    const TileInfo tg = decode_tile(s_plan[0], a.E, a.k, a.T);
-    if (tg.valid) {
-      GateupLoads gl;
-      gateup_issue(a, j - g_gu * ncbI, tg.e, gl);
-      gateup_finish(a, tg, j - g_gu * ncbI, stamp, lds, gl);
-    } else {
-      // no tile here: the x rows still land in the LDS the down job reuses
-      __builtin_amdgcn_s_waitcnt(0);
-    }
-  }
   // the check-in's atomics wait on wave 3 where it has nothing else to do
   if (threadIdx.x == 3 * kWave) check_in(a.sync, cs.epoch);
-  for (int t = t0; t < a.G; ++t) {
-    const int cb = j - (t + 1) * ncbI;
-    if (cb < 0 || cb >= ncbH) continue;
-    unsigned p = s_plan[1], pn = s_plan[2];
-    if (t != t0) {  // only when H/16 > I/16
-      __syncthreads();
-      if (threadIdx.x == 0) {
-        const u64* src[2] = {&P->tile[t], &P->tile[min(t + 1, a.G - 1)]};
-        const bool use[2] = {true, t + 1 < a.G};
-        u64 v[2];
-        settle(src, use, v, stamp, &a.sync->error, spin_limit);
-        s_plan[3] = (unsigned)v[0];
-        s_plan[4] = use[1] ? (unsigned)v[1] : kNoTile;
-      }
-      __syncthreads();
-      p = s_plan[3];
-      pn = s_plan[4];
-    }
-    const TileInfo tt = decode_tile(p, a.E, a.k, a.T);
-    if (!tt.valid) break;  // uniform: no tiles from here on
-    const bool last = (pn & kNoTile) != 0;
+  const TileInfo t = decode_tile(s_plan[0], a.E, a.k, a.T);
+  if (!t.valid) {  // uniform; no barrier below for this workgroup
+    __builtin_amdgcn_s_waitcnt(0);  // the x rows land before the workgroup ends
+    return;
+  }
+  if (gu) {
+    GateupLoads gl;
+    gateup_issue(a, cb, t.e, gl);
+    gateup_finish(a, t, cb, stamp, lds, gl);
+  } else {
     DownLoads dl;
-    down_issue(a, cb, tt.e, dl);
-    down_finish(a, tt, cb, last, stamp, spin_limit, P, lds, dl);
+    down_issue(a, cb, t.e, dl);
+    down_finish(a, t, cb, (s_plan[1] & kNoTile) != 0, stamp, cs.spin_limit, P, lds, dl);
   }
 }
 
@@ -610,7 +585,7 @@ void launch_layer_small_batch(const uint16_t* x, const float* w_router, const fl
   a.y = reinterpret_cast<u64*>(ws + off);
   a.out = out;
   const int ncbI = I / kRowsPerBlock, ncbH = H / kRowsPerBlock;
-  const int grid = a.n_route + a.G * ncbI + ncbH;
+  const int grid = a.n_route + a.G * (ncbI + ncbH);
   hipLaunchKernelGGL(moe_layer_small_batch_kernel, dim3(grid), dim3(kThreads), 0, stream, a);
 }
 

@@ -139,9 +139,9 @@ class MoeLayer:
         self.one_ws = (torch.zeros(one_ws, dtype=torch.uint8, device=dev)
                        if self.one_launch else None)
         # 2..4 tokens (T * k <= 16, blocked codes): the small-batch one launch,
-        # only on request: on MI355X it measured slower than the separate
-        # launches (20b shape: 37.0 against 35.3 us at 2 tokens, 61.4 against
-        # 52.4 at 4), so it serves callers bound by the host's enqueue rate
+        # only on request: on MI355X it does not beat the separate launches
+        # (20b shape: 35.4 against 35.3 us at 2 tokens, 59.4 against 52.7 at
+        # 4), so it serves callers bound by the host's enqueue rate
         small_ws = (B.layer_small_batch_workspace_bytes(T, H, I, E, k)
                     if 2 <= T and self.layout == B.LAYOUTS["blocked"] else 0)
         self.small_launch = bool(one_launch and small_batch and small_ws > 0 and not self.gptoss)
