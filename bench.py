@@ -391,10 +391,15 @@ def measure(args) -> dict:
         del src, dst
 
     gu_us = kernel_us["gateup"]
-    # the 128-row matrix-core kernels run when the library picks them
-    # (expert_mma_ok: 128-row tiles, K <= 3072, >= 32 slots per expert)
-    uses_mma = BM == 128 and max(H, I) <= 3072 and T * k >= 32 * E
+    # the gate/up GEMM runs on the 128-row matrix-core kernel when the library
+    # picks it (expert_mma_ok: 128-row tiles, >= 32 slots per expert, the
+    # scale slab of K = H in its 48 KB: K <= 3072, or K = 4096)
+    KB = H // 32
+    slab = 2 * (((15 if KB % 16 else 0) + 192 * KB + 15) // 16)
+    uses_mma = BM == 128 and T * k >= 32 * E and slab <= 6 * 512
     traffic_key = inp["name"] + ("" if args.layout == "canonical" else "/" + args.layout)
+    gu_bytes = n_touched * gateup_bytes(H, I) + T * H * 2 + T * k * I * 2
+    gu_flops = 2 * T * k * 2 * I * H
     if layer.one_launch:
         # the step is one launch: every byte the layer touches, per launch of it
         achieved = touched / (us * 1e-6) / 1e9
@@ -403,16 +408,15 @@ def measure(args) -> dict:
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": measured_traffic(traffic_key, kname),
                 "algorithmic_bytes_per_launch": touched, "avg_launch_us": round(us, 2)}
-    elif T <= 64 or not uses_mma:
-        gu_bytes = n_touched * gateup_bytes(H, I) + T * H * 2 + T * k * I * 2
+    elif T <= 64 or not uses_mma or gu_flops < gu_bytes * BF16_PEAK_TFLOPS / HBM_PEAK_GBS * 1e3:
+        # weight streaming: fewer flops per byte than the MFMA/HBM peak ratio
         achieved = gu_bytes / (gu_us * 1e-6) / 1e9
-        kname = "expert_gemm_kernel<gate/up>"
+        kname = "expert_mma_kernel<gate/up>" if uses_mma else "expert_gemm_kernel<gate/up>"
         roof = {"kernel": kname, "bound": "hbm", "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": measured_traffic(traffic_key, kname),
                 "algorithmic_bytes_per_launch": gu_bytes, "avg_launch_us": round(gu_us, 2)}
     else:
-        gu_flops = 2 * T * k * 2 * I * H
         achieved = gu_flops / (gu_us * 1e-6) / 1e12
         kname = "expert_mma_kernel<gate/up>"
         roof = {"kernel": kname, "bound": "mfma", "achieved": round(achieved, 1),

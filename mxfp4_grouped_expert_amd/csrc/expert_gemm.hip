@@ -637,7 +637,7 @@ void launch_gateup_swiglu(const uint16_t* x, const uint8_t* w13_q, const uint8_t
                           const int32_t* num_tiles, int tiles_max, int T, int H, int I, int E,
                           int k, int BM, bool blocked, uint16_t* h, const ExpertAct& fn,
                           hipStream_t stream) {
-  if (expert_mma_ok(T, H, I, E, k, BM)) {
+  if (expert_mma_ok(true, T, H, I, E, k, BM)) {
     launch_expert_mma(true, x, w13_q, w13_s, sorted_ids, tiles, num_tiles, tiles_max, T, H, I, E,
                       k, blocked, h, fn, stream);
     return;
@@ -670,7 +670,7 @@ void launch_down(const uint16_t* h, const uint8_t* w2_q, const uint8_t* w2_s,
                  const int32_t* sorted_ids, const int32_t* tiles, const int32_t* num_tiles,
                  int tiles_max, int T, int H, int I, int E, int k, int BM, bool blocked,
                  float* y, const ExpertAct& fn, hipStream_t stream) {
-  if (expert_mma_ok(T, H, I, E, k, BM)) {
+  if (expert_mma_ok(false, T, H, I, E, k, BM)) {
     launch_expert_mma(false, h, w2_q, w2_s, sorted_ids, tiles, num_tiles, tiles_max, T, H, I, E,
                       k, blocked, y, fn, stream);
     return;

@@ -67,9 +67,8 @@ constexpr int kWSlice = kWRowsSlice * kBK / 2;     // 3 KB of e2m1 codes per sli
 constexpr int kWStage = 4 * kWSlice;
 constexpr int kStage = kXStage + kWStage;          // 28 KB
 constexpr int kWLoadsSlice = kWSlice / 1024;       // direct loads per slice and stage (3)
-constexpr int kMaxKB = 96;                         // K <= 3072
-constexpr int kSlabUnits = 5;                      // of kThreads pieces of 16 B
-constexpr int kSlabBytes = kSlabUnits * kThreads * 16;  // 40 KB of raw scale bytes
+constexpr int kSlabUnits = 6;                      // of kThreads pieces of 16 B
+constexpr int kSlabBytes = kSlabUnits * kThreads * 16;  // 48 KB of raw scale bytes
 constexpr int kLdsBytes = kStages * kStage + kSlabBytes + kXRows * 8 + kXRows * 4;
 constexpr int kNFW = 6;                            // weight fragments per wave
 constexpr int kColsGateUp = 48;                    // output columns per slice
@@ -78,9 +77,19 @@ constexpr int kColsDown = 96;
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 static_assert(kWLoadsSlice == 3, "slice loads split 2 + 1 between the two waves of a SIMD");
 static_assert(kNFW * 16 == kWRowsSlice, "one wave decodes a whole slice");
-// slab pieces: gate/up two runs of 192 rows, down one run of 384 rows
-static_assert(2 * ((15 + 4 * kColsGateUp * kMaxKB + 15) / 16) <= kSlabUnits * kThreads, "slab");
-static_assert((15 + 4 * kColsDown * kMaxKB + 15) / 16 <= kSlabUnits * kThreads, "slab size");
+// 16-byte pieces of the scale slab for K = 32 * KB: gate/up two runs of 192
+// rows, down one run of 384 rows, each run fetched from its first byte
+// rounded down to 16 (a run starts at a multiple of KB bytes, so at a
+// multiple of 16 when KB is one)
+__host__ __device__ constexpr int slab_pieces(bool gateup, int KB) {
+  const int run_rows = gateup ? 4 * kColsGateUp : 4 * kColsDown;
+  return (gateup ? 2 : 1) * (((KB % 16 ? 15 : 0) + run_rows * KB + 15) / 16);
+}
+// every K up to 3072 fits, and K = 4096 (KB = 128, runs 16-byte aligned)
+static_assert(slab_pieces(true, 96) <= kSlabUnits * kThreads, "slab size");
+static_assert(slab_pieces(false, 96) <= kSlabUnits * kThreads, "slab size");
+static_assert(slab_pieces(true, 128) <= kSlabUnits * kThreads, "slab size");
+static_assert(slab_pieces(false, 128) <= kSlabUnits * kThreads, "slab size");
 
 __device__ __forceinline__ bool tile_ok(int e, int r0, int rows, int E, long long nslots) {
   return e >= 0 && e < E && r0 >= 0 && rows > 0 && rows <= kMT && (long long)r0 + rows <= nslots;
@@ -505,7 +514,7 @@ __global__ __launch_bounds__(kThreads, 1) void expert_mma_kernel(
   }
   const bool dma_slab = whole >= 16;
   if (dma_slab) {
-    const int nunits = (npieces + kThreads - 1) / kThreads;  // <= kSlabUnits
+    const int nunits = (npieces + kThreads - 1) / kThreads;  // <= kSlabUnits (expert_mma_ok)
     for (int u = 0; u < nunits; ++u) {
       const int p = min(u * kThreads + tid, npieces - 1);
       const int ch = (kRuns > 1 && p >= pbase[kRuns - 1]) ? kRuns - 1 : 0;
@@ -618,11 +627,13 @@ __global__ __launch_bounds__(kThreads, 1) void expert_mma_kernel(
 
 }  // namespace
 
-bool expert_mma_ok(int T, int H, int I, int E, int k, int BM) {
-  // large token tiles, K small enough for the scale slab, and the expected
-  // rows per expert large enough that 128-row tiles are mostly full
-  const int Kmax = H > I ? H : I;
-  return BM == kMT && Kmax <= 32 * kMaxKB && (long long)T * k >= 32LL * E;
+bool expert_mma_ok(bool gateup, int T, int H, int I, int E, int k, int BM) {
+  // large token tiles, the scale slab of K = H (gate/up) or I (down) within
+  // its LDS area, and the expected rows per expert large enough that
+  // 128-row tiles are mostly full
+  const int KB = (gateup ? H : I) / 32;
+  return BM == kMT && KB > 0 && slab_pieces(gateup, KB) <= kSlabUnits * kThreads &&
+         (long long)T * k >= 32LL * E;
 }
 
 void launch_expert_mma(bool gateup, const uint16_t* act, const uint8_t* wq, const uint8_t* ws,

@@ -75,8 +75,9 @@ void launch_down_combine_one_token(const uint16_t* h, const uint8_t* w2_q, const
                                    const ExpertAct& act, hipStream_t stream);
 
 // Large-tile (prefill) form of the grouped GEMMs: 128-row tiles, LDS-staged
-// operands.  expert_mma_ok says when the launchers above use it.
-bool expert_mma_ok(int T, int H, int I, int E, int k, int BM);
+// operands.  expert_mma_ok says when the launchers above use it for the
+// gate/up GEMM (gateup, K = H) or the down GEMM (K = I).
+bool expert_mma_ok(bool gateup, int T, int H, int I, int E, int k, int BM);
 void launch_expert_mma(bool gateup, const uint16_t* act, const uint8_t* wq, const uint8_t* ws,
                        const int32_t* sorted_ids, const int32_t* tiles, const int32_t* num_tiles,
                        int tiles_max, int T, int H, int I, int E, int k, bool blocked,

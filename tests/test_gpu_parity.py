@@ -265,9 +265,15 @@ RANDOM_CASES = [
     (3, 65536, 2, 2, 64, False, 0.02, 16),
     (3, 64, 2, 1, 65536, True, 0.3, 16),
     # K > 3072 with three 16-row passes per tile: two passes share each
-    # chunk's weights, the third runs alone (gate/up side, then down side)
-    (70, 4096, 2, 1, 64, False, 0.3, 128),
-    (70, 64, 2, 1, 4096, False, 0.3, 128),
+    # chunk's weights, the third runs alone (gate/up side, then down side;
+    # K = 4160 is past the 128-row kernel's scale slab)
+    (70, 4160, 2, 1, 64, False, 0.3, 128),
+    (70, 64, 2, 1, 4160, False, 0.3, 128),
+    # the 128-row matrix-core kernel past K = 3072: K = 4096 on the gate/up
+    # side (a partial column block of 32 outputs), K = 3584 on the down side
+    # and K = 3136 (98 MX blocks: scale runs not 16-byte aligned) on gate/up
+    (200, 4096, 4, 2, 224, False, 0.3, 128),
+    (150, 3136, 4, 2, 3584, True, 0.5, 128),
 ]
 
 
